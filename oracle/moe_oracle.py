@@ -1,0 +1,493 @@
+"""Plain CPU oracle for the MoE FFN layer forward of DFlash/DSpark draft models.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check of the repository's entry
+module and the CPU-baseline leg of the benchmark do.  It shares no code with
+the HIP library and does not import the product package; it takes plain numpy
+arrays (bf16 tensors as their uint16 bit patterns) and returns numpy arrays.
+
+Every step is the plain definition, written so that it can be checked against
+the pages by eye.  Floating point is fp64 except where the pages fix fp32
+(router logits, scores, the selection values and the combine weights are fp32
+per the router contract), in which case the value is computed in fp64 and
+rounded once to fp32, or, for the short fp32 chains the pages spell out
+(choice = score + bias, the renormalisation), computed in fp32 directly.
+
+Pages cited (title and section; no other source):
+  [SF1033]  SpecForge PR #1033 "MoE FFN for DFlash-family drafts: the module"
+            -- "Router" section (table with rows score / select /
+            routing_weights), and its commit notes.
+  [SF1073]  SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own DSpark draft
+            (stacked on #1035)" -- commit notes: the fp32 expert_bias, select on
+            shifted scores, the DeepSeek-V4 family, the V4.1 converter.
+  [SGL48763] sglang PR #48763 "[Feat] dflash: Serve MoE FFN drafts for DFlash
+            and DSpark" -- Modifications, Verification, commit notes on the
+            DraftMLP / DraftMoE forward and on the CUDA fixes.
+  [SF941]   SpecForge PR #941 "feat(serving): SGLang draft classes for the
+            Qwen3.8-27B DSpark MoE drafter (SGLang FusedMoE path) + tuned
+            fused-MoE configs" -- "What" and "Validation" sections, follow-up
+            comment on DeepSeek-V4 drafters.
+  [MI143]   MoE-Infinity PR #143 "feat(dflash): converge DFlash spec-decode
+            stack -> dev (supersedes #140)" -- commit note on loading the
+            resident gpt-oss MXFP4 experts.
+
+Readings taken where the pages leave a step open are marked READING; each is
+listed in the design notes of the repository.  Pins: every function below is
+pinned by a test in tests/test_oracle_pins.py against brute force, closed
+forms, library routines or the invariants the pages state.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Callable, Optional
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+# [SF1033] commit note on the renormalisation epsilon: the top-k sum is guarded
+# with 1e-20 (the DeepSeek / torchtitan value), added in fp32.
+RENORM_EPS = F32(1e-20)
+
+SCORE_FNS = ("softmax", "sigmoid", "sqrtsoftplus")
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values.
+
+    A bf16 value is the upper half of an IEEE binary32 word, so widening the
+    bits by 16 zero bits gives the fp32 value, which fp64 holds exactly.
+    """
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(F64)
+
+
+def e2m1_to_f64(code: np.ndarray) -> np.ndarray:
+    """OCP Microscaling FP4 (E2M1) element code 0..15 -> float64.
+
+    Bit 3 is the sign, bits 2..1 the exponent (bias 1), bit 0 the mantissa.
+    Exponent 0 is subnormal: 0.5 * m.  Otherwise 2**(e-1) * (1 + m/2).
+    """
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where((code >> 3) & 1, -1.0, 1.0)
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int32)))
+    return sign * mag
+
+
+def e8m0_to_f64(scale: np.ndarray) -> np.ndarray:
+    """OCP Microscaling E8M0 shared scale 0..254 -> 2**(s-127) (255 is NaN)."""
+    s = np.asarray(scale, dtype=np.int64)
+    out = np.ldexp(np.ones(s.shape, dtype=F64), (s - 127).astype(np.int32))
+    return np.where(s == 255, np.nan, out)
+
+
+def mxfp4_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Packed MXFP4 weight matrix -> float64 [N, Kin].
+
+    Layout per [MI143] (commit note on the resident gpt-oss experts): blocks
+    are output-major, codes [N, Kin/2] uint8 and scales [N, Kin/32] uint8,
+    used without a transpose.  Packing per [SF1073] (V4.1 converter commit
+    note): two E2M1 codes per byte along the input dimension, low nibble
+    first, one E8M0 scale per 32 inputs.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    n, half = codes.shape
+    kin = 2 * half
+    assert scales.shape == (n, kin // 32), (scales.shape, n, kin)
+    elem = np.empty((n, kin), dtype=np.uint8)
+    elem[:, 0::2] = codes & 0x0F      # even input index: low nibble
+    elem[:, 1::2] = codes >> 4        # odd input index: high nibble
+    vals = e2m1_to_f64(elem)
+    scale_per_elem = np.repeat(e8m0_to_f64(scales), 32, axis=1)
+    return vals * scale_per_elem
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Activation / weight tensor in its storage format -> float64."""
+    if dtype == "bf16":
+        return bf16_to_f64(a)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(F64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# Router: score -> select -> routing_weights   ([SF1033] "Router" table)
+# ----------------------------------------------------------------------------
+
+def router_logits(x64: np.ndarray, gate64: np.ndarray,
+                  router_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp32 router logits [T, E] = x [T,H] . gate [E,H]^T.
+
+    [SF1033] "Router" table, row score: a linear gate weight [E, H].
+    [SGL48763] DraftMoE forward commit note and [SF941] "What": the logits
+    reach top-k in fp32.  READING: the products of bf16 (or fp32) inputs are
+    exact in fp64; the fp64 sum is rounded once to fp32.  The optional
+    router_bias (the logit-bias variant of the qwen3_5_moe recipe, [SF941]
+    "What") is one fp32 add after that rounding.
+    """
+    logits = (x64 @ gate64.T).astype(F32)
+    if router_bias is not None:
+        logits = (logits + np.asarray(router_bias, dtype=F32)).astype(F32)
+    return logits
+
+
+def score(logits32: np.ndarray, fn: str) -> np.ndarray:
+    """fp32 scores [T, E] from fp32 logits, evaluated in fp64, rounded once.
+
+    softmax: [SF1033] "Router" table, row score (probabilities in [0, 1]).
+    sigmoid: [SF1033] text under the table (DeepSeek-V4 as TopKRouter with
+             score_fn sigmoid).
+    sqrtsoftplus: [SF1073] DeepSeek-V4 family commit note (sqrt of softplus
+             scores); softplus written in its overflow-free form
+             max(l, 0) + log1p(exp(-|l|)).
+    """
+    l = np.asarray(logits32, dtype=F32).astype(F64)
+    if fn == "softmax":
+        z = np.exp(l - l.max(axis=-1, keepdims=True))
+        s = z / z.sum(axis=-1, keepdims=True)
+    elif fn == "sigmoid":
+        s = 1.0 / (1.0 + np.exp(-l))
+    elif fn == "sqrtsoftplus":
+        s = np.sqrt(np.maximum(l, 0.0) + np.log1p(np.exp(-np.abs(l))))
+    else:
+        raise ValueError(fn)
+    return s.astype(F32)
+
+
+def choice(scores32: np.ndarray, expert_bias: Optional[np.ndarray]) -> np.ndarray:
+    """Selection values: scores shifted by the fp32 expert_bias (one fp32 add).
+
+    [SF1073] expert-bias commit note: an fp32 expert_bias moves the top-k picks
+    and never the weights; select-on-shifted-scores commit note: select gets
+    the shifted scores.
+    """
+    s = np.asarray(scores32, dtype=F32)
+    if expert_bias is None:
+        return s.copy()
+    return (s + np.asarray(expert_bias, dtype=F32)).astype(F32)
+
+
+def topk_desc(values32: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest values, largest first; equal values go to the
+    lower index (READING: the pages state no tie rule; lowest index wins).
+
+    A stable ascending sort of the negated values keeps equal values in index
+    order, which is exactly that rule (negation of an fp32 value is exact).
+    """
+    v = np.asarray(values32, dtype=F32)
+    order = np.argsort(-v, kind="stable")
+    return order[:k].astype(np.int32)
+
+
+def group_scores(choice_row32: np.ndarray, n_group: int) -> np.ndarray:
+    """Per-group score for group-limited selection: sum of the two largest
+    selection values inside the group, one fp32 add.
+
+    [SF1033] "Router" table, row select (DeepSeek-V3's group-limited top-k as a
+    select override).  READING: the DeepSeek-V3 group score (top-2 sum) over
+    the bias-shifted values, per [SF1073] (select sees only shifted scores).
+    """
+    c = np.asarray(choice_row32, dtype=F32)
+    e = c.shape[-1]
+    g = c.reshape(n_group, e // n_group)
+    two = -np.sort(-g, axis=-1)[:, :2]          # two largest per group
+    return (two[:, 0] + two[:, 1]).astype(F32)
+
+
+def select(choice32: np.ndarray, k: int, n_group: int = 1, topk_group: int = 1) -> np.ndarray:
+    """indices [T, K] int32 from selection values [T, E].
+
+    Plain: top-k of the selection values.  Group-limited (n_group > 1): keep
+    the topk_group groups with the largest group score (ties to the lower
+    group), drop every expert of the other groups, then plain top-k over what
+    is left.  [SF1033] "Router" table, row select.
+    """
+    c = np.asarray(choice32, dtype=F32)
+    t_count, e = c.shape
+    out = np.empty((t_count, k), dtype=np.int32)
+    for t in range(t_count):
+        row = c[t]
+        if n_group > 1:
+            gs = group_scores(row, n_group)
+            keep = topk_desc(gs, topk_group)
+            size = e // n_group
+            masked = np.full(e, -np.inf, dtype=F32)
+            for g in keep:
+                masked[g * size:(g + 1) * size] = row[g * size:(g + 1) * size]
+            row = masked
+        out[t] = topk_desc(row, k)
+    return out
+
+
+def routing_weights(scores32: np.ndarray, indices: np.ndarray, norm_topk_prob: bool,
+                    route_scale: float, eps=RENORM_EPS) -> np.ndarray:
+    """weights [T, K] fp32.
+
+    [SF1033] "Router" table, row routing_weights: gather from the UNSHIFTED
+    scores; renormalise by their sum when norm_topk_prob, with the 1e-20 guard
+    (commit note on the epsilon); then multiply by route_scale.  READING: the
+    sum runs in fp32 in output order (k = 0..K-1), the guard is added to the
+    sum, the division comes before the scale.
+    """
+    s = np.asarray(scores32, dtype=F32)
+    idx = np.asarray(indices)
+    t_count, k = idx.shape
+    rs = F32(route_scale)
+    w = np.empty((t_count, k), dtype=F32)
+    for t in range(t_count):
+        picked = s[t, idx[t]]
+        if norm_topk_prob:
+            total = F32(0.0)
+            for v in picked:
+                total = F32(total + v)
+            denom = F32(total + F32(eps))
+            w[t] = (picked / denom).astype(F32) * rs
+        else:
+            w[t] = picked * rs
+    return w.astype(F32)
+
+
+@dataclass
+class RouteResult:
+    logits: np.ndarray    # fp32 [T, E] (after the optional logit bias)
+    scores: np.ndarray    # fp32 [T, E], unshifted
+    choice: np.ndarray    # fp32 [T, E], scores + expert_bias
+    indices: np.ndarray   # int32 [T, K]
+    weights: np.ndarray   # fp32 [T, K]
+
+
+def route(x64, gate64, *, k, score_fn="softmax", n_group=1, topk_group=1,
+          norm_topk_prob=True, route_scale=1.0, expert_bias=None,
+          router_bias=None) -> RouteResult:
+    """The Router's fixed forward: score -> select -> routing_weights.
+
+    [SF1033] "Router" section: forward is fixed and returns scores, indices,
+    weights; the bias is applied between score and select ([SF1073]).
+    """
+    lg = router_logits(x64, gate64, router_bias)
+    sc = score(lg, score_fn)
+    ch = choice(sc, expert_bias)
+    idx = select(ch, k, n_group, topk_group)
+    w = routing_weights(sc, idx, norm_topk_prob, route_scale)
+    return RouteResult(lg, sc, ch, idx, w)
+
+
+def selection_margins(choice32: np.ndarray, indices: np.ndarray, n_group: int = 1,
+                      topk_group: int = 1) -> np.ndarray:
+    """Per-token distance of the selection from its nearest tie [T] (fp64).
+
+    The gap between the K-th picked value and the best value not picked among
+    the admissible experts and, for group-limited selection, the gap between
+    the last kept group score and the best dropped one.  A token whose margin
+    is larger than the fp32 rounding differences of two implementations has
+    one correct top-k; a smaller margin marks a near-tie.
+    """
+    c = np.asarray(choice32, dtype=F32).astype(F64)
+    t_count, e = c.shape
+    k = indices.shape[1]
+    out = np.empty(t_count, dtype=F64)
+    for t in range(t_count):
+        row = c[t].copy()
+        m = np.inf
+        if n_group > 1:
+            gs = group_scores(c[t].astype(F32), n_group).astype(F64)
+            order = np.argsort(-gs, kind="stable")
+            if topk_group < n_group:
+                m = min(m, gs[order[topk_group - 1]] - gs[order[topk_group]])
+            size = e // n_group
+            allowed = np.zeros(e, dtype=bool)
+            for g in order[:topk_group]:
+                allowed[g * size:(g + 1) * size] = True
+            row[~allowed] = -np.inf
+        picked = row[indices[t]]
+        rest = np.delete(row, indices[t])
+        rest = rest[np.isfinite(rest)]
+        if rest.size:
+            m = min(m, picked.min() - rest.max())
+        out[t] = m
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Experts
+# ----------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float) -> np.ndarray:
+    """SwiGLU activation with the optional clamp.
+
+    [SGL48763] Modifications / DraftMLP commit note: gate-up and down linears
+    with silu, or DeepSeek's clamped SwiGLU; [SF1073] DeepSeek-V4 family commit
+    note (swiglu_limit on routed and shared experts).  READING of the clamp
+    (the pages do not spell it out): the gate pre-activation is capped above at
+    +limit, the up pre-activation is clipped to [-limit, +limit];
+    limit = +inf means no clamp.
+    """
+    if math.isinf(limit):
+        return silu(gate_pre) * up_pre
+    return silu(np.minimum(gate_pre, limit)) * np.clip(up_pre, -limit, limit)
+
+
+def expert_mlp(rows64: np.ndarray, w_gate_up64: np.ndarray, w_down64: np.ndarray,
+               limit: float, b_gate_up64=None, b_down64=None) -> np.ndarray:
+    """One expert (or the dense/shared MLP) on rows [n, H] -> [n, H], fp64.
+
+    w_gate_up is the stacked [2I, H] matrix ([SF1073] converter commit note:
+    w1 and w3 fused into gate_up_proj, w2 into down_proj).  READING: rows
+    [0, I) are the gate (w1), rows [I, 2I) the up projection (w3).  The
+    optional per-expert biases of the gpt-oss-style experts ([MI143]) are
+    added to the pre-activations and to the output.
+    """
+    i2 = w_gate_up64.shape[0]
+    inter = i2 // 2
+    pre = rows64 @ w_gate_up64.T
+    if b_gate_up64 is not None:
+        pre = pre + b_gate_up64
+    h = swiglu(pre[:, :inter], pre[:, inter:], limit)
+    y = h @ w_down64.T
+    if b_down64 is not None:
+        y = y + b_down64
+    return y
+
+
+@dataclass
+class ExpertWeights:
+    """One expert's weights in fp64: w_gate_up [2I, H], w_down [H, I], and the
+    optional biases b_gate_up [2I], b_down [H]."""
+    w_gate_up: np.ndarray
+    w_down: np.ndarray
+    b_gate_up: Optional[np.ndarray] = None
+    b_down: Optional[np.ndarray] = None
+
+
+def expert_counts(indices: np.ndarray, n_experts: int) -> np.ndarray:
+    """Kept slots per expert ([SF1073] commit note on tokens_per_expert)."""
+    return np.bincount(np.asarray(indices).ravel(), minlength=n_experts).astype(np.int64)
+
+
+def permutation(indices: np.ndarray, n_experts: int):
+    """Slots t*K+k grouped by expert, stable in slot order.
+
+    Returns (slots [T*K], offsets [E+1]); the rows of expert e are
+    slots[offsets[e]:offsets[e+1]].
+    """
+    flat = np.asarray(indices).ravel()
+    slots = np.argsort(flat, kind="stable")
+    offs = np.zeros(n_experts + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(expert_counts(indices, n_experts))
+    return slots, offs
+
+
+def routed_grouped(x64: np.ndarray, indices: np.ndarray, weights32: np.ndarray,
+                   get_expert: Callable[[int], ExpertWeights], n_experts: int,
+                   limit: float) -> np.ndarray:
+    """Weighted routed output [T, H] (fp64), expert-grouped coding.
+
+    Slots are grouped by expert (permutation), each expert runs once on its
+    rows, and each row's output is added to its token with the slot's weight,
+    in k order per token ([SF1033] routing_weights row: the weights combine the
+    experts' outputs).
+    """
+    t_count, k = indices.shape
+    slots, offs = permutation(indices, n_experts)
+    y_slot = np.zeros((t_count * k, x64.shape[1]), dtype=F64)
+    for e in range(n_experts):
+        sl = slots[offs[e]:offs[e + 1]]
+        if sl.size == 0:
+            continue
+        w = get_expert(e)
+        y_slot[sl] = expert_mlp(x64[sl // k], w.w_gate_up, w.w_down, limit,
+                                w.b_gate_up, w.b_down)
+    out = np.zeros_like(x64)
+    w64 = weights32.astype(F64)
+    for kk in range(k):
+        out += w64[:, kk:kk + 1] * y_slot[np.arange(t_count) * k + kk]
+    return out
+
+
+def routed_loop(x64: np.ndarray, indices: np.ndarray, weights32: np.ndarray,
+                get_expert: Callable[[int], ExpertWeights], limit: float) -> np.ndarray:
+    """The same routed output, token by token (a second, independent coding)."""
+    t_count, k = indices.shape
+    out = np.zeros_like(x64)
+    for t in range(t_count):
+        acc = np.zeros(x64.shape[1], dtype=F64)
+        for kk in range(k):
+            w = get_expert(int(indices[t, kk]))
+            y = expert_mlp(x64[t:t + 1], w.w_gate_up, w.w_down, limit,
+                           w.b_gate_up, w.b_down)[0]
+            acc = acc + F64(weights32[t, kk]) * y
+        out[t] = acc
+    return out
+
+
+def shared_expert(x64: np.ndarray, sh_gate_up64: np.ndarray, sh_down64: np.ndarray,
+                  limit: float, sh_gate64: Optional[np.ndarray]) -> np.ndarray:
+    """gamma_t * SwiGLU-MLP(x_t) [T, H], fp64.
+
+    [SGL48763] DraftMoE commit notes: the shared expert is a DraftMLP with an
+    optional sigmoid gate, added to the routed sum; [SF941] "What": the
+    Qwen-style block's sigmoid-gated shared expert; [SF1073] DeepSeek-V4
+    family: one ungated shared expert with the same clamp.  READING: the gate
+    is a bias-free H -> 1 linear, gamma = sigmoid(x . sh_gate); ungated means
+    gamma = 1; route_scale does not touch the shared expert.
+    """
+    sh = expert_mlp(x64, sh_gate_up64, sh_down64, limit)
+    if sh_gate64 is None:
+        return sh
+    gamma = 1.0 / (1.0 + np.exp(-(x64 @ sh_gate64)))
+    return gamma[:, None] * sh
+
+
+def ffn_forward(x64, gate64, get_expert, *, n_experts, k, score_fn="softmax",
+                n_group=1, topk_group=1, norm_topk_prob=True, route_scale=1.0,
+                expert_bias=None, router_bias=None, limit=math.inf,
+                sh_gate_up64=None, sh_down64=None, sh_gate64=None,
+                coding="grouped"):
+    """Whole layer forward: (RouteResult, out [T, H] fp64).
+
+    out[t] = sum_k w[t,k] * expert_{idx[t,k]}(x_t) + gamma_t * shared(x_t).
+    """
+    r = route(x64, gate64, k=k, score_fn=score_fn, n_group=n_group,
+              topk_group=topk_group, norm_topk_prob=norm_topk_prob,
+              route_scale=route_scale, expert_bias=expert_bias,
+              router_bias=router_bias)
+    if coding == "grouped":
+        out = routed_grouped(x64, r.indices, r.weights, get_expert, n_experts, limit)
+    elif coding == "loop":
+        out = routed_loop(x64, r.indices, r.weights, get_expert, limit)
+    else:
+        raise ValueError(coding)
+    if sh_gate_up64 is not None:
+        out = out + shared_expert(x64, sh_gate_up64, sh_down64, limit, sh_gate64)
+    return r, out
+
+
+def token_output(x_row64, indices_row, weights_row32, get_expert, limit,
+                 sh_gate_up64=None, sh_down64=None, sh_gate64=None) -> np.ndarray:
+    """One token's output row [H] (fp64) given its routing; for sampled checks
+    at sizes where the whole layer is too large to evaluate on the CPU."""
+    x1 = np.asarray(x_row64, dtype=F64)[None, :]
+    acc = np.zeros(x1.shape[1], dtype=F64)
+    for kk in range(len(indices_row)):
+        w = get_expert(int(indices_row[kk]))
+        acc = acc + F64(weights_row32[kk]) * expert_mlp(
+            x1, w.w_gate_up, w.w_down, limit, w.b_gate_up, w.b_down)[0]
+    if sh_gate_up64 is not None:
+        acc = acc + shared_expert(x1, sh_gate_up64, sh_down64, limit, sh_gate64)[0]
+    return acc
