@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
+
+One step = one moe_ffn_forward call (router, permutation, expert GEMMs,
+combine, shared expert) on one batch of T tokens whose inputs already sit in
+HBM.  Expert weights rotate over several copies whose total exceeds the
+256 MB last-level cache, so every step reads its expert weights from HBM.
+
+Prints ONE JSON line.  `value` is tokens/s of the whole layer.  `roofline`
+covers the dominant kernel (routed gate_up + SwiGLU): algorithmic bytes (or
+flops) per launch divided by its mean duration, timed with HIP events
+recorded on the launch stream around that kernel inside the timed loop.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN layer tokens/s at T=72 and T=4096; achieved HBM GB/s / MFMA % of peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+STAGE_GATE_UP = 3
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles for the library's measurement hook."""
+
+    def __init__(self, n):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for arr in (self.start, self.stop):
+            for i in range(n):
+                h = ctypes.c_void_p()
+                assert self.rt.hipEventCreate(ctypes.byref(h)) == 0
+                arr[i] = h
+        self.n = n
+
+    def elapsed_ms(self):
+        out = []
+        for i in range(self.n):
+            assert self.rt.hipEventSynchronize(self.stop[i]) == 0
+            ms = ctypes.c_float()
+            assert self.rt.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i]) == 0
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for arr in (self.start, self.stop):
+            for i in range(self.n):
+                self.rt.hipEventDestroy(arr[i])
+
+
+def gate_up_cost(wl, active, T):
+    """Algorithmic bytes and flops of one routed gate_up launch: the active
+    experts' gate/up weights (+ MXFP4 scales, + linear biases) read once, the
+    activation rows read, the SwiGLU output h written."""
+    H, I, K = wl.H, wl.I, wl.K
+    if wl.w_dtype == "mxfp4":
+        w = 2 * I * H // 2 + 2 * I * H // 32
+    else:
+        w = 2 * I * H * (4 if wl.w_dtype == "f32" else 2)
+    act = 4 if wl.act_dtype == "f32" else 2
+    b = 2 * I * act if wl.expert_linear_bias_std else 0
+    bytes_ = active * (w + b) + T * H * act + T * K * I * act
+    flops = 4 * T * K * H * I
+    return bytes_, flops
+
+
+def run_gpu(wl, steps, warmup, copies=None):
+    import torch
+    from mixture_experts_ffn_04_amd import _lib, api
+    from mixture_experts_ffn_04_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    cfg = api.config_from_workload(wl)
+    log(f"workload {wl.name} T={wl.T}: drawing inputs")
+    x = W.gen_x(wl, dev)
+    base = api.layer_weights_from_workload(wl, dev)
+    expert_bytes = sum(getattr(base, f).numel() * getattr(base, f).element_size()
+                       for f in ("w_gate_up", "w_down", "w_gate_up_scale", "w_down_scale")
+                       if getattr(base, f) is not None)
+    if copies is None:
+        copies = 1 if expert_bytes > 4 * MALL_BYTES else max(2, math.ceil(1.2e9 / expert_bytes))
+        copies = min(copies, 8)
+    sets = [base]
+    for _ in range(copies - 1):
+        kw = {f: getattr(base, f) for f in api.LayerWeights.FIELDS}
+        for f in ("w_gate_up", "w_down", "w_gate_up_scale", "w_down_scale"):
+            if kw[f] is not None:
+                kw[f] = kw[f].clone()
+        sets.append(api.LayerWeights(**kw))
+    ws = api.alloc_workspace(cfg, dev)
+    out = torch.empty(wl.T, wl.H, dtype=wl.torch_act_dtype, device=dev)
+    routing = api.empty_routing(cfg, dev)
+    log(f"expert weights {expert_bytes / 1e6:.1f} MB x {copies} copies; warmup {warmup}")
+    for i in range(warmup):
+        api.ffn_forward(cfg, x, sets[i % copies], out=out, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+
+    ev = HipEvents(steps)
+    L = _lib.lib()
+    _lib.check(L.moe_profile_stage(STAGE_GATE_UP, ev.start, ev.stop, steps))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        api.ffn_forward(cfg, x, sets[i % copies], out=out, routing=routing, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    _lib.check(L.moe_profile_stage(-1, None, None, 0))
+    total_ms = t0.elapsed_time(t1)
+    k_ms = ev.elapsed_ms()
+    ev.close()
+    counts = routing.counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    log(f"timed {steps} steps: {total_ms / steps * 1e3:.1f} us/step, gate_up "
+        f"{sum(k_ms) / len(k_ms) * 1e3:.1f} us, active experts {active}")
+    res = dict(ms_per_step=total_ms / steps, kernel_ms=sum(k_ms) / len(k_ms), active=active,
+               max_count=int(counts.max()), copies=copies, expert_bytes=expert_bytes)
+    host = dict(x=x, base=base, routing=routing)
+    return res, host
+
+
+def roofline(wl, res):
+    b, f = gate_up_cost(wl, res["active"], wl.T)
+    t = res["kernel_ms"] * 1e-3
+    hbm_bound = b / (PEAK_HBM_GBS * 1e9) >= f / (PEAK_BF16_TFLOPS * 1e12)
+    if hbm_bound:
+        ach = b / t / 1e9
+        return {"kernel": "routed gate_up + SwiGLU", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": None, "algorithmic_bytes_per_launch": b,
+                "kernel_us": round(res["kernel_ms"] * 1e3, 2)}
+    ach = f / t / 1e12
+    return {"kernel": "routed gate_up + SwiGLU", "bound": "mfma", "achieved": round(ach, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None, "algorithmic_flops_per_launch": f,
+            "kernel_us": round(res["kernel_ms"] * 1e3, 2)}
+
+
+def cpu_baseline(wl, host, budget_s):
+    """The oracle, as it stands, on the same inputs (copied to the host), over
+    a bounded number of whole-batch repetitions."""
+    import numpy as np
+    from mixture_experts_ffn_04_amd import workloads as W
+    from oracle import moe_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    base = host["base"]
+    st = W.to_numpy_storage
+    x_h = st(host["x"])
+    gate_h = st(base.gate_w)
+    eb = st(base.expert_bias) if base.expert_bias is not None else None
+    rb = st(base.router_bias) if base.router_bias is not None else None
+    # expert weights of the experts this batch uses, in storage format
+    used = sorted(set(host["routing"].indices.cpu().numpy().ravel().tolist()))
+    store = {}
+    for e in used:
+        if wl.w_dtype == "mxfp4":
+            store[e] = (st(base.w_gate_up[e]), st(base.w_gate_up_scale[e]), st(base.w_down[e]),
+                        st(base.w_down_scale[e]))
+        else:
+            store[e] = (st(base.w_gate_up[e]), st(base.w_down[e]))
+    bgu = {e: st(base.b_gate_up[e]) for e in used} if base.b_gate_up is not None else None
+    bd = {e: st(base.b_down[e]) for e in used} if base.b_down is not None else None
+    sh = (st(base.sh_gate_up), st(base.sh_down)) if base.sh_gate_up is not None else None
+    shg = st(base.sh_gate) if base.sh_gate is not None else None
+    ad = wl.act_dtype
+
+    def get_expert(e):
+        s = store[e]
+        if wl.w_dtype == "mxfp4":
+            wgu, wd = O.mxfp4_dequant(s[0], s[1]), O.mxfp4_dequant(s[2], s[3])
+        else:
+            wgu, wd = O.to_f64(s[0], wl.w_dtype), O.to_f64(s[1], wl.w_dtype)
+        return O.ExpertWeights(wgu, wd, O.to_f64(bgu[e], ad) if bgu else None,
+                               O.to_f64(bd[e], ad) if bd else None)
+
+    def once():
+        return O.ffn_forward(
+            O.to_f64(x_h, ad), O.to_f64(gate_h, ad), get_expert, n_experts=wl.E, k=wl.K,
+            score_fn=wl.score_fn, n_group=wl.n_group, topk_group=wl.topk_group,
+            norm_topk_prob=wl.norm_topk_prob, route_scale=wl.route_scale,
+            expert_bias=eb, router_bias=rb, limit=wl.swiglu_limit,
+            sh_gate_up64=O.to_f64(sh[0], ad) if sh else None,
+            sh_down64=O.to_f64(sh[1], ad) if sh else None,
+            sh_gate64=O.to_f64(shg, ad) if shg is not None else None)
+
+    reps, t_total = 0, 0.0
+    while reps < 1 or (t_total < budget_s and reps < 20):
+        t = time.perf_counter()
+        once()
+        t_total += time.perf_counter() - t
+        reps += 1
+    return {"value": round(reps * wl.T / t_total, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} whole-batch forward(s) of T={wl.T} ({wl.name}), "
+                      f"{t_total:.1f} s, numpy fp64 oracle incl. weight decoding"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_8b_moe_draft")
+    ap.add_argument("--T", type=int, default=72)
+    ap.add_argument("--score-fn", default=None)
+    ap.add_argument("--copies", type=int, default=None)
+    ap.add_argument("--extra-T", type=int, default=8192,
+                    help="also time the same family at this token count (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path)", file=sys.stderr)
+        return 2
+
+    from mixture_experts_ffn_04_amd import workloads as W
+    kw = {"T": args.T}
+    if args.score_fn:
+        kw["score_fn"] = args.score_fn
+    wl = W.workload(args.workload, **kw) if args.workload != "tiny_f32" else W.workload("tiny_f32")
+
+    res, host = run_gpu(wl, args.steps, args.warmup, args.copies)
+    value = wl.T / (res["ms_per_step"] * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.act_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "I": wl.I, "K": wl.K,
+                   "expert_weights": wl.w_dtype, "weight_copies": res["copies"],
+                   "active_experts": res["active"], "max_tokens_per_expert": res["max_count"]},
+        "roofline": roofline(wl, res),
+    }
+    extra = []
+    if args.extra_T and args.extra_T != wl.T and args.workload != "tiny_f32":
+        import torch
+        del host
+        torch.cuda.empty_cache()
+        wl2 = wl.with_T(args.extra_T)
+        res2, host2 = run_gpu(wl2, max(10, args.steps // 10), max(3, args.warmup // 4), copies=1)
+        extra.append({"workload": wl2.name, "T": wl2.T,
+                      "value": round(wl2.T / (res2["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+                      "ms_per_step": round(res2["ms_per_step"], 5), "roofline": roofline(wl2, res2)})
+        del host2
+        torch.cuda.empty_cache()
+        _, host = run_gpu(wl, 2, 1, copies=1)  # inputs of the headline batch for the CPU leg
+    if extra:
+        line["extra"] = extra
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,100 @@
+"""ctypes view of include/moe_ffn.h and loading of libmoe_ffn.so.
+
+The structures and prototypes below mirror the header field for field.
+Loading fails loudly: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
+
+ABI_VERSION = 1
+
+MOE_DTYPE = {"f32": 0, "bf16": 1, "mxfp4": 2}
+MOE_SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+
+EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route", "moe_ffn_forward",
+            "moe_status_string", "moe_last_error", "moe_abi_version", "moe_profile_stage")
+
+STAGES = ("router_logits", "router_select", "permute", "gate_up", "shared_gate_up", "down",
+          "shared_down", "combine")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+        ("I", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
+        ("score_fn", ctypes.c_int32), ("n_group", ctypes.c_int32),
+        ("topk_group", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
+        ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
+        ("shared_I", ctypes.c_int32), ("shared_gated", ctypes.c_int32),
+    ]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [
+        ("gate_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+        ("expert_bias", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p),
+        ("w_down", ctypes.c_void_p), ("w_gate_up_scale", ctypes.c_void_p),
+        ("w_down_scale", ctypes.c_void_p), ("b_gate_up", ctypes.c_void_p),
+        ("b_down", ctypes.c_void_p), ("sh_gate_up", ctypes.c_void_p),
+        ("sh_down", ctypes.c_void_p), ("sh_gate", ctypes.c_void_p),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"moe_ffn status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built in-tree by mixture_experts_ffn_04_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m mixture_experts_ffn_04_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    cfgp = ctypes.POINTER(MoeConfig)
+    L.moe_validate.argtypes = [cfgp]
+    L.moe_validate.restype = ctypes.c_int
+    L.moe_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_workspace_bytes.restype = ctypes.c_int
+    L.moe_route.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_ffn_forward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, P, P, P, P, P,
+                                  ctypes.c_size_t, P]
+    L.moe_ffn_forward.restype = ctypes.c_int
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_profile_stage.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                    ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.moe_profile_stage.restype = ctypes.c_int
+    L.moe_abi_version.argtypes = []
+    L.moe_abi_version.restype = ctypes.c_int
+    if L.moe_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libmoe_ffn ABI {L.moe_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != MOE_OK:
+        L = lib()
+        raise MoeError(status, f"{L.moe_status_string(status).decode()}: {L.moe_last_error().decode()}")

@@ -1,0 +1,464 @@
+// Host side of the C ABI: validation, workspace layout and the launch
+// sequence of the layer forward.  No allocation, no host copy, no
+// synchronisation: every call only enqueues kernels on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe_ffn.h"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// measurement hook (moe_profile_stage)
+struct ProfileHook {
+  int stage = -1;
+  void *const *start = nullptr;
+  void *const *stop = nullptr;
+  int n = 0;
+  long calls = 0;
+};
+thread_local ProfileHook g_profile;
+
+// Records the hook's start (begin = true) or stop event around `stage`.
+hipError_t profile_mark(int stage, bool begin, hipStream_t st) {
+  if (g_profile.stage != stage || g_profile.n <= 0) return hipSuccess;
+  const int i = (int)(g_profile.calls % g_profile.n);
+  hipEvent_t ev = static_cast<hipEvent_t>(begin ? g_profile.start[i] : g_profile.stop[i]);
+  return hipEventRecord(ev, st);
+}
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() { return MOE_OK; }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t act_bytes(const moe_config &c) { return c.act_dtype == MOE_DTYPE_F32 ? 4 : 2; }
+
+bool has_shared(const moe_config &c) { return c.shared_I > 0; }
+bool has_shared_gate(const moe_config &c) { return c.shared_I > 0 && c.shared_gated; }
+int logits_ld(const moe_config &c) { return c.E + (has_shared_gate(c) ? 1 : 0); }
+
+// Workspace carve-up; every buffer starts on a 256-byte boundary.
+struct Layout {
+  size_t logits, gamma, scores, indices, weights, counts, offsets, active, n_active, perm, inv;
+  size_t h, y, sh_h, sh_y, total;
+};
+
+Layout make_layout(const moe_config &c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t T = c.T, K = c.K, E = c.E, H = c.H, I = c.I, Is = c.shared_I;
+  L.logits = take(T * logits_ld(c) * 4);
+  L.gamma = take(T * 4);
+  L.scores = take(T * E * 4);
+  L.indices = take(T * K * 4);
+  L.weights = take(T * K * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.active = take(E * 4);
+  L.n_active = take(4);
+  L.perm = take(T * K * 4);
+  L.inv = take(T * K * 4);
+  L.h = take(T * K * I * act_bytes(c));
+  L.y = take(T * K * H * 4);
+  L.sh_h = take(T * Is * act_bytes(c));
+  L.sh_y = take(Is ? T * H * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int check_workspace(const moe_config &c, void *ws, size_t ws_bytes) {
+  const size_t need = make_layout(c).total;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return MOE_OK;
+}
+
+#define REQUIRE_PTR(p, name)                                                          \
+  do {                                                                                \
+    if (!(p)) return fail(MOE_ERR_INVALID, "%s is NULL", name);                       \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define OPTIONAL_PTR(p, name)                                                        \
+  do {                                                                               \
+    if ((p) && !aligned16(p)) return fail(MOE_ERR_INVALID, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                         \
+  do {                                              \
+    hipError_t e_ = (expr);                         \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+struct RouteBuffers {
+  float *scores;
+  int32_t *indices;
+  float *weights;
+};
+
+// Router + permutation; shared by both entry points.
+int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const void *sh_gate,
+                  const float *router_bias, const float *expert_bias, const RouteBuffers &rb,
+                  int32_t *user_counts, char *ws, const Layout &L, bool need_permute,
+                  hipStream_t st) {
+  LogitsArgs la{};
+  la.x = x;
+  la.gate = gate_w;
+  la.sh_gate = has_shared_gate(c) ? sh_gate : nullptr;
+  la.logits = reinterpret_cast<float *>(ws + L.logits);
+  la.T = c.T;
+  la.H = c.H;
+  la.E = c.E;
+  la.ldl = logits_ld(c);
+  HIP_TRY(profile_mark(MOE_STAGE_ROUTER_LOGITS, true, st), "profile event");
+  HIP_TRY(launch_router_logits(la, c.act_dtype == MOE_DTYPE_BF16, st), "router logits launch");
+  HIP_TRY(profile_mark(MOE_STAGE_ROUTER_LOGITS, false, st), "profile event");
+
+  SelectArgs sa{};
+  sa.logits = la.logits;
+  sa.router_bias = router_bias;
+  sa.expert_bias = expert_bias;
+  sa.scores = rb.scores;
+  sa.indices = rb.indices;
+  sa.weights = rb.weights;
+  sa.gamma = reinterpret_cast<float *>(ws + L.gamma);
+  sa.T = c.T;
+  sa.E = c.E;
+  sa.K = c.K;
+  sa.ldl = la.ldl;
+  sa.score_fn = c.score_fn;
+  sa.n_group = c.n_group;
+  sa.topk_group = c.topk_group;
+  sa.norm = c.norm_topk_prob;
+  sa.route_scale = c.route_scale;
+  sa.has_shared_gate = la.sh_gate != nullptr;
+  HIP_TRY(profile_mark(MOE_STAGE_ROUTER_SELECT, true, st), "profile event");
+  HIP_TRY(launch_router_select(sa, st), "router select launch");
+  HIP_TRY(profile_mark(MOE_STAGE_ROUTER_SELECT, false, st), "profile event");
+
+  if (need_permute || user_counts) {
+    PermuteArgs pa{};
+    pa.indices = rb.indices;
+    pa.counts = reinterpret_cast<int32_t *>(ws + L.counts);
+    pa.user_counts = user_counts;
+    pa.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    pa.active = reinterpret_cast<int32_t *>(ws + L.active);
+    pa.n_active = reinterpret_cast<int32_t *>(ws + L.n_active);
+    pa.perm = reinterpret_cast<int32_t *>(ws + L.perm);
+    pa.inv = reinterpret_cast<int32_t *>(ws + L.inv);
+    pa.n_slots = c.T * c.K;
+    pa.E = c.E;
+    HIP_TRY(profile_mark(MOE_STAGE_PERMUTE, true, st), "profile event");
+    HIP_TRY(launch_permute(pa, st), "permute launch");
+    HIP_TRY(profile_mark(MOE_STAGE_PERMUTE, false, st), "profile event");
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+MOE_API int moe_profile_stage(int stage, void *const *start_events, void *const *stop_events,
+                              int n_events) {
+  if (stage >= MOE_NUM_STAGES) return fail(MOE_ERR_INVALID, "stage %d >= %d", stage, MOE_NUM_STAGES);
+  if (stage < 0) {
+    g_profile = ProfileHook{};
+    return MOE_OK;
+  }
+  if (!start_events || !stop_events || n_events <= 0)
+    return fail(MOE_ERR_INVALID, "profile events missing");
+  g_profile = ProfileHook{stage, start_events, stop_events, n_events, 0};
+  return MOE_OK;
+}
+
+MOE_API const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+MOE_API const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int moe_validate(const moe_config *cfg) {
+  if (!cfg) return fail(MOE_ERR_INVALID, "config is NULL");
+  const moe_config &c = *cfg;
+  if (c.T < 0) return fail(MOE_ERR_INVALID, "T = %d < 0", c.T);
+  if (c.H <= 0 || c.E <= 0 || c.I <= 0 || c.K <= 0)
+    return fail(MOE_ERR_INVALID, "H, E, I, K must be positive (got %d, %d, %d, %d)", c.H, c.E, c.I, c.K);
+  if (c.K > c.E) return fail(MOE_ERR_INVALID, "K = %d > E = %d", c.K, c.E);
+  if (c.act_dtype != MOE_DTYPE_F32 && c.act_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_INVALID, "act_dtype %d is not f32 or bf16", c.act_dtype);
+  if (c.w_dtype != MOE_DTYPE_F32 && c.w_dtype != MOE_DTYPE_BF16 && c.w_dtype != MOE_DTYPE_MXFP4)
+    return fail(MOE_ERR_INVALID, "w_dtype %d is unknown", c.w_dtype);
+  if (c.score_fn < MOE_SCORE_SOFTMAX || c.score_fn > MOE_SCORE_SQRTSOFTPLUS)
+    return fail(MOE_ERR_INVALID, "score_fn %d is unknown", c.score_fn);
+  if (c.n_group < 1) return fail(MOE_ERR_INVALID, "n_group = %d < 1", c.n_group);
+  if (c.E % c.n_group) return fail(MOE_ERR_INVALID, "E = %d is not a multiple of n_group = %d", c.E, c.n_group);
+  if (c.topk_group < 1 || c.topk_group > c.n_group)
+    return fail(MOE_ERR_INVALID, "topk_group = %d outside [1, n_group = %d]", c.topk_group, c.n_group);
+  if (c.n_group > 1 && c.E / c.n_group < 2)
+    return fail(MOE_ERR_INVALID, "group-limited selection needs at least 2 experts per group");
+  if (c.n_group > 1 && c.K > c.topk_group * (c.E / c.n_group))
+    return fail(MOE_ERR_INVALID, "K = %d exceeds the %d experts of the kept groups", c.K,
+                c.topk_group * (c.E / c.n_group));
+  if (c.norm_topk_prob != 0 && c.norm_topk_prob != 1)
+    return fail(MOE_ERR_INVALID, "norm_topk_prob must be 0 or 1");
+  if (!std::isfinite(c.route_scale)) return fail(MOE_ERR_INVALID, "route_scale is not finite");
+  if (std::isnan(c.swiglu_limit) || c.swiglu_limit < 0)
+    return fail(MOE_ERR_INVALID, "swiglu_limit must be >= 0 or +inf");
+  if (c.shared_I < 0) return fail(MOE_ERR_INVALID, "shared_I = %d < 0", c.shared_I);
+  if (c.shared_gated != 0 && c.shared_gated != 1) return fail(MOE_ERR_INVALID, "shared_gated must be 0 or 1");
+
+  if (c.E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", c.E, MOE_MAX_EXPERTS);
+  if (c.K > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "K = %d > %d", c.K, MOE_MAX_TOPK);
+  if (c.n_group > MOE_MAX_GROUPS)
+    return fail(MOE_ERR_UNSUPPORTED, "n_group = %d > %d", c.n_group, MOE_MAX_GROUPS);
+  if (c.H % 32 || c.I % 32 || c.shared_I % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "H, I and shared_I must be multiples of 32 (got %d, %d, %d)", c.H,
+                c.I, c.shared_I);
+  const bool pair_ok = (c.act_dtype == MOE_DTYPE_F32 && c.w_dtype == MOE_DTYPE_F32) ||
+                       (c.act_dtype == MOE_DTYPE_BF16 && c.w_dtype == MOE_DTYPE_BF16) ||
+                       (c.act_dtype == MOE_DTYPE_BF16 && c.w_dtype == MOE_DTYPE_MXFP4);
+  if (!pair_ok)
+    return fail(MOE_ERR_UNSUPPORTED, "activation/weight formats %d/%d are not implemented", c.act_dtype,
+                c.w_dtype);
+  const double slots = (double)c.T * c.K;
+  if (slots * c.H * 4 > 1.0e12 || (double)c.T * c.E > 2.0e9)
+    return fail(MOE_ERR_UNSUPPORTED, "T = %d is too large for 32-bit row indexing", c.T);
+  return ok();
+}
+
+MOE_API int moe_workspace_bytes(const moe_config *cfg, size_t *bytes) {
+  const int v = moe_validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+  *bytes = make_layout(*cfg).total;
+  return MOE_OK;
+}
+
+MOE_API int moe_route(const moe_config *cfg, const void *x, const void *gate_w,
+                      const float *router_bias, const float *expert_bias, float *scores,
+                      int32_t *indices, float *weights, int32_t *counts, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  const int v = moe_validate(cfg);
+  if (v != MOE_OK) return v;
+  const moe_config &c = *cfg;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  OPTIONAL_PTR(counts, "counts");
+  if (c.T == 0) {
+    if (counts) HIP_TRY(launch_fill_i32(counts, 0, c.E, st), "fill launch");
+    return MOE_OK;
+  }
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(gate_w, "gate_w");
+  REQUIRE_PTR(scores, "scores");
+  REQUIRE_PTR(indices, "indices");
+  REQUIRE_PTR(weights, "weights");
+  OPTIONAL_PTR(router_bias, "router_bias");
+  OPTIONAL_PTR(expert_bias, "expert_bias");
+  const int w = check_workspace(c, workspace, workspace_bytes);
+  if (w != MOE_OK) return w;
+  moe_config rc = c;
+  rc.shared_gated = 0;  // the router call has no shared-expert gate column
+  const Layout L = make_layout(c);
+  return enqueue_route(rc, x, gate_w, nullptr, router_bias, expert_bias,
+                       RouteBuffers{scores, indices, weights}, counts,
+                       static_cast<char *>(workspace), L, false, st);
+}
+
+MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weights *wt, void *out,
+                            float *scores, int32_t *indices, float *weights, int32_t *counts,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  const int v = moe_validate(cfg);
+  if (v != MOE_OK) return v;
+  const moe_config &c = *cfg;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  OPTIONAL_PTR(counts, "counts");
+  if (c.T == 0) {
+    if (counts) HIP_TRY(launch_fill_i32(counts, 0, c.E, st), "fill launch");
+    return MOE_OK;
+  }
+  if (!wt) return fail(MOE_ERR_INVALID, "weights struct is NULL");
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(out, "out");
+  REQUIRE_PTR(wt->gate_w, "gate_w");
+  REQUIRE_PTR(wt->w_gate_up, "w_gate_up");
+  REQUIRE_PTR(wt->w_down, "w_down");
+  OPTIONAL_PTR(wt->router_bias, "router_bias");
+  OPTIONAL_PTR(wt->expert_bias, "expert_bias");
+  OPTIONAL_PTR(wt->b_gate_up, "b_gate_up");
+  OPTIONAL_PTR(wt->b_down, "b_down");
+  OPTIONAL_PTR(scores, "scores");
+  OPTIONAL_PTR(indices, "indices");
+  OPTIONAL_PTR(weights, "weights");
+  if (c.w_dtype == MOE_DTYPE_MXFP4) {
+    if (!wt->w_gate_up_scale || !wt->w_down_scale)
+      return fail(MOE_ERR_INVALID, "MXFP4 experts need w_gate_up_scale and w_down_scale");
+  }
+  if (has_shared(c)) {
+    REQUIRE_PTR(wt->sh_gate_up, "sh_gate_up");
+    REQUIRE_PTR(wt->sh_down, "sh_down");
+    if (c.shared_gated) REQUIRE_PTR(wt->sh_gate, "sh_gate");
+  }
+  const size_t io_bytes = (size_t)c.T * c.H * act_bytes(c);
+  if (overlaps(x, io_bytes, out, io_bytes))
+    return fail(MOE_ERR_INVALID, "out overlaps x (the shared expert reads the unmodified input)");
+  const int w = check_workspace(c, workspace, workspace_bytes);
+  if (w != MOE_OK) return w;
+
+  char *ws = static_cast<char *>(workspace);
+  const Layout L = make_layout(c);
+  RouteBuffers rb{scores ? scores : reinterpret_cast<float *>(ws + L.scores),
+                  indices ? indices : reinterpret_cast<int32_t *>(ws + L.indices),
+                  weights ? weights : reinterpret_cast<float *>(ws + L.weights)};
+  int r = enqueue_route(c, x, wt->gate_w, wt->sh_gate, wt->router_bias, wt->expert_bias, rb, counts, ws,
+                        L, true, st);
+  if (r != MOE_OK) return r;
+
+  const WFormat wf = c.w_dtype == MOE_DTYPE_F32 ? W_F32 : (c.w_dtype == MOE_DTYPE_BF16 ? W_BF16 : W_MXFP4);
+  const WFormat af = c.act_dtype == MOE_DTYPE_F32 ? W_F32 : W_BF16;
+  const int32_t *counts_ws = reinterpret_cast<int32_t *>(ws + L.counts);
+  const int32_t *offsets_ws = reinterpret_cast<int32_t *>(ws + L.offsets);
+  const int32_t *active_ws = reinterpret_cast<int32_t *>(ws + L.active);
+  const int32_t *n_active_ws = reinterpret_cast<int32_t *>(ws + L.n_active);
+  const int32_t *perm_ws = reinterpret_cast<int32_t *>(ws + L.perm);
+  const int max_groups = (int)std::min<long>(c.E, (long)c.T * c.K);
+  const size_t H = c.H, I = c.I, Is = c.shared_I;
+
+  // routed gate_up + SwiGLU over x rows gathered by slot
+  ExpertGemmArgs g1{};
+  g1.A = x;
+  g1.perm = perm_ws;
+  g1.topk = c.K;
+  g1.counts = counts_ws;
+  g1.offsets = offsets_ws;
+  g1.active = active_ws;
+  g1.n_active = n_active_ws;
+  g1.W = wt->w_gate_up;
+  g1.Wscale = wt->w_gate_up_scale;
+  g1.w_stride = wf == W_MXFP4 ? 2 * I * H / 2 : 2 * I * H;
+  g1.s_stride = 2 * I * H / 32;
+  g1.Kdim = c.H;
+  g1.N = c.I;
+  g1.n_tiles = c.I / 16;
+  g1.bias = wt->b_gate_up;
+  g1.bias_stride = 2 * I;
+  g1.out = ws + L.h;
+  g1.limit = c.swiglu_limit;
+  HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, true, st), "profile event");
+  HIP_TRY(launch_gate_up(g1, wf, max_groups, c.T, st), "routed gate_up launch");
+  HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, false, st), "profile event");
+
+  if (has_shared(c)) {
+    ExpertGemmArgs s1{};
+    s1.A = x;
+    s1.single_rows = c.T;
+    s1.W = wt->sh_gate_up;
+    s1.Kdim = c.H;
+    s1.N = c.shared_I;
+    s1.n_tiles = c.shared_I / 16;
+    s1.out = ws + L.sh_h;
+    s1.limit = c.swiglu_limit;
+    HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, true, st), "profile event");
+    HIP_TRY(launch_gate_up(s1, af, 1, c.T, st), "shared gate_up launch");
+    HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, false, st), "profile event");
+  }
+
+  // routed down
+  ExpertGemmArgs g2{};
+  g2.A = ws + L.h;
+  g2.counts = counts_ws;
+  g2.offsets = offsets_ws;
+  g2.active = active_ws;
+  g2.n_active = n_active_ws;
+  g2.W = wt->w_down;
+  g2.Wscale = wt->w_down_scale;
+  g2.w_stride = wf == W_MXFP4 ? H * I / 2 : H * I;
+  g2.s_stride = H * I / 32;
+  g2.Kdim = c.I;
+  g2.N = c.H;
+  g2.n_tiles = c.H / 32;
+  g2.bias = wt->b_down;
+  g2.bias_stride = H;
+  g2.out = ws + L.y;
+  HIP_TRY(profile_mark(MOE_STAGE_DOWN, true, st), "profile event");
+  HIP_TRY(launch_down(g2, wf, max_groups, c.T, st), "routed down launch");
+  HIP_TRY(profile_mark(MOE_STAGE_DOWN, false, st), "profile event");
+
+  if (has_shared(c)) {
+    ExpertGemmArgs s2{};
+    s2.A = ws + L.sh_h;
+    s2.single_rows = c.T;
+    s2.W = wt->sh_down;
+    s2.Kdim = c.shared_I;
+    s2.N = c.H;
+    s2.n_tiles = c.H / 32;
+    s2.out = ws + L.sh_y;
+    HIP_TRY(profile_mark(MOE_STAGE_SHARED_DOWN, true, st), "profile event");
+    HIP_TRY(launch_down(s2, af, 1, c.T, st), "shared down launch");
+    HIP_TRY(profile_mark(MOE_STAGE_SHARED_DOWN, false, st), "profile event");
+  }
+
+  CombineArgs ca{};
+  ca.y = reinterpret_cast<const float *>(ws + L.y);
+  ca.inv = reinterpret_cast<const int32_t *>(ws + L.inv);
+  ca.weights = rb.weights;
+  ca.ysh = has_shared(c) ? reinterpret_cast<const float *>(ws + L.sh_y) : nullptr;
+  ca.gamma = has_shared_gate(c) ? reinterpret_cast<const float *>(ws + L.gamma) : nullptr;
+  ca.out = out;
+  ca.T = c.T;
+  ca.H = c.H;
+  ca.K = c.K;
+  HIP_TRY(profile_mark(MOE_STAGE_COMBINE, true, st), "profile event");
+  HIP_TRY(launch_combine(ca, c.act_dtype == MOE_DTYPE_BF16, st), "combine launch");
+  HIP_TRY(profile_mark(MOE_STAGE_COMBINE, false, st), "profile event");
+  ++g_profile.calls;
+  return MOE_OK;
+}
+
+}  // extern "C"

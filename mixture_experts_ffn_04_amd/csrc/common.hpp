@@ -1,0 +1,158 @@
+// Shared definitions of the gfx950 MoE FFN kernels: vector types, bf16
+// conversion, the MFMA wrapper and the argument blocks the host launchers
+// pass to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Low / high bf16 of a packed pair, as f32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// MFMA: D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16), one wavefront.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each with the 8
+// consecutive reduction elements 8*(l/16) .. 8*(l/16)+7; it receives
+// D[4*(l/16) + q][l % 16], q = 0..3.  Any permutation of the reduction index
+// applied to both operands gives the same product, which the kernels use to
+// let each lane read longer contiguous runs.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Streaming (read-once) 16-byte load that does not displace reused lines.
+__device__ __forceinline__ u32x4_t load_stream16(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+__device__ __forceinline__ u32x4_t load16(const void *p) {
+  return *reinterpret_cast<const u32x4_t *>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (butterfly: every lane ends with the result; the order of
+// the additions is fixed, so results are reproducible).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Argument blocks
+// ---------------------------------------------------------------------------
+
+// Router logits: logits[t, c] = x[t] . gate[c] for c < E, plus column E =
+// x[t] . sh_gate when sh_gate is given.  fp32 out, row stride ldl.
+struct LogitsArgs {
+  const void *x;        // [T, H] act dtype
+  const void *gate;     // [E, H]
+  const void *sh_gate;  // [H] or null
+  float *logits;        // [T, ldl]
+  int T, H, E, ldl;
+};
+
+// Score / select / routing weights, one wavefront per token.
+struct SelectArgs {
+  const float *logits;       // [T, ldl]
+  const float *router_bias;  // [E] or null
+  const float *expert_bias;  // [E] or null
+  float *scores;             // [T, E]
+  int32_t *indices;          // [T, K]
+  float *weights;            // [T, K]
+  float *gamma;              // [T] shared-expert gate (when has_shared_gate)
+  int T, E, K, ldl;
+  int score_fn, n_group, topk_group, norm;
+  float route_scale;
+  int has_shared_gate;
+};
+
+// Histogram / scan / scatter of the T*K slots by expert.
+struct PermuteArgs {
+  const int32_t *indices;  // [T*K]
+  int32_t *counts;         // [E]
+  int32_t *user_counts;    // [E] or null
+  int32_t *offsets;        // [E+1]
+  int32_t *active;         // [E] active experts, ascending
+  int32_t *n_active;       // [1]
+  int32_t *perm;           // [T*K] row -> slot
+  int32_t *inv;            // [T*K] slot -> row
+  int n_slots, E;
+};
+
+// Grouped expert GEMM over row groups (one group per active expert, or one
+// group of `single_rows` rows for the shared expert).
+//   gate_up (SwiGLU epilogue): out h[row, j], j < N_half, from weight rows j
+//           (gate) and N_half + j (up) of the group's [2*N_half, Kdim] matrix.
+//   down (store epilogue):     out y[row, n] f32, n < N, from weight row n of
+//           the group's [N, Kdim] matrix.
+struct ExpertGemmArgs {
+  // activation rows
+  const void *A;            // direct: [rows, Kdim]; gather: x [T, Kdim]
+  const int32_t *perm;      // gather mode: row -> slot (token = slot / topk)
+  int topk;
+  // groups
+  const int32_t *counts;    // [E] rows per expert; null = single group
+  const int32_t *offsets;   // [E+1]
+  const int32_t *active;    // [E]
+  const int32_t *n_active;  // [1]
+  int single_rows;
+  // weights
+  const void *W;            // bf16/f32 values or MXFP4 codes
+  const uint8_t *Wscale;    // MXFP4 scales
+  size_t w_stride;          // per group, in elements (bf16/f32) or bytes (codes)
+  size_t s_stride;          // per group, bytes of scales
+  int Kdim;
+  int N;                    // output columns (gate_up: N_half = I; down: H)
+  int n_tiles;              // column tiles per group
+  const void *bias;         // gate_up: [G, 2*N]; down: [G, N]; act dtype; or null
+  size_t bias_stride;
+  // output
+  void *out;                // gate_up: h [rows, N] act dtype; down: y [rows, N] f32
+  float limit;              // SwiGLU clamp (+inf = none)
+};
+
+// out[t] = sum_k weights[t,k] * y[inv[t*K+k]] + gamma[t] * ysh[t]
+struct CombineArgs {
+  const float *y;        // [T*K, H]
+  const int32_t *inv;    // [T*K]
+  const float *weights;  // [T, K]
+  const float *ysh;      // [T, H] or null
+  const float *gamma;    // [T] or null (null = 1)
+  void *out;             // [T, H] act dtype
+  int T, H, K;
+};
+
+}  // namespace moe

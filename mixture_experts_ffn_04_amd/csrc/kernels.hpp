@@ -1,0 +1,26 @@
+// Host-side launchers of the gfx950 kernels (one per kernel family).  Each
+// enqueues its kernels on `st` and returns the launch status.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+hipError_t launch_router_logits(const LogitsArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_router_select(const SelectArgs &a, hipStream_t st);
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t st);
+
+enum WFormat { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
+
+// Routed or shared expert GEMMs.  `max_groups` bounds the number of active
+// groups (host-known), `max_rows` the rows of any group; the launchers size
+// their grids from these bounds and read the actual schedule on the device.
+hipError_t launch_gate_up(const ExpertGemmArgs &a, WFormat wf, int max_groups, int max_rows,
+                          hipStream_t st);
+hipError_t launch_down(const ExpertGemmArgs &a, WFormat wf, int max_groups, int max_rows,
+                       hipStream_t st);
+
+hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st);
+hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t st);
+
+}  // namespace moe

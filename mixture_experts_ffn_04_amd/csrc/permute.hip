@@ -1,0 +1,96 @@
+// Permutation of the T*K (token, k) slots by expert: per-expert counts (the
+// kept-slot counts of SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own
+// DSpark draft (stacked on #1035)", tokens_per_expert commit note), exclusive
+// offsets, the list of active experts and the row <-> slot maps that the
+// grouped expert GEMMs and the combine read.
+//
+// One workgroup of 1024 threads: LDS histogram (integer atomics, so the
+// counts are exact and order independent), block scan over the experts,
+// scatter through per-expert LDS cursors.  The order of the rows inside one
+// expert depends on atomic timing; every row is computed independently of
+// its position, and the combine reads rows through the slot -> row map, so
+// the layer's results do not.
+#include "../../include/moe_ffn.h"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kPermuteThreads = 1024;
+static_assert(MOE_MAX_EXPERTS <= kPermuteThreads, "one expert per thread in the scan");
+
+// Inclusive scan of one int per thread over the block (1024 threads).
+__device__ __forceinline__ int block_inclusive_scan(int v, int *wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int n = __shfl_up(v, off, kWave);
+    if (lane >= off) v += n;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kPermuteThreads / 64 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int n = __shfl_up(w, off, kWave);
+      if (lane >= off) w += n;
+    }
+    if (lane < kPermuteThreads / 64) wsum[lane] = w;
+  }
+  __syncthreads();
+  if (wave > 0) v += wsum[wave - 1];
+  __syncthreads();
+  return v;
+}
+
+__global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) {
+  __shared__ int hist[MOE_MAX_EXPERTS];
+  __shared__ int wsum[kPermuteThreads / 64];
+  const int tid = threadIdx.x;
+
+  if (tid < a.E) hist[tid] = 0;
+  __syncthreads();
+  for (int s = tid; s < a.n_slots; s += kPermuteThreads) atomicAdd(&hist[a.indices[s]], 1);
+  __syncthreads();
+
+  const int v = tid < a.E ? hist[tid] : 0;
+  const int incl = block_inclusive_scan(v, wsum);
+  const int act = (tid < a.E && v > 0) ? 1 : 0;
+  const int act_incl = block_inclusive_scan(act, wsum);
+  if (tid < a.E) {
+    a.counts[tid] = v;
+    if (a.user_counts) a.user_counts[tid] = v;
+    a.offsets[tid] = incl - v;
+    if (act) a.active[act_incl - 1] = tid;
+    hist[tid] = incl - v;  // becomes the scatter cursor
+  }
+  if (tid == kPermuteThreads - 1) {
+    a.offsets[a.E] = incl;
+    a.n_active[0] = act_incl;
+  }
+  __syncthreads();
+
+  for (int s = tid; s < a.n_slots; s += kPermuteThreads) {
+    const int row = atomicAdd(&hist[a.indices[s]], 1);
+    a.perm[row] = s;
+    a.inv[s] = row;
+  }
+}
+
+__global__ void fill_i32(int32_t *p, int32_t v, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(permute_slots, dim3(1), dim3(kPermuteThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe
