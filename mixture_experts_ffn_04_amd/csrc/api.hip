@@ -69,7 +69,9 @@ Layout make_layout(const moe_config &c) {
     return o;
   };
   const size_t T = c.T, K = c.K, E = c.E, H = c.H, I = c.I, Is = c.shared_I;
-  L.logits = take(T * logits_ld(c) * 4);
+  int mt, n_split, per;
+  router_logits_plan(c.T, c.H, logits_ld(c), c.act_dtype == MOE_DTYPE_BF16, &mt, &n_split, &per);
+  L.logits = take((size_t)n_split * T * logits_ld(c) * 8);
   L.gamma = take(T * 4);
   L.scores = take(T * E * 4);
   L.indices = take(T * K * 4);
@@ -142,17 +144,21 @@ int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const 
   la.x = x;
   la.gate = gate_w;
   la.sh_gate = has_shared_gate(c) ? sh_gate : nullptr;
-  la.logits = reinterpret_cast<float *>(ws + L.logits);
+  la.partial = reinterpret_cast<double *>(ws + L.logits);
   la.T = c.T;
   la.H = c.H;
   la.E = c.E;
   la.ldl = logits_ld(c);
+  int mt;
+  router_logits_plan(c.T, c.H, la.ldl, c.act_dtype == MOE_DTYPE_BF16, &mt, &la.n_split,
+                     &la.blocks_per_split);
   HIP_TRY(profile_mark(MOE_STAGE_ROUTER_LOGITS, true, st), "profile event");
   HIP_TRY(launch_router_logits(la, c.act_dtype == MOE_DTYPE_BF16, st), "router logits launch");
   HIP_TRY(profile_mark(MOE_STAGE_ROUTER_LOGITS, false, st), "profile event");
 
   SelectArgs sa{};
-  sa.logits = la.logits;
+  sa.partial = la.partial;
+  sa.n_split = la.n_split;
   sa.router_bias = router_bias;
   sa.expert_bias = expert_bias;
   sa.scores = rb.scores;

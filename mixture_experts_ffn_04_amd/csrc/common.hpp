@@ -74,19 +74,24 @@ __device__ __forceinline__ float wave_max(float v) {
 // Argument blocks
 // ---------------------------------------------------------------------------
 
-// Router logits: logits[t, c] = x[t] . gate[c] for c < E, plus column E =
-// x[t] . sh_gate when sh_gate is given.  fp32 out, row stride ldl.
+// Router logits: partial[s][t, c] = x[t, K_s] . gate[c, K_s] over the s-th
+// slice K_s of the hidden dimension, for c < E, plus column E = x[t] .
+// sh_gate when sh_gate is given.  fp64 partial sums, row stride ldl; the
+// select kernel adds the n_split slices in order and rounds once to fp32.
 struct LogitsArgs {
   const void *x;        // [T, H] act dtype
   const void *gate;     // [E, H]
   const void *sh_gate;  // [H] or null
-  float *logits;        // [T, ldl]
+  double *partial;      // [n_split][T][ldl]
   int T, H, E, ldl;
+  int n_split;          // slices of the hidden dimension
+  int blocks_per_split; // 128-element blocks per slice (the last takes the 32-element tail)
 };
 
 // Score / select / routing weights, one wavefront per token.
 struct SelectArgs {
-  const float *logits;       // [T, ldl]
+  const double *partial;     // [n_split][T][ldl] logit partial sums
+  int n_split;
   const float *router_bias;  // [E] or null
   const float *expert_bias;  // [E] or null
   float *scores;             // [T, E]

@@ -6,6 +6,8 @@
 
 namespace moe {
 
+void router_logits_plan(int T, int H, int ncols, bool bf16, int *mt, int *n_split,
+                        int *blocks_per_split);
 hipError_t launch_router_logits(const LogitsArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_router_select(const SelectArgs &a, hipStream_t st);
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t st);

@@ -15,45 +15,92 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Logits, bf16 inputs: logits[t, c] = x[t] . gate[c] (c < E), column E =
-// x[t] . sh_gate.  Workgroup tile: 16 columns x MT*16 tokens; products of
-// bf16 are exact in f32, accumulation in f32 on the matrix cores.
+// Logits, bf16 inputs.  Workgroup tile: 16 columns x MT*16 tokens over one
+// slice of the hidden dimension (blockIdx.z).  Every MFMA step sums 32 exact
+// bf16 products into a fresh f32 accumulator; the step results are added in
+// fp64, so the only rounding left before the final one is the step's own
+// (logits end within about one f32 ulp of the exactly rounded sum, which is
+// what keeps the GPU's top-k on the oracle's side of near-ties).
 // ---------------------------------------------------------------------------
 template <int MT>
 __global__ __launch_bounds__(kBlockThreads) void router_logits_bf16(LogitsArgs a) {
-  __shared__ f32x4_t red[kSplitWaves * MT * 64];
+  __shared__ double red[kSplitWaves * MT * 64 * 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int ncols = a.E + (a.sh_gate ? 1 : 0);
   const int c0 = blockIdx.x * 16;
   const int m0 = blockIdx.y * MT * 16;
+  const int split = blockIdx.z;
   const uint16_t *gate = static_cast<const uint16_t *>(a.gate);
   const uint16_t *x = static_cast<const uint16_t *>(a.x);
 
   const int col = c0 + lr;
-  const uint16_t *wrow[1];
+  const uint16_t *wrow;
   if (col < a.E)
-    wrow[0] = gate + (size_t)col * a.H;
+    wrow = gate + (size_t)col * a.H;
   else if (col == a.E && a.sh_gate)
-    wrow[0] = static_cast<const uint16_t *>(a.sh_gate);
+    wrow = static_cast<const uint16_t *>(a.sh_gate);
   else
-    wrow[0] = gate;  // padding column: any valid row, result discarded
+    wrow = gate;  // padding column: any valid row, result discarded
 
-  const int rows_left = a.T - m0;
-  const int mt_count = min(MT, (rows_left + 15) / 16);
+  const int mt_count = min(MT, (a.T - m0 + 15) / 16);
   const uint16_t *arow[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = min(m0 + mt * 16 + lr, a.T - 1);
-    arow[mt] = x + (size_t)r * a.H;
-  }
-  f32x4_t acc[MT][1];
+  for (int mt = 0; mt < MT; ++mt) arow[mt] = x + (size_t)min(m0 + mt * 16 + lr, a.T - 1) * a.H;
+
+  double acc[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[mt][q] = 0.0;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 
-  accum_bf16<MT, 1>(wrow, arow, mt_count, a.H, wave, acc);
-  splitk_merge<MT, 1>(acc, red, mt_count, wave);
+  const int nblk = a.H / kKBlock;
+  const int b0 = split * a.blocks_per_split;
+  const int b1 = min(nblk, b0 + a.blocks_per_split);
+  for (int b = b0 + wave; b < b1; b += kSplitWaves) {
+    u32x4_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = load16(wrow + b * kKBlock + 32 * i + 8 * lg);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < mt_count) {
+        u32x4_t av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = load16(arow[mt] + b * kKBlock + 32 * i + 8 * lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t p = mfma_16x16x32(w[i], av[i], zero);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[mt][q] += (double)p[q];
+        }
+      }
+    }
+  }
+  if (split == a.n_split - 1) {  // 32-element tail of the hidden dimension
+    const int ntail = (a.H % kKBlock) / 32;
+    for (int t = wave; t < ntail; t += kSplitWaves) {
+      const int k = nblk * kKBlock + 32 * t + 8 * lg;
+      const u32x4_t w = load16(wrow + k);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt < mt_count) {
+          const f32x4_t p = mfma_16x16x32(w, load16(arow[mt] + k), zero);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[mt][q] += (double)p[q];
+        }
+      }
+    }
+  }
 
+  // merge the waves' partials in wave order
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    if (mt < mt_count)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[((wave * MT + mt) * 64 + lane) * 4 + q] = acc[mt][q];
+  __syncthreads();
+  double *out = a.partial + (size_t)split * a.T * a.ldl;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt < mt_count && (mt % kSplitWaves) == wave) {
@@ -61,16 +108,20 @@ __global__ __launch_bounds__(kBlockThreads) void router_logits_bf16(LogitsArgs a
       if (t < a.T) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          double v = red[((0 * MT + mt) * 64 + lane) * 4 + q];
+#pragma unroll
+          for (int w = 1; w < kSplitWaves; ++w) v += red[((w * MT + mt) * 64 + lane) * 4 + q];
           const int c = c0 + 4 * lg + q;
-          if (c < ncols) a.logits[(size_t)t * a.ldl + c] = acc[mt][0][q];
+          if (c < ncols) out[(size_t)t * a.ldl + c] = v;
         }
       }
     }
   }
 }
 
-// Logits, f32 inputs: one thread per (token, column), f32 fused multiply-add
-// in index order.
+// Logits, f32 inputs: one thread per (token, column).  Products of two f32
+// values are exact in fp64 and the fp64 sum of a few thousand of them is far
+// inside one f32 ulp, so the rounded logit is the exactly rounded one.
 __global__ __launch_bounds__(256) void router_logits_f32(LogitsArgs a) {
   const int ncols = a.E + (a.sh_gate ? 1 : 0);
   const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -79,9 +130,9 @@ __global__ __launch_bounds__(256) void router_logits_f32(LogitsArgs a) {
   const float *x = static_cast<const float *>(a.x) + (size_t)t * a.H;
   const float *w = c < a.E ? static_cast<const float *>(a.gate) + (size_t)c * a.H
                            : static_cast<const float *>(a.sh_gate);
-  float acc = 0.f;
-  for (int h = 0; h < a.H; ++h) acc = fmaf(x[h], w[h], acc);
-  a.logits[(size_t)t * a.ldl + c] = acc;
+  double acc = 0.0;
+  for (int h = 0; h < a.H; ++h) acc = fma((double)x[h], (double)w[h], acc);
+  a.partial[(size_t)t * a.ldl + c] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -110,40 +161,53 @@ __global__ __launch_bounds__(256) void router_select(SelectArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;  // whole wavefront leaves together
   const float NEG_INF = -__builtin_inff();
-  const float *lrow = a.logits + (size_t)t * a.ldl;
+  const size_t slice = (size_t)a.T * a.ldl;
+  const double *prow = a.partial + (size_t)t * a.ldl;
 
+  // fp32 logits: the slices' fp64 partial sums added in order, rounded once;
+  // the optional logit bias is one f32 add after that ([SF941] "What")
   float l[J], s[J], c[J];
   bool valid[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
     valid[j] = e < a.E;
-    l[j] = valid[j] ? lrow[e] : NEG_INF;
-    if (valid[j] && a.router_bias) l[j] += a.router_bias[e];
+    if (valid[j]) {
+      double v = prow[e];
+      for (int sp = 1; sp < a.n_split; ++sp) v += prow[sp * slice + e];
+      l[j] = (float)v;
+      if (a.router_bias) l[j] += a.router_bias[e];
+    } else {
+      l[j] = NEG_INF;
+    }
   }
 
-  // score ([SF1033] Router table, row score; [SF1073] DeepSeek-V4 family)
+  // scores ([SF1033] Router table, row score; [SF1073] DeepSeek-V4 family),
+  // evaluated in fp64 from the f32 logits and rounded once to f32
   if (a.score_fn == 0) {  // softmax
     float m = NEG_INF;
 #pragma unroll
     for (int j = 0; j < J; ++j) m = fmaxf(m, l[j]);
     m = wave_max(m);
-    float z[J], part = 0.f;
+    double z[J], part = 0.0;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      z[j] = valid[j] ? expf(l[j] - m) : 0.f;
+      z[j] = valid[j] ? exp((double)l[j] - (double)m) : 0.0;
       part += z[j];
     }
-    const float tot = wave_sum(part);
 #pragma unroll
-    for (int j = 0; j < J; ++j) s[j] = z[j] / tot;
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+#pragma unroll
+    for (int j = 0; j < J; ++j) s[j] = (float)(z[j] / part);
   } else if (a.score_fn == 1) {  // sigmoid
 #pragma unroll
-    for (int j = 0; j < J; ++j) s[j] = 1.f / (1.f + expf(-l[j]));
+    for (int j = 0; j < J; ++j) s[j] = (float)(1.0 / (1.0 + exp(-(double)l[j])));
   } else {  // sqrt(softplus), overflow-free softplus
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      s[j] = sqrtf(fmaxf(l[j], 0.f) + log1pf(expf(-fabsf(l[j]))));
+    for (int j = 0; j < J; ++j) {
+      const double v = (double)l[j];
+      s[j] = (float)sqrt(fmax(v, 0.0) + log1p(exp(-fabs(v))));
+    }
   }
 
   // unshifted scores out; selection values = scores + expert_bias ([SF1073])
@@ -242,12 +306,37 @@ __global__ __launch_bounds__(256) void router_select(SelectArgs a) {
     a.indices[(size_t)t * a.K + lane] = my_idx;
     a.weights[(size_t)t * a.K + lane] = w;
   }
-  if (a.has_shared_gate && lane == 0) a.gamma[t] = 1.f / (1.f + expf(-lrow[a.E]));
+  if (a.has_shared_gate && lane == 0) {
+    double v = prow[a.E];
+    for (int sp = 1; sp < a.n_split; ++sp) v += prow[sp * slice + a.E];
+    a.gamma[t] = (float)(1.0 / (1.0 + exp(-v)));
+  }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+
+// Row-tile width and number of hidden-dimension slices of the bf16 logits
+// kernel for a problem (host side; the same numbers size the workspace).
+void router_logits_plan(int T, int H, int ncols, bool bf16, int *mt, int *n_split,
+                        int *blocks_per_split) {
+  if (!bf16) {
+    *mt = 1;
+    *n_split = 1;
+    *blocks_per_split = H / kKBlock + 1;
+    return;
+  }
+  *mt = T <= 16 ? 1 : (T <= 256 ? 2 : 4);
+  const int n_ct = (ncols + 15) / 16, n_rt = (T + *mt * 16 - 1) / (*mt * 16);
+  const int nblk = H / kKBlock;
+  const long base = std::max(1L, (long)n_ct * n_rt);
+  int s = (int)std::max(1L, (512 + base - 1) / base);
+  s = std::min(s, std::max(1, nblk / kSplitWaves));
+  const int per = nblk > 0 ? (nblk + s - 1) / s : 0;
+  *n_split = per > 0 ? (nblk + per - 1) / per : 1;
+  *blocks_per_split = per;
+}
 
 hipError_t launch_router_logits(const LogitsArgs &a, bool bf16, hipStream_t st) {
   const int ncols = a.E + (a.sh_gate ? 1 : 0);
@@ -257,9 +346,16 @@ hipError_t launch_router_logits(const LogitsArgs &a, bool bf16, hipStream_t st) 
     hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  constexpr int MT = 4;
-  dim3 grid((ncols + 15) / 16, (a.T + MT * 16 - 1) / (MT * 16));
-  hipLaunchKernelGGL(router_logits_bf16<MT>, grid, dim3(kBlockThreads), 0, st, a);
+  int mt, n_split, per;
+  router_logits_plan(a.T, a.H, ncols, true, &mt, &n_split, &per);
+  const dim3 block(kBlockThreads);
+  const dim3 grid((ncols + 15) / 16, (a.T + mt * 16 - 1) / (mt * 16), n_split);
+  if (mt == 1)
+    hipLaunchKernelGGL(router_logits_bf16<1>, grid, block, 0, st, a);
+  else if (mt == 2)
+    hipLaunchKernelGGL(router_logits_bf16<2>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(router_logits_bf16<4>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -104,6 +104,91 @@ __device__ __forceinline__ void accum_bf16(const uint16_t *const (&wrow)[NS],
   }
 }
 
+// Pipelined variant.  Reduction layout per 128-block: MFMA step i (0..3) uses
+// elements [32i, 32i+32) of the block with the standard operand layout (lane
+// group g holds elements 32i + 8g .. 32i + 8g + 7), so each load
+// instruction reads 64 contiguous bytes of every row it touches.  The next
+// block's weights (and, with PFA, activations) are loaded before the MFMAs of
+// the current block, so HBM latency overlaps the matrix work.
+template <int MT, int NS, bool PFA, int SW = kSplitWaves>
+__device__ __forceinline__ void accum_bf16_pf(const uint16_t *const (&wrow)[NS],
+                                              const uint16_t *const (&arow)[MT], int mt_count,
+                                              int kdim, int wave, f32x4_t (&acc)[MT][NS]) {
+  const int lg = (threadIdx.x & 63) >> 4;
+  const int nblk = kdim / kKBlock;
+  auto load_w = [&](u32x4_t (&w)[NS][4], int b) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[s][i] = load_stream16(wrow[s] + b * kKBlock + 32 * i + 8 * lg);
+  };
+  auto load_a = [&](u32x4_t (&a)[MT][4], int b) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      if (mt < mt_count)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[mt][i] = load16(arow[mt] + b * kKBlock + 32 * i + 8 * lg);
+  };
+  auto mma = [&](const u32x4_t (&w)[NS][4], const u32x4_t (&a)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      if (mt < mt_count)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int s = 0; s < NS; ++s) acc[mt][s] = mfma_16x16x32(w[s][i], a[mt][i], acc[mt][s]);
+  };
+  int b = wave;
+  if (b < nblk) {
+    u32x4_t w0[NS][4], a0[MT][4];
+    load_w(w0, b);
+    if constexpr (PFA) load_a(a0, b);
+    while (true) {
+      const int bn = b + SW;
+      if (bn < nblk) {
+        u32x4_t w1[NS][4], a1[MT][4];
+        load_w(w1, bn);
+        if constexpr (PFA) {
+          load_a(a1, bn);
+        } else {
+          load_a(a0, b);
+        }
+        mma(w0, a0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w0[s][i] = w1[s][i];
+        if constexpr (PFA) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a0[mt][i] = a1[mt][i];
+        }
+        b = bn;
+      } else {
+        if constexpr (!PFA) load_a(a0, b);
+        mma(w0, a0);
+        break;
+      }
+    }
+  }
+  const int ntail = (kdim % kKBlock) / 32;
+  for (int t = wave; t < ntail; t += SW) {
+    const int k = nblk * kKBlock + 32 * t + 8 * lg;
+    u32x4_t w[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) w[s] = load_stream16(wrow[s] + k);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < mt_count) {
+        const u32x4_t av = load16(arow[mt] + k);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[mt][s] = mfma_16x16x32(w[s], av, acc[mt][s]);
+      }
+    }
+  }
+}
+
 // Same with MXFP4 weights: crow[s] = this lane's code row (bytes, two
 // elements per byte), srow[s] = its E8M0 scale row (one byte per 32).
 template <int MT, int NS>
@@ -162,7 +247,7 @@ __device__ __forceinline__ void accum_mxfp4(const uint8_t *const (&crow)[NS],
 // w adds, in wave order, the partials of the row tiles mt with mt % kSplitWaves
 // == w.  After the call acc[mt] of those tiles holds the full sums.
 // `red` must hold kSplitWaves * MT * NS * 64 f32x4 values.
-template <int MT, int NS>
+template <int MT, int NS, int SW = kSplitWaves>
 __device__ __forceinline__ void splitk_merge(f32x4_t (&acc)[MT][NS], f32x4_t *red, int mt_count,
                                              int wave) {
   const int lane = threadIdx.x & 63;
@@ -174,12 +259,12 @@ __device__ __forceinline__ void splitk_merge(f32x4_t (&acc)[MT][NS], f32x4_t *re
   __syncthreads();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    if (mt < mt_count && (mt % kSplitWaves) == wave) {
+    if (mt < mt_count && (mt % SW) == wave) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         f32x4_t sum = red[((0 * MT + mt) * NS + s) * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kSplitWaves; ++w) sum += red[((w * MT + mt) * NS + s) * 64 + lane];
+        for (int w = 1; w < SW; ++w) sum += red[((w * MT + mt) * NS + s) * 64 + lane];
         acc[mt][s] = sum;
       }
     }

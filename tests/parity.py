@@ -8,9 +8,12 @@ rounded in a different order than the oracle's exact-then-rounded logits:
     weights within 1e-6 (this pins the selection logic bit for bit);
  2. scores: GPU scores are within a small relative distance of the oracle's;
  3. end to end: on every token whose oracle selection margin exceeds
-    tau = 8 x the largest selection-value difference, the indices are equal;
-    at the committed seeds no token falls below tau, so all indices and the
-    per-expert counts are equal.
+    tau = 8 x the largest selection-value difference, the indices are equal.
+    A token inside that distance of a tie has more than one correct top-k at
+    the precision both sides decide in (f32); if the GPU picks differently
+    there, its pick must be a top-k of the oracle's own selection values up
+    to tau, and its weights and output are checked against the oracle
+    evaluated on that pick.  Counts equal the oracle's when no token differs.
 Outputs: max |gpu - oracle| <= 2e-2 * rms(oracle) for bf16 outputs (the
 bound the pages' measured drift supports), 1e-5 * rms + 1e-6 for f32.
 """
@@ -111,8 +114,9 @@ class Case:
 
 
 def check_routing(case: Case, o: O.RouteResult, g: api.Routing, report: dict):
-    """Three-layer routing comparison (module docstring).  Returns the mask of
-    tokens whose routing is unique at the measured rounding distance."""
+    """Three-layer routing comparison (module docstring).  Returns (mask of
+    tokens where the GPU picked differently inside a near-tie, the oracle's
+    weights for the GPU's picks)."""
     wl = case.wl
     gs = g.scores.cpu().numpy()
     gi = g.indices.cpu().numpy()
@@ -139,15 +143,47 @@ def check_routing(case: Case, o: O.RouteResult, g: api.Routing, report: dict):
     tau = 8.0 * max(dch, 1e-12)
     margins = O.selection_margins(o.choice, o.indices, wl.n_group, wl.topk_group)
     unique = margins > tau
+    mism = np.any(gi != o.indices, axis=1)
     report.update(choice_maxabs=dch, tau=tau, min_margin=float(margins.min()) if margins.size else math.inf,
-                  near_ties=int((~unique).sum()))
-    assert np.array_equal(gi[unique], o.indices[unique]), "indices differ on a token with a clear margin"
-    assert report["near_ties"] == 0, f"near-tied tokens at this seed: {np.nonzero(~unique)[0][:10]}"
-    assert np.array_equal(gc, O.expert_counts(o.indices, wl.E)), "per-expert counts differ"
-    dw = np.abs(gw - o.weights)
+                  near_ties=int((~unique).sum()), index_mismatches=int(mism.sum()),
+                  indices_equal_frac=float(1.0 - mism.mean()) if mism.size else 1.0)
+    assert not np.any(mism & unique), "indices differ on a token with a clear margin"
+    for t in np.nonzero(mism)[0]:
+        assert valid_near_tie(o.choice[t], gi[t], tau, wl), f"token {t}: GPU pick is not a near-tie"
+    if not mism.any():
+        assert np.array_equal(gc, O.expert_counts(o.indices, wl.E)), "per-expert counts differ"
+    assert np.array_equal(gc, O.expert_counts(gi, wl.E)), "counts inconsistent with the GPU indices"
+    # weights: the oracle's weights for the GPU's own selection
+    ow = o.weights.copy()
+    if mism.any():
+        ow[mism] = O.routing_weights(o.scores[mism], gi[mism], wl.norm_topk_prob, wl.route_scale)
+    dw = np.abs(gw - ow)
     report["weights_maxabs"] = float(dw.max()) if dw.size else 0.0
     assert report["weights_maxabs"] <= WEIGHT_TOL
-    return unique
+    return mism, ow
+
+
+def valid_near_tie(choice_row, picked, tau, wl):
+    """The GPU's pick, judged by the oracle's selection values, is a top-K
+    (and a top-topk_group group choice) up to tau, and is ordered up to tau."""
+    c = np.asarray(choice_row, dtype=np.float64)
+    picked = np.asarray(picked)
+    allowed = np.ones(c.shape[0], dtype=bool)
+    if wl.n_group > 1:
+        gs = O.group_scores(choice_row, wl.n_group).astype(np.float64)
+        size = c.shape[0] // wl.n_group
+        kth = np.sort(gs)[::-1][wl.topk_group - 1]
+        ok_groups = gs >= kth - 2 * tau
+        used = np.unique(picked // size)
+        if not np.all(ok_groups[used]) or len(used) > wl.topk_group:
+            return False
+        allowed = np.repeat(ok_groups, size)
+    rest = np.ones(c.shape[0], dtype=bool)
+    rest[picked] = False
+    rest &= allowed
+    if rest.any() and c[picked].min() < c[rest].max() - tau:
+        return False
+    return bool(np.all(c[picked][:-1] >= c[picked][1:] - tau))
 
 
 def check_output(case: Case, gpu_out: torch.Tensor, ref: np.ndarray, report: dict, rows=None):
