@@ -46,6 +46,15 @@ int fail(int code, const char *fmt, ...) {
 
 int ok() { return MOE_OK; }
 
+// Experts with at most this many rows run the narrow (one 16-row tile) GEMM
+// launch; the others the wide one.
+constexpr int kSmallRows = 16;
+
+// Token counts from which the expert GEMMs use the LDS-tiled kernels (routed
+// experts, shared expert); below them the weight-streaming kernels.
+constexpr int kTiledMinTokens = 512;
+constexpr int kTiledMinTokensShared = 256;
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 size_t act_bytes(const moe_config &c) { return c.act_dtype == MOE_DTYPE_F32 ? 4 : 2; }
@@ -56,7 +65,8 @@ int logits_ld(const moe_config &c) { return c.E + (has_shared_gate(c) ? 1 : 0); 
 
 // Workspace carve-up; every buffer starts on a 256-byte boundary.
 struct Layout {
-  size_t logits, gamma, scores, indices, weights, counts, offsets, active, n_active, perm, inv;
+  size_t logits, gamma, scores, indices, weights, counts, offsets, active, n_active, active_big,
+      n_active_big, active_all, n_active_all, mtile_prefix, perm, inv;
   size_t h, y, sh_h, sh_y, total;
 };
 
@@ -80,11 +90,18 @@ Layout make_layout(const moe_config &c) {
   L.offsets = take((E + 1) * 4);
   L.active = take(E * 4);
   L.n_active = take(4);
+  L.active_big = take(E * 4);
+  L.n_active_big = take(4);
+  L.active_all = take(E * 4);
+  L.n_active_all = take(4);
+  L.mtile_prefix = take((E + 1) * 4);
   L.perm = take(T * K * 4);
   L.inv = take(T * K * 4);
-  L.h = take(T * K * I * act_bytes(c));
+  // bf16 activations keep h as a bf16 (hi, lo) pair: h = hi + lo to ~16 bits
+  const size_t hparts = c.act_dtype == MOE_DTYPE_BF16 ? 2 : 1;
+  L.h = take(hparts * T * K * I * act_bytes(c));
   L.y = take(T * K * H * 4);
-  L.sh_h = take(T * Is * act_bytes(c));
+  L.sh_h = take(hparts * T * Is * act_bytes(c));
   L.sh_y = take(Is ? T * H * 4 : 0);
   L.total = off;
   return L;
@@ -187,6 +204,13 @@ int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const 
     pa.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     pa.active = reinterpret_cast<int32_t *>(ws + L.active);
     pa.n_active = reinterpret_cast<int32_t *>(ws + L.n_active);
+    pa.active_big = reinterpret_cast<int32_t *>(ws + L.active_big);
+    pa.n_active_big = reinterpret_cast<int32_t *>(ws + L.n_active_big);
+    pa.small_rows = kSmallRows;
+    pa.active_all = reinterpret_cast<int32_t *>(ws + L.active_all);
+    pa.n_active_all = reinterpret_cast<int32_t *>(ws + L.n_active_all);
+    pa.mtile_prefix = reinterpret_cast<int32_t *>(ws + L.mtile_prefix);
+    pa.tile_rows = tiled_tile_rows();
     pa.perm = reinterpret_cast<int32_t *>(ws + L.perm);
     pa.inv = reinterpret_cast<int32_t *>(ws + L.inv);
     pa.n_slots = c.T * c.K;
@@ -395,9 +419,33 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   g1.bias = wt->b_gate_up;
   g1.bias_stride = 2 * I;
   g1.out = ws + L.h;
+  const bool hilo = c.act_dtype == MOE_DTYPE_BF16;
+  char *h_lo = ws + L.h + (size_t)c.T * c.K * c.I * 2;
+  char *sh_h_lo = ws + L.sh_h + (size_t)c.T * c.shared_I * 2;
+  if (hilo) g1.out_lo = h_lo;
   g1.limit = c.swiglu_limit;
+  const int32_t *active_big_ws = reinterpret_cast<int32_t *>(ws + L.active_big);
+  const int32_t *n_active_big_ws = reinterpret_cast<int32_t *>(ws + L.n_active_big);
+  const long slots = (long)c.T * c.K;
+  const int max_big = (int)std::min<long>(c.E, slots / (kSmallRows + 1));
+  const bool tiled = wf != W_F32 && c.T >= kTiledMinTokens;
+  const bool tiled_shared = af != W_F32 && c.T >= kTiledMinTokensShared;
+  const int32_t *active_all_ws = reinterpret_cast<int32_t *>(ws + L.active_all);
+  const int32_t *n_active_all_ws = reinterpret_cast<int32_t *>(ws + L.n_active_all);
+  const int32_t *mtile_prefix_ws = reinterpret_cast<int32_t *>(ws + L.mtile_prefix);
   HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, true, st), "profile event");
-  HIP_TRY(launch_gate_up(g1, wf, max_groups, c.T, st), "routed gate_up launch");
+  if (tiled) {
+    TiledGemmArgs t1{g1, active_all_ws, n_active_all_ws, mtile_prefix_ws};
+    HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
+  } else {
+    HIP_TRY(launch_gate_up(g1, wf, max_groups, std::min(c.T, kSmallRows), st), "routed gate_up launch");
+    if (max_big > 0) {  // experts with more rows than one narrow tile holds
+      ExpertGemmArgs g1b = g1;
+      g1b.active = active_big_ws;
+      g1b.n_active = n_active_big_ws;
+      HIP_TRY(launch_gate_up(g1b, wf, max_big, c.T, st), "routed gate_up launch");
+    }
+  }
   HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, false, st), "profile event");
 
   if (has_shared(c)) {
@@ -409,15 +457,22 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
     s1.N = c.shared_I;
     s1.n_tiles = c.shared_I / 16;
     s1.out = ws + L.sh_h;
+    if (hilo) s1.out_lo = sh_h_lo;
     s1.limit = c.swiglu_limit;
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, true, st), "profile event");
-    HIP_TRY(launch_gate_up(s1, af, 1, c.T, st), "shared gate_up launch");
+    if (tiled_shared) {
+      TiledGemmArgs ts{s1, nullptr, nullptr, nullptr};
+      HIP_TRY(launch_tiled(ts, true, af, c.T, 1, st), "shared gate_up launch");
+    } else {
+      HIP_TRY(launch_gate_up(s1, af, 1, c.T, st), "shared gate_up launch");
+    }
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, false, st), "profile event");
   }
 
   // routed down
   ExpertGemmArgs g2{};
   g2.A = ws + L.h;
+  if (hilo) g2.A_lo = h_lo;
   g2.counts = counts_ws;
   g2.offsets = offsets_ws;
   g2.active = active_ws;
@@ -432,13 +487,33 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   g2.bias = wt->b_down;
   g2.bias_stride = H;
   g2.out = ws + L.y;
+  // one expert per token and no shared expert: the down epilogue writes the
+  // weighted output row itself and no combine pass is needed
+  const bool direct = c.K == 1 && !has_shared(c) && wf != W_F32;
+  if (direct) {
+    g2.direct_out = out;
+    g2.perm = perm_ws;
+    g2.weights = rb.weights;
+  }
   HIP_TRY(profile_mark(MOE_STAGE_DOWN, true, st), "profile event");
-  HIP_TRY(launch_down(g2, wf, max_groups, c.T, st), "routed down launch");
+  if (tiled) {
+    TiledGemmArgs t2{g2, active_all_ws, n_active_all_ws, mtile_prefix_ws};
+    HIP_TRY(launch_tiled(t2, false, wf, slots, max_groups, st), "routed down launch");
+  } else {
+    HIP_TRY(launch_down(g2, wf, max_groups, std::min(c.T, kSmallRows), st), "routed down launch");
+    if (max_big > 0) {  // experts with more rows than one narrow tile holds
+      ExpertGemmArgs g2b = g2;
+      g2b.active = active_big_ws;
+      g2b.n_active = n_active_big_ws;
+      HIP_TRY(launch_down(g2b, wf, max_big, c.T, st), "routed down launch");
+    }
+  }
   HIP_TRY(profile_mark(MOE_STAGE_DOWN, false, st), "profile event");
 
   if (has_shared(c)) {
     ExpertGemmArgs s2{};
     s2.A = ws + L.sh_h;
+    if (hilo) s2.A_lo = sh_h_lo;
     s2.single_rows = c.T;
     s2.W = wt->sh_down;
     s2.Kdim = c.shared_I;
@@ -446,8 +521,18 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
     s2.n_tiles = c.H / 32;
     s2.out = ws + L.sh_y;
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_DOWN, true, st), "profile event");
-    HIP_TRY(launch_down(s2, af, 1, c.T, st), "shared down launch");
+    if (tiled_shared) {
+      TiledGemmArgs ts{s2, nullptr, nullptr, nullptr};
+      HIP_TRY(launch_tiled(ts, false, af, c.T, 1, st), "shared down launch");
+    } else {
+      HIP_TRY(launch_down(s2, af, 1, c.T, st), "shared down launch");
+    }
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_DOWN, false, st), "profile event");
+  }
+
+  if (direct) {
+    ++g_profile.calls;
+    return MOE_OK;
   }
 
   CombineArgs ca{};

@@ -10,11 +10,14 @@
 
 namespace moe {
 
+// grid: (column chunks of 1024, tokens); each thread owns 4 adjacent columns.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
-  const int t = blockIdx.x;
+  const int t = blockIdx.y;
   const float gam = a.ysh ? (a.gamma ? a.gamma[t] : 1.f) : 0.f;
-  for (int c = threadIdx.x * 4; c < a.H; c += 256 * 4) {
+  {
+    const int c = blockIdx.x * 1024 + threadIdx.x * 4;
+    if (c >= a.H) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k = 0; k < a.K; ++k) {
       const float w = a.weights[(size_t)t * a.K + k];
@@ -44,10 +47,11 @@ __global__ __launch_bounds__(256) void combine_rows(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
+  const dim3 grid((a.H + 1023) / 1024, a.T);
   if (bf16_out)
-    hipLaunchKernelGGL(combine_rows<true>, dim3(a.T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_rows<true>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(combine_rows<false>, dim3(a.T), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(combine_rows<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -110,8 +110,15 @@ struct PermuteArgs {
   int32_t *counts;         // [E]
   int32_t *user_counts;    // [E] or null
   int32_t *offsets;        // [E+1]
-  int32_t *active;         // [E] active experts, ascending
+  int32_t *active;         // [E] experts with 1..small_rows rows, ascending
   int32_t *n_active;       // [1]
+  int32_t *active_big;     // [E] experts with more than small_rows rows, ascending
+  int32_t *n_active_big;   // [1]
+  int small_rows;
+  int32_t *active_all;     // [E] every expert with rows, ascending
+  int32_t *n_active_all;   // [1]
+  int32_t *mtile_prefix;   // [E+1] prefix over active_all of ceil(rows / tile_rows)
+  int tile_rows;
   int32_t *perm;           // [T*K] row -> slot
   int32_t *inv;            // [T*K] slot -> row
   int n_slots, E;
@@ -144,9 +151,24 @@ struct ExpertGemmArgs {
   int n_tiles;              // column tiles per group
   const void *bias;         // gate_up: [G, 2*N]; down: [G, N]; act dtype; or null
   size_t bias_stride;
+  const void *A_lo;         // down with bf16 h: low halves of h (h = hi + lo); or null
   // output
   void *out;                // gate_up: h [rows, N] act dtype; down: y [rows, N] f32
+  void *out_lo;             // gate_up with bf16 h: bf16(h - hi) [rows, N]; or null
   float limit;              // SwiGLU clamp (+inf = none)
+  // down only: write out[token] = weight * y (bf16) instead of y; valid when
+  // every token has one expert and there is no shared expert
+  void *direct_out;
+  const float *weights;     // [T*K] routing weights by slot
+};
+
+// Tiled grouped GEMM (large token counts): same operands and epilogues as
+// ExpertGemmArgs; groups are walked through active_all / mtile_prefix.
+struct TiledGemmArgs {
+  ExpertGemmArgs g;
+  const int32_t *active_all;
+  const int32_t *n_active_all;
+  const int32_t *mtile_prefix;
 };
 
 // out[t] = sum_k weights[t,k] * y[inv[t*K+k]] + gamma[t] * ysh[t]

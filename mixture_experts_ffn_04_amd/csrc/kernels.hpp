@@ -22,6 +22,12 @@ hipError_t launch_gate_up(const ExpertGemmArgs &a, WFormat wf, int max_groups, i
 hipError_t launch_down(const ExpertGemmArgs &a, WFormat wf, int max_groups, int max_rows,
                        hipStream_t st);
 
+// Tiled grouped GEMM (large token counts).  max_rows_total bounds the rows of
+// all groups together, max_groups the number of groups.
+hipError_t launch_tiled(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total,
+                        int max_groups, hipStream_t st);
+int tiled_tile_rows();
+
 hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t st);
 

@@ -1,8 +1,9 @@
 // Permutation of the T*K (token, k) slots by expert: per-expert counts (the
 // kept-slot counts of SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own
 // DSpark draft (stacked on #1035)", tokens_per_expert commit note), exclusive
-// offsets, the list of active experts and the row <-> slot maps that the
-// grouped expert GEMMs and the combine read.
+// offsets, the active experts split into two lists by row count (the grouped
+// GEMMs run narrow and wide row tiles as separate launches) and the row <->
+// slot maps that the grouped expert GEMMs and the combine read.
 //
 // One workgroup of 1024 threads: LDS histogram (integer atomics, so the
 // counts are exact and order independent), block scan over the experts,
@@ -55,18 +56,32 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) 
 
   const int v = tid < a.E ? hist[tid] : 0;
   const int incl = block_inclusive_scan(v, wsum);
-  const int act = (tid < a.E && v > 0) ? 1 : 0;
-  const int act_incl = block_inclusive_scan(act, wsum);
+  const int small = (tid < a.E && v > 0 && v <= a.small_rows) ? 1 : 0;
+  const int big = (tid < a.E && v > a.small_rows) ? 1 : 0;
+  const int small_incl = block_inclusive_scan(small, wsum);
+  const int big_incl = block_inclusive_scan(big, wsum);
+  const int any = small | big;
+  const int any_incl = block_inclusive_scan(any, wsum);
+  const int mtiles = (v + a.tile_rows - 1) / a.tile_rows;
+  const int mt_incl = block_inclusive_scan(mtiles, wsum);
   if (tid < a.E) {
     a.counts[tid] = v;
     if (a.user_counts) a.user_counts[tid] = v;
     a.offsets[tid] = incl - v;
-    if (act) a.active[act_incl - 1] = tid;
+    if (small) a.active[small_incl - 1] = tid;
+    if (big) a.active_big[big_incl - 1] = tid;
+    if (any) {
+      a.active_all[any_incl - 1] = tid;
+      a.mtile_prefix[any_incl] = mt_incl;
+    }
     hist[tid] = incl - v;  // becomes the scatter cursor
   }
   if (tid == kPermuteThreads - 1) {
     a.offsets[a.E] = incl;
-    a.n_active[0] = act_incl;
+    a.n_active[0] = small_incl;
+    a.n_active_big[0] = big_incl;
+    a.n_active_all[0] = any_incl;
+    a.mtile_prefix[0] = 0;
   }
   __syncthreads();
 

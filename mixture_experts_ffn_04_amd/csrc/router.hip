@@ -168,14 +168,25 @@ __global__ __launch_bounds__(256) void router_select(SelectArgs a) {
   // the optional logit bias is one f32 add after that ([SF941] "What")
   float l[J], s[J], c[J];
   bool valid[J];
+  double v[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    valid[j] = lane + 64 * j < a.E;
+    v[j] = valid[j] ? prow[lane + 64 * j] : 0.0;
+  }
+#pragma unroll 4
+  for (int sp = 1; sp < a.n_split; ++sp) {
+    double p[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) p[j] = valid[j] ? prow[sp * slice + lane + 64 * j] : 0.0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] += p[j];
+  }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
-    valid[j] = e < a.E;
     if (valid[j]) {
-      double v = prow[e];
-      for (int sp = 1; sp < a.n_split; ++sp) v += prow[sp * slice + e];
-      l[j] = (float)v;
+      l[j] = (float)v[j];
       if (a.router_bias) l[j] += a.router_bias[e];
     } else {
       l[j] = NEG_INF;

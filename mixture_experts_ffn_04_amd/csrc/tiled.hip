@@ -1,0 +1,367 @@
+// Tiled grouped expert GEMMs for large token counts (matrix-core bound).
+//
+// Same operations as the streaming kernels in experts.hip (gate_up + SwiGLU,
+// down + optional per-expert bias; bf16 or MXFP4 weights, bf16 activations),
+// organised for operand reuse: a workgroup computes a 128-token x 256-weight-
+// row tile, staging 64-deep slices of both operands in LDS (double-buffered:
+// the next slice's global loads are issued before the current slice's MFMAs
+// and stored to the other buffer afterwards).  Four waves each compute a
+// 64-token x 128-weight-row sub-tile with 16x16x32 bf16 MFMAs (weights as
+// operand A, tokens as operand B, so a lane ends with four adjacent output
+// columns of one token).  gate_up tiles hold 128 gate rows and the matching
+// 128 up rows, and each wave takes 64 of each, so SwiGLU pairs meet in one
+// lane.  MXFP4 codes are decoded to bf16 on their way into LDS.
+//
+// A persistent grid walks the (expert, column tile, row tile) list built from
+// the per-expert row counts (mtile_prefix); row tiles of one column tile are
+// consecutive, so the weight tile is reused from L2.
+//
+// [SF1073] SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own DSpark draft
+// (stacked on #1035)" (clamped SwiGLU; stacked gate_up_proj; FP4 experts two
+// codes per byte, low nibble first, E8M0 scale per 32 inputs) and [MI143]
+// MoE-Infinity PR #143 (output-major MXFP4 blocks, expert biases).
+#include "kernels.hpp"
+#include "tile.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int TBM = 128;          // tokens per tile
+constexpr int TBN = 256;          // weight rows per tile
+constexpr int TBK = 64;           // reduction slice
+constexpr int TLD = TBK + 8;      // padded LDS row (elements): conflict-free 16 B reads
+constexpr int TTHREADS = 256;
+
+__device__ __forceinline__ float swiglu_t(float g, float u, float lim) {
+  g = fminf(g, lim);
+  u = fminf(fmaxf(u, -lim), lim);
+  return g / (1.f + expf(-g)) * u;
+}
+
+struct TileCoord {
+  int g, nrows, row0;  // group
+  int m0, n0;          // first token row (in the group) and first column
+};
+
+__device__ __forceinline__ bool tile_coord(const TiledGemmArgs &t, int tile, int n_tiles, TileCoord &c) {
+  const ExpertGemmArgs &a = t.g;
+  if (!a.counts) {  // one group of single_rows rows
+    const int mt = (a.single_rows + TBM - 1) / TBM;
+    c.g = 0;
+    c.nrows = a.single_rows;
+    c.row0 = 0;
+    c.m0 = (tile % mt) * TBM;
+    c.n0 = tile / mt;  // column tile index; scaled by the caller
+    return true;
+  }
+  const int q = tile / n_tiles;  // global row-tile index (of all experts)
+  // binary search: mtile_prefix[ai] <= q < mtile_prefix[ai + 1]
+  int lo = 0, hi = t.n_active_all[0];
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (t.mtile_prefix[mid] <= q) lo = mid;
+    else hi = mid;
+  }
+  const int mt_e = t.mtile_prefix[lo + 1] - t.mtile_prefix[lo];
+  const int local = tile - t.mtile_prefix[lo] * n_tiles;
+  c.g = t.active_all[lo];
+  c.nrows = a.counts[c.g];
+  c.row0 = a.offsets[c.g];
+  c.m0 = (local % mt_e) * TBM;
+  c.n0 = local / mt_e;  // column tile index; scaled by the caller
+  return true;
+}
+
+}  // namespace
+
+template <bool GATE_UP, int WF, bool GATHER, bool LO>
+__global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
+  const ExpertGemmArgs &a = ta.g;
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t *Xs = smem;                         // [2][TBM][TLD]
+  uint16_t *Ws = smem + 2 * TBM * TLD;         // [2][TBN][TLD]
+  uint16_t *Xl = Ws + 2 * TBN * TLD;           // [2][TBM][TLD] low halves of h (down, LO)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // column tiles: gate_up covers 128 gate columns per tile, down 256 columns
+  const int cols_per_tile = GATE_UP ? TBN / 2 : TBN;
+  const int n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
+  int total;
+  if (a.counts) total = ta.mtile_prefix[ta.n_active_all[0]] * n_tiles;
+  else total = ((a.single_rows + TBM - 1) / TBM) * n_tiles;
+
+  const uint16_t *A = static_cast<const uint16_t *>(a.A);
+  const int nks = (a.Kdim + TBK - 1) / TBK;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    TileCoord c;
+    tile_coord(ta, tile, n_tiles, c);
+    const int col0 = c.n0 * cols_per_tile;
+
+    // ---- per-thread global source rows for the loads of every slice ----
+    // X: 128 rows x 8 chunks of 16 B: chunk id = tid + 256 i, i < 4
+    const uint16_t *xsrc[4];
+    int xrow[4], xkc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cid = tid + TTHREADS * i;
+      xrow[i] = cid >> 3;
+      xkc[i] = cid & 7;
+      const int r = min(c.m0 + xrow[i], c.nrows - 1);
+      size_t ar;
+      if constexpr (GATHER)
+        ar = (size_t)(a.perm[c.row0 + r] / a.topk);
+      else
+        ar = (size_t)(c.row0 + r);
+      xsrc[i] = A + ar * a.Kdim;
+    }
+    const uint16_t *xlsrc[4];
+    if constexpr (LO) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xlsrc[i] = static_cast<const uint16_t *>(a.A_lo) +
+                   (size_t)(c.row0 + min(c.m0 + xrow[i], c.nrows - 1)) * a.Kdim;
+    }
+    // W rows of this tile: LDS row r -> global weight row
+    auto wrow_of = [&](int r) {
+      int g;
+      if constexpr (GATE_UP) g = r < TBN / 2 ? col0 + r : a.N + col0 + (r - TBN / 2);
+      else g = col0 + r;
+      const int lim = GATE_UP ? (r < TBN / 2 ? a.N - 1 : 2 * a.N - 1) : a.N - 1;
+      return min(g, lim);
+    };
+
+    constexpr int WCH = (WF == W_MXFP4) ? 2 : 8;   // W chunks per thread per slice
+    u32x4_t xbuf[4], xlbuf[4], wbuf[WCH];
+    uint32_t sbuf[WCH];
+    int wr_l[WCH], wkc[WCH];
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int cid = tid + TTHREADS * i;
+      if constexpr (WF == W_MXFP4) {  // 256 rows x 2 halves of 32 elements (16 code bytes)
+        wr_l[i] = cid >> 1;
+        wkc[i] = cid & 1;
+      } else {  // 256 rows x 8 chunks of 8 elements
+        wr_l[i] = cid >> 3;
+        wkc[i] = cid & 7;
+      }
+    }
+    const size_t wbase_rows = (size_t)c.g;
+
+    auto gload = [&](int ks) {
+      const int k0 = ks * TBK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = k0 + xkc[i] * 8;
+        xbuf[i] = k < a.Kdim ? load16(xsrc[i] + k) : u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (LO) xlbuf[i] = k < a.Kdim ? load16(xlsrc[i] + k) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < WCH; ++i) {
+        const int grow = wrow_of(wr_l[i]);
+        if constexpr (WF == W_MXFP4) {
+          const int k = k0 + wkc[i] * 32;
+          if (k < a.Kdim) {
+            const uint8_t *cp = static_cast<const uint8_t *>(a.W) + wbase_rows * a.w_stride +
+                                (size_t)grow * (a.Kdim / 2) + k / 2;
+            wbuf[i] = load_stream16(cp);
+            sbuf[i] = a.Wscale[wbase_rows * a.s_stride + (size_t)grow * (a.Kdim / 32) + k / 32];
+          } else {
+            wbuf[i] = u32x4_t{0u, 0u, 0u, 0u};
+            sbuf[i] = 127u;
+          }
+        } else {
+          const int k = k0 + wkc[i] * 8;
+          const uint16_t *wp = static_cast<const uint16_t *>(a.W) + wbase_rows * a.w_stride + (size_t)grow * a.Kdim;
+          wbuf[i] = k < a.Kdim ? load16(wp + k) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    auto lstore = [&](int buf) {
+      uint16_t *xs = Xs + buf * TBM * TLD;
+      uint16_t *ws = Ws + buf * TBN * TLD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t *>(xs + xrow[i] * TLD + xkc[i] * 8) = xbuf[i];
+      if constexpr (LO) {
+        uint16_t *xl = Xl + buf * TBM * TLD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t *>(xl + xrow[i] * TLD + xkc[i] * 8) = xlbuf[i];
+      }
+#pragma unroll
+      for (int i = 0; i < WCH; ++i) {
+        if constexpr (WF == W_MXFP4) {
+          const float sc = e8m0_to_f32(sbuf[i]);
+          uint16_t *dst = ws + wr_l[i] * TLD + wkc[i] * 32;
+          *reinterpret_cast<u32x4_t *>(dst + 0) = decode_e2m1x8(wbuf[i].x, sc);
+          *reinterpret_cast<u32x4_t *>(dst + 8) = decode_e2m1x8(wbuf[i].y, sc);
+          *reinterpret_cast<u32x4_t *>(dst + 16) = decode_e2m1x8(wbuf[i].z, sc);
+          *reinterpret_cast<u32x4_t *>(dst + 24) = decode_e2m1x8(wbuf[i].w, sc);
+        } else {
+          *reinterpret_cast<u32x4_t *>(ws + wr_l[i] * TLD + wkc[i] * 8) = wbuf[i];
+        }
+      }
+    };
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int cf = 0; cf < 8; ++cf)
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) acc[cf][tf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // LDS row of this wave's column fragment cf
+    auto wfrag_row = [&](int cf) {
+      if constexpr (GATE_UP) return cf < 4 ? wn * 64 + cf * 16 : TBN / 2 + wn * 64 + (cf - 4) * 16;
+      else return wn * 128 + cf * 16;
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+      const int buf = ks & 1;
+      if (ks + 1 < nks) gload(ks + 1);
+      const uint16_t *xs = Xs + buf * TBM * TLD;
+      const uint16_t *ws = Ws + buf * TBN * TLD;
+#pragma unroll
+      for (int kk = 0; kk < TBK / 32; ++kk) {
+        u32x4_t xf[4], wf[8];
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf)
+          xf[tf] = *reinterpret_cast<const u32x4_t *>(xs + (wm * 64 + tf * 16 + lr) * TLD + kk * 32 + lg * 8);
+#pragma unroll
+        for (int cf = 0; cf < 8; ++cf)
+          wf[cf] = *reinterpret_cast<const u32x4_t *>(ws + (wfrag_row(cf) + lr) * TLD + kk * 32 + lg * 8);
+#pragma unroll
+        for (int cf = 0; cf < 8; ++cf)
+#pragma unroll
+          for (int tf = 0; tf < 4; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
+        if constexpr (LO) {  // same weight fragments times the low halves of h
+          const uint16_t *xl = Xl + buf * TBM * TLD;
+#pragma unroll
+          for (int tf = 0; tf < 4; ++tf)
+            xf[tf] = *reinterpret_cast<const u32x4_t *>(xl + (wm * 64 + tf * 16 + lr) * TLD + kk * 32 + lg * 8);
+#pragma unroll
+          for (int cf = 0; cf < 8; ++cf)
+#pragma unroll
+            for (int tf = 0; tf < 4; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
+        }
+      }
+      if (ks + 1 < nks) lstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogue ----
+#pragma unroll
+    for (int tf = 0; tf < 4; ++tf) {
+      const int row = c.m0 + wm * 64 + tf * 16 + lr;
+      if (row >= c.nrows) continue;
+      if constexpr (GATE_UP) {
+#pragma unroll
+        for (int cf = 0; cf < 4; ++cf) {
+          const int col = col0 + wn * 64 + cf * 16 + 4 * lg;
+          if (col >= a.N) continue;
+          float gb[4] = {0.f, 0.f, 0.f, 0.f}, ub[4] = {0.f, 0.f, 0.f, 0.f};
+          if (a.bias) {
+            const uint16_t *b = static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              gb[q] = bf16_to_f32(b[col + q]);
+              ub[q] = bf16_to_f32(b[a.N + col + q]);
+            }
+          }
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float hv = swiglu_t(acc[cf][tf][q] + gb[q], acc[cf + 4][tf][q] + ub[q], a.limit);
+            hb[q] = f32_to_bf16(hv);
+            lb[q] = f32_to_bf16(hv - bf16_to_f32(hb[q]));
+          }
+          const size_t off = (size_t)(c.row0 + row) * a.N + col;
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) =
+              make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+          if (a.out_lo)
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out_lo) + off) =
+                make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+        }
+      } else {
+        int slot = 0;
+        float wt = 0.f;
+        if (a.direct_out) {
+          slot = a.perm[c.row0 + row];
+          wt = a.weights[slot];
+        }
+#pragma unroll
+        for (int cf = 0; cf < 8; ++cf) {
+          const int col = col0 + wn * 128 + cf * 16 + 4 * lg;
+          if (col >= a.N) continue;
+          float4 v = make_float4(acc[cf][tf][0], acc[cf][tf][1], acc[cf][tf][2], acc[cf][tf][3]);
+          if (a.bias) {
+            const uint16_t *b = static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride + col;
+            v.x += bf16_to_f32(b[0]);
+            v.y += bf16_to_f32(b[1]);
+            v.z += bf16_to_f32(b[2]);
+            v.w += bf16_to_f32(b[3]);
+          }
+          if (a.direct_out) {
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.direct_out) + (size_t)slot * a.N + col) =
+                make_uint2(f32_to_bf16(wt * v.x) | (f32_to_bf16(wt * v.y) << 16),
+                           f32_to_bf16(wt * v.z) | (f32_to_bf16(wt * v.w) << 16));
+          } else {
+            *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + (size_t)(c.row0 + row) * a.N + col) = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+static size_t tiled_lds_bytes(bool lo) {
+  return (size_t)2 * (TBM + TBN + (lo ? TBM : 0)) * TLD * sizeof(uint16_t);
+}
+
+template <bool GATE_UP, int WF, bool GATHER, bool LO>
+static hipError_t launch_tiled_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
+  auto kern = expert_tiled<GATE_UP, WF, GATHER, LO>;
+  static bool attr_set = false;  // LDS above 64 KB must be allowed once per kernel
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)tiled_lds_bytes(LO));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(TTHREADS), tiled_lds_bytes(LO), st, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiled(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total,
+                        int max_groups, hipStream_t st) {
+  const ExpertGemmArgs &a = t.g;
+  const int cols_per_tile = gate_up ? TBN / 2 : TBN;
+  const long n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
+  const long mtiles_bound = (max_rows_total + TBM - 1) / TBM + max_groups;
+  const long tiles_bound = mtiles_bound * n_tiles;
+  const bool gather = gate_up && a.perm != nullptr;
+  if (gate_up) {
+    if (wf == W_MXFP4)
+      return gather ? launch_tiled_t<true, W_MXFP4, true, false>(t, tiles_bound, st)
+                    : launch_tiled_t<true, W_MXFP4, false, false>(t, tiles_bound, st);
+    return gather ? launch_tiled_t<true, W_BF16, true, false>(t, tiles_bound, st)
+                  : launch_tiled_t<true, W_BF16, false, false>(t, tiles_bound, st);
+  }
+  if (a.A_lo) {
+    if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, true>(t, tiles_bound, st);
+    return launch_tiled_t<false, W_BF16, false, true>(t, tiles_bound, st);
+  }
+  if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, false>(t, tiles_bound, st);
+  return launch_tiled_t<false, W_BF16, false, false>(t, tiles_bound, st);
+}
+
+int tiled_tile_rows() { return TBM; }
+
+}  // namespace moe

@@ -186,9 +186,13 @@ def valid_near_tie(choice_row, picked, tau, wl):
     return bool(np.all(c[picked][:-1] >= c[picked][1:] - tau))
 
 
-def check_output(case: Case, gpu_out: torch.Tensor, ref: np.ndarray, report: dict, rows=None):
+def check_output(case: Case, gpu_out: torch.Tensor, ref: np.ndarray, report: dict, rows=None,
+                 floor_allowance=0.0):
     """Max-abs error relative to the oracle output's RMS, with the bf16
-    rounding floor reported beside it."""
+    rounding floor reported beside it.  `floor_allowance` (used only for
+    deliberately heavy-tailed outputs, where rounding the output to bf16 alone
+    exceeds the bound) adds that many times the output's own bf16 rounding
+    error to the bound."""
     got = gpu_out.float().cpu().numpy().astype(np.float64)
     if rows is not None:
         got = got[rows]
@@ -197,8 +201,9 @@ def check_output(case: Case, gpu_out: torch.Tensor, ref: np.ndarray, report: dic
     report.update(out_rms=rms, out_maxabs_err=err, out_err_over_rms=err / rms if rms else err)
     if case.wl.act_dtype == "bf16":
         floor = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
-        report["bf16_floor_over_rms"] = float(np.max(np.abs(floor - ref))) / rms if rms else 0.0
-        assert err <= BF16_TOL * rms, report
+        floor_abs = float(np.max(np.abs(floor - ref))) if ref.size else 0.0
+        report["bf16_floor_over_rms"] = floor_abs / rms if rms else 0.0
+        assert err <= BF16_TOL * rms + floor_allowance * floor_abs, report
     else:
         assert err <= F32_TOL * rms + 1e-6, report
     assert np.all(np.isfinite(got))

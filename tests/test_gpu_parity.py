@@ -50,9 +50,19 @@ SMALL = [
        expert_linear_bias_std=0.02),
     Wl("gpt_oss_like_mxfp4_t150", T=150, H=256, E=8, I=128, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
        expert_linear_bias_std=0.02),
+    Wl("mxfp4_wide_scales", T=40, H=512, E=8, I=256, K=2, w_dtype="mxfp4", mx_scale_lo=-40,
+       mx_scale_hi=20),
+    Wl("top1_with_shared", T=40, H=256, E=8, I=64, K=1, shared_I=64, shared_gated=True),
     Wl("all_experts_k_eq_e", T=20, H=256, E=8, I=64, K=8),
     Wl("single_expert_dense", T=24, H=256, E=1, I=96, K=1),
     Wl("e1024_top16", T=24, H=256, E=1024, I=32, K=16),
+    # tiled kernels (routed from 512 tokens, shared from 256), ragged column
+    # tiles (160 = 128 + 32) and ragged 64-deep reduction slices (160, 96)
+    Wl("tiled_routed_t600", T=600, H=384, E=8, I=160, K=2, shared_I=96, shared_gated=True),
+    Wl("tiled_mxfp4_t520", T=520, H=352, E=8, I=288, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
+       expert_linear_bias_std=0.02),
+    Wl("tiled_top1_direct_t640", T=640, H=256, E=4, I=128, K=1),
+    Wl("tiled_shared_only_t300", T=300, H=256, E=16, I=64, K=4, shared_I=320, expert_bias_std=0.05),
 ]
 
 
@@ -71,7 +81,9 @@ def test_small_full_parity(wl):
     gi = r.indices.cpu().numpy()
     for t in np.nonzero(mism)[0]:      # near-tie tokens: the oracle on the GPU's pick
         ref[t] = case.oracle_token(t, gi[t], ow[t])
-    check_output(case, out, ref, rep)
+    # scales over 2^-40..2^20 make the output so heavy-tailed that its own bf16
+    # rounding exceeds 2e-2 of its RMS; allow two of those roundings there
+    check_output(case, out, ref, rep, floor_allowance=2.0 if wl.name == "mxfp4_wide_scales" else 0.0)
     _report(wl.name, rep)
 
 
