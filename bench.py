@@ -248,7 +248,21 @@ def main(argv=None):
                     help="also time the same family at this token count (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (the reference kernel "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args(argv)
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "

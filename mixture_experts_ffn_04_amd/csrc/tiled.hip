@@ -29,8 +29,8 @@ namespace {
 
 constexpr int TBM = 128;          // tokens per tile
 constexpr int TBN = 256;          // weight rows per tile
-constexpr int TBK = 64;           // reduction slice
-constexpr int TLD = TBK + 8;      // padded LDS row (elements): conflict-free 16 B reads
+constexpr int TBK = 32;           // reduction slice
+constexpr int TLD = TBK + 8;      // padded LDS row (80 B): conflict-free 16 B fragment reads
 constexpr int TTHREADS = 256;
 
 __device__ __forceinline__ float swiglu_t(float g, float u, float lim) {
@@ -76,7 +76,7 @@ __device__ __forceinline__ bool tile_coord(const TiledGemmArgs &t, int tile, int
 }  // namespace
 
 template <bool GATE_UP, int WF, bool GATHER, bool LO>
-__global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
+__global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
   const ExpertGemmArgs &a = ta.g;
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t *Xs = smem;                         // [2][TBM][TLD]
@@ -98,20 +98,29 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
   const uint16_t *A = static_cast<const uint16_t *>(a.A);
   const int nks = (a.Kdim + TBK - 1) / TBK;
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  // Workgroups are dispatched to the 8 XCDs round-robin; the tile list is cut
+  // into 8 contiguous chunks so that the workgroups of one XCD walk one chunk
+  // and share its weight and token tiles through their L2.
+  const int nx = gridDim.x % 8 == 0 ? 8 : 1;
+  const int xcd = blockIdx.x % nx, wg_in_xcd = blockIdx.x / nx, wgs_per_xcd = gridDim.x / nx;
+  const int chunk = (total + nx - 1) / nx;
+  for (int local = wg_in_xcd; local < chunk; local += wgs_per_xcd) {
+    const int tile = xcd * chunk + local;
+    if (tile >= total) break;
     TileCoord c;
     tile_coord(ta, tile, n_tiles, c);
     const int col0 = c.n0 * cols_per_tile;
 
     // ---- per-thread global source rows for the loads of every slice ----
-    // X: 128 rows x 8 chunks of 16 B: chunk id = tid + 256 i, i < 4
-    const uint16_t *xsrc[4];
-    int xrow[4], xkc[4];
+    // X: 128 rows x 4 chunks of 16 B: chunk id = tid + 256 i, i < 2
+    constexpr int XCH = TBM * (TBK / 8) / TTHREADS;
+    const uint16_t *xsrc[XCH];
+    int xrow[XCH], xkc[XCH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < XCH; ++i) {
       const int cid = tid + TTHREADS * i;
-      xrow[i] = cid >> 3;
-      xkc[i] = cid & 7;
+      xrow[i] = cid / (TBK / 8);
+      xkc[i] = cid % (TBK / 8);
       const int r = min(c.m0 + xrow[i], c.nrows - 1);
       size_t ar;
       if constexpr (GATHER)
@@ -120,10 +129,10 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
         ar = (size_t)(c.row0 + r);
       xsrc[i] = A + ar * a.Kdim;
     }
-    const uint16_t *xlsrc[4];
+    const uint16_t *xlsrc[XCH];
     if constexpr (LO) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < XCH; ++i)
         xlsrc[i] = static_cast<const uint16_t *>(a.A_lo) +
                    (size_t)(c.row0 + min(c.m0 + xrow[i], c.nrows - 1)) * a.Kdim;
     }
@@ -136,19 +145,21 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
       return min(g, lim);
     };
 
-    constexpr int WCH = (WF == W_MXFP4) ? 2 : 8;   // W chunks per thread per slice
-    u32x4_t xbuf[4], xlbuf[4], wbuf[WCH];
+    // W: bf16 256 rows x 4 chunks of 8 elements; MXFP4 256 rows x one 32-element
+    // block (16 code bytes + 1 scale)
+    constexpr int WCH = (WF == W_MXFP4) ? TBN / TTHREADS : TBN * (TBK / 8) / TTHREADS;
+    u32x4_t xbuf[XCH], xlbuf[XCH], wbuf[WCH];
     uint32_t sbuf[WCH];
     int wr_l[WCH], wkc[WCH];
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int cid = tid + TTHREADS * i;
-      if constexpr (WF == W_MXFP4) {  // 256 rows x 2 halves of 32 elements (16 code bytes)
-        wr_l[i] = cid >> 1;
-        wkc[i] = cid & 1;
-      } else {  // 256 rows x 8 chunks of 8 elements
-        wr_l[i] = cid >> 3;
-        wkc[i] = cid & 7;
+      if constexpr (WF == W_MXFP4) {
+        wr_l[i] = cid;
+        wkc[i] = 0;
+      } else {
+        wr_l[i] = cid / (TBK / 8);
+        wkc[i] = cid % (TBK / 8);
       }
     }
     const size_t wbase_rows = (size_t)c.g;
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
     auto gload = [&](int ks) {
       const int k0 = ks * TBK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < XCH; ++i) {
         const int k = k0 + xkc[i] * 8;
         xbuf[i] = k < a.Kdim ? load16(xsrc[i] + k) : u32x4_t{0u, 0u, 0u, 0u};
         if constexpr (LO) xlbuf[i] = k < a.Kdim ? load16(xlsrc[i] + k) : u32x4_t{0u, 0u, 0u, 0u};
@@ -165,12 +176,11 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
       for (int i = 0; i < WCH; ++i) {
         const int grow = wrow_of(wr_l[i]);
         if constexpr (WF == W_MXFP4) {
-          const int k = k0 + wkc[i] * 32;
-          if (k < a.Kdim) {
+          if (k0 < a.Kdim) {
             const uint8_t *cp = static_cast<const uint8_t *>(a.W) + wbase_rows * a.w_stride +
-                                (size_t)grow * (a.Kdim / 2) + k / 2;
+                                (size_t)grow * (a.Kdim / 2) + k0 / 2;
             wbuf[i] = load_stream16(cp);
-            sbuf[i] = a.Wscale[wbase_rows * a.s_stride + (size_t)grow * (a.Kdim / 32) + k / 32];
+            sbuf[i] = a.Wscale[wbase_rows * a.s_stride + (size_t)grow * (a.Kdim / 32) + k0 / 32];
           } else {
             wbuf[i] = u32x4_t{0u, 0u, 0u, 0u};
             sbuf[i] = 127u;
@@ -186,17 +196,17 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
       uint16_t *xs = Xs + buf * TBM * TLD;
       uint16_t *ws = Ws + buf * TBN * TLD;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t *>(xs + xrow[i] * TLD + xkc[i] * 8) = xbuf[i];
+      for (int i = 0; i < XCH; ++i) *reinterpret_cast<u32x4_t *>(xs + xrow[i] * TLD + xkc[i] * 8) = xbuf[i];
       if constexpr (LO) {
         uint16_t *xl = Xl + buf * TBM * TLD;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t *>(xl + xrow[i] * TLD + xkc[i] * 8) = xlbuf[i];
+        for (int i = 0; i < XCH; ++i) *reinterpret_cast<u32x4_t *>(xl + xrow[i] * TLD + xkc[i] * 8) = xlbuf[i];
       }
 #pragma unroll
       for (int i = 0; i < WCH; ++i) {
         if constexpr (WF == W_MXFP4) {
           const float sc = e8m0_to_f32(sbuf[i]);
-          uint16_t *dst = ws + wr_l[i] * TLD + wkc[i] * 32;
+          uint16_t *dst = ws + wr_l[i] * TLD;
           *reinterpret_cast<u32x4_t *>(dst + 0) = decode_e2m1x8(wbuf[i].x, sc);
           *reinterpret_cast<u32x4_t *>(dst + 8) = decode_e2m1x8(wbuf[i].y, sc);
           *reinterpret_cast<u32x4_t *>(dst + 16) = decode_e2m1x8(wbuf[i].z, sc);
@@ -219,12 +229,7 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
       else return wn * 128 + cf * 16;
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-      const int buf = ks & 1;
-      if (ks + 1 < nks) gload(ks + 1);
+    auto compute = [&](int buf) {
       const uint16_t *xs = Xs + buf * TBM * TLD;
       const uint16_t *ws = Ws + buf * TBN * TLD;
 #pragma unroll
@@ -251,6 +256,17 @@ __global__ __launch_bounds__(TTHREADS) void expert_tiled(TiledGemmArgs ta) {
             for (int tf = 0; tf < 4; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
         }
       }
+    };
+
+    // double-buffered LDS: the next slice's global loads are in flight while
+    // the current slice is multiplied, then stored to the other buffer
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+      const int buf = ks & 1;
+      if (ks + 1 < nks) gload(ks + 1);
+      compute(buf);
       if (ks + 1 < nks) lstore(buf ^ 1);
       __syncthreads();
     }
@@ -334,7 +350,7 @@ static hipError_t launch_tiled_t(const TiledGemmArgs &t, long tiles_bound, hipSt
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));
+  const int grid = (int)std::max(1L, std::min(tiles_bound, 512L));  // two per CU
   hipLaunchKernelGGL(kern, dim3(grid), dim3(TTHREADS), tiled_lds_bytes(LO), st, t);
   return hipGetLastError();
 }
