@@ -46,10 +46,6 @@ int fail(int code, const char *fmt, ...) {
 
 int ok() { return MOE_OK; }
 
-// Experts with at most this many rows run the narrow (one 16-row tile) GEMM
-// launch; the others the wide one.
-constexpr int kSmallRows = 16;
-
 // Token counts from which the expert GEMMs use the LDS-tiled kernels (routed
 // experts, shared expert); below them the weight-streaming kernels.
 constexpr int kTiledMinTokens = 512;
@@ -63,10 +59,27 @@ bool has_shared(const moe_config &c) { return c.shared_I > 0; }
 bool has_shared_gate(const moe_config &c) { return c.shared_I > 0 && c.shared_gated; }
 int logits_ld(const moe_config &c) { return c.E + (has_shared_gate(c) ? 1 : 0); }
 
+// Which kernels run the routed expert GEMMs, and the rows per chunk of the
+// expert-sorted rows that the permutation cuts for them.
+struct GemmPlan {
+  bool tiled;       // routed experts on the LDS-tiled kernel
+  bool tiled_shared;
+  int chunk_rows;   // streaming kernel chunks (tiled: its row tile)
+};
+
+GemmPlan gemm_plan(const moe_config &c) {
+  GemmPlan p;
+  const bool mfma = c.w_dtype != MOE_DTYPE_F32;
+  p.tiled = mfma && c.T >= kTiledMinTokens;
+  p.tiled_shared = c.act_dtype != MOE_DTYPE_F32 && c.T >= kTiledMinTokensShared;
+  p.chunk_rows = p.tiled ? tiled_tile_rows() : stream_chunk_rows((long)c.T * c.K, c.E);
+  return p;
+}
+
 // Workspace carve-up; every buffer starts on a 256-byte boundary.
 struct Layout {
-  size_t logits, gamma, scores, indices, weights, counts, offsets, active, n_active, active_big,
-      n_active_big, active_all, n_active_all, mtile_prefix, perm, inv;
+  size_t logits, gamma, scores, indices, weights, counts, offsets, active_all, n_active_all,
+      mtile_prefix, chunks, n_chunks, perm, inv;
   size_t h, y, sh_h, sh_y, total;
 };
 
@@ -88,13 +101,11 @@ Layout make_layout(const moe_config &c) {
   L.weights = take(T * K * 4);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
-  L.active = take(E * 4);
-  L.n_active = take(4);
-  L.active_big = take(E * 4);
-  L.n_active_big = take(4);
   L.active_all = take(E * 4);
   L.n_active_all = take(4);
   L.mtile_prefix = take((E + 1) * 4);
+  L.chunks = take((T * K + E) * 16);
+  L.n_chunks = take(4);
   L.perm = take(T * K * 4);
   L.inv = take(T * K * 4);
   // bf16 activations keep h as a bf16 (hi, lo) pair: h = hi + lo to ~16 bits
@@ -202,15 +213,13 @@ int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const 
     pa.counts = reinterpret_cast<int32_t *>(ws + L.counts);
     pa.user_counts = user_counts;
     pa.offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
-    pa.active = reinterpret_cast<int32_t *>(ws + L.active);
-    pa.n_active = reinterpret_cast<int32_t *>(ws + L.n_active);
-    pa.active_big = reinterpret_cast<int32_t *>(ws + L.active_big);
-    pa.n_active_big = reinterpret_cast<int32_t *>(ws + L.n_active_big);
-    pa.small_rows = kSmallRows;
     pa.active_all = reinterpret_cast<int32_t *>(ws + L.active_all);
     pa.n_active_all = reinterpret_cast<int32_t *>(ws + L.n_active_all);
     pa.mtile_prefix = reinterpret_cast<int32_t *>(ws + L.mtile_prefix);
     pa.tile_rows = tiled_tile_rows();
+    pa.chunks = reinterpret_cast<int4 *>(ws + L.chunks);
+    pa.n_chunks = reinterpret_cast<int32_t *>(ws + L.n_chunks);
+    pa.chunk_rows = gemm_plan(c).chunk_rows;
     pa.perm = reinterpret_cast<int32_t *>(ws + L.perm);
     pa.inv = reinterpret_cast<int32_t *>(ws + L.inv);
     pa.n_slots = c.T * c.K;
@@ -392,23 +401,39 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
 
   const WFormat wf = c.w_dtype == MOE_DTYPE_F32 ? W_F32 : (c.w_dtype == MOE_DTYPE_BF16 ? W_BF16 : W_MXFP4);
   const WFormat af = c.act_dtype == MOE_DTYPE_F32 ? W_F32 : W_BF16;
+  const GemmPlan plan = gemm_plan(c);
   const int32_t *counts_ws = reinterpret_cast<int32_t *>(ws + L.counts);
   const int32_t *offsets_ws = reinterpret_cast<int32_t *>(ws + L.offsets);
-  const int32_t *active_ws = reinterpret_cast<int32_t *>(ws + L.active);
-  const int32_t *n_active_ws = reinterpret_cast<int32_t *>(ws + L.n_active);
+  const int32_t *active_all_ws = reinterpret_cast<int32_t *>(ws + L.active_all);
+  const int32_t *n_active_all_ws = reinterpret_cast<int32_t *>(ws + L.n_active_all);
+  const int32_t *mtile_prefix_ws = reinterpret_cast<int32_t *>(ws + L.mtile_prefix);
+  const int4 *chunks_ws = reinterpret_cast<const int4 *>(ws + L.chunks);
+  const int32_t *n_chunks_ws = reinterpret_cast<int32_t *>(ws + L.n_chunks);
   const int32_t *perm_ws = reinterpret_cast<int32_t *>(ws + L.perm);
-  const int max_groups = (int)std::min<long>(c.E, (long)c.T * c.K);
+  const long slots = (long)c.T * c.K;
+  const int max_groups = (int)std::min<long>(c.E, slots);
+  const long max_chunks = std::min(slots, slots / plan.chunk_rows + max_groups);
   const size_t H = c.H, I = c.I, Is = c.shared_I;
+  const bool hilo = c.act_dtype == MOE_DTYPE_BF16;
+  char *h_lo = ws + L.h + (size_t)c.T * c.K * c.I * 2;
+  char *sh_h_lo = ws + L.sh_h + (size_t)c.T * c.shared_I * 2;
+  // shared expert: one group of T rows, cut into chunks on the fly (narrow
+  // chunks at small T, so that enough work items stream its weights)
+  const int sh_chunk_rows = c.T <= 128 ? 16 : 32;
+  const long sh_chunks = ((long)c.T + sh_chunk_rows - 1) / sh_chunk_rows;
 
   // routed gate_up + SwiGLU over x rows gathered by slot
   ExpertGemmArgs g1{};
   g1.A = x;
   g1.perm = perm_ws;
   g1.topk = c.K;
+  g1.chunks = chunks_ws;
+  g1.n_chunks = n_chunks_ws;
+  g1.chunk_rows = plan.chunk_rows;
   g1.counts = counts_ws;
   g1.offsets = offsets_ws;
-  g1.active = active_ws;
-  g1.n_active = n_active_ws;
+  g1.active = active_all_ws;
+  g1.n_active = n_active_all_ws;
   g1.W = wt->w_gate_up;
   g1.Wscale = wt->w_gate_up_scale;
   g1.w_stride = wf == W_MXFP4 ? 2 * I * H / 2 : 2 * I * H;
@@ -419,32 +444,16 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   g1.bias = wt->b_gate_up;
   g1.bias_stride = 2 * I;
   g1.out = ws + L.h;
-  const bool hilo = c.act_dtype == MOE_DTYPE_BF16;
-  char *h_lo = ws + L.h + (size_t)c.T * c.K * c.I * 2;
-  char *sh_h_lo = ws + L.sh_h + (size_t)c.T * c.shared_I * 2;
   if (hilo) g1.out_lo = h_lo;
   g1.limit = c.swiglu_limit;
-  const int32_t *active_big_ws = reinterpret_cast<int32_t *>(ws + L.active_big);
-  const int32_t *n_active_big_ws = reinterpret_cast<int32_t *>(ws + L.n_active_big);
-  const long slots = (long)c.T * c.K;
-  const int max_big = (int)std::min<long>(c.E, slots / (kSmallRows + 1));
-  const bool tiled = wf != W_F32 && c.T >= kTiledMinTokens;
-  const bool tiled_shared = af != W_F32 && c.T >= kTiledMinTokensShared;
-  const int32_t *active_all_ws = reinterpret_cast<int32_t *>(ws + L.active_all);
-  const int32_t *n_active_all_ws = reinterpret_cast<int32_t *>(ws + L.n_active_all);
-  const int32_t *mtile_prefix_ws = reinterpret_cast<int32_t *>(ws + L.mtile_prefix);
   HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, true, st), "profile event");
-  if (tiled) {
+  if (wf == W_F32) {
+    HIP_TRY(launch_gate_up_f32(g1, max_groups, st), "routed gate_up launch");
+  } else if (plan.tiled) {
     TiledGemmArgs t1{g1, active_all_ws, n_active_all_ws, mtile_prefix_ws};
     HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
   } else {
-    HIP_TRY(launch_gate_up(g1, wf, max_groups, std::min(c.T, kSmallRows), st), "routed gate_up launch");
-    if (max_big > 0) {  // experts with more rows than one narrow tile holds
-      ExpertGemmArgs g1b = g1;
-      g1b.active = active_big_ws;
-      g1b.n_active = n_active_big_ws;
-      HIP_TRY(launch_gate_up(g1b, wf, max_big, c.T, st), "routed gate_up launch");
-    }
+    HIP_TRY(launch_stream(g1, true, wf, max_chunks, st), "routed gate_up launch");
   }
   HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, false, st), "profile event");
 
@@ -452,6 +461,7 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
     ExpertGemmArgs s1{};
     s1.A = x;
     s1.single_rows = c.T;
+    s1.chunk_rows = sh_chunk_rows;
     s1.W = wt->sh_gate_up;
     s1.Kdim = c.H;
     s1.N = c.shared_I;
@@ -460,11 +470,13 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
     if (hilo) s1.out_lo = sh_h_lo;
     s1.limit = c.swiglu_limit;
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, true, st), "profile event");
-    if (tiled_shared) {
+    if (af == W_F32) {
+      HIP_TRY(launch_gate_up_f32(s1, 1, st), "shared gate_up launch");
+    } else if (plan.tiled_shared) {
       TiledGemmArgs ts{s1, nullptr, nullptr, nullptr};
       HIP_TRY(launch_tiled(ts, true, af, c.T, 1, st), "shared gate_up launch");
     } else {
-      HIP_TRY(launch_gate_up(s1, af, 1, c.T, st), "shared gate_up launch");
+      HIP_TRY(launch_stream(s1, true, af, sh_chunks, st), "shared gate_up launch");
     }
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, false, st), "profile event");
   }
@@ -473,10 +485,13 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   ExpertGemmArgs g2{};
   g2.A = ws + L.h;
   if (hilo) g2.A_lo = h_lo;
+  g2.chunks = chunks_ws;
+  g2.n_chunks = n_chunks_ws;
+  g2.chunk_rows = plan.chunk_rows;
   g2.counts = counts_ws;
   g2.offsets = offsets_ws;
-  g2.active = active_ws;
-  g2.n_active = n_active_ws;
+  g2.active = active_all_ws;
+  g2.n_active = n_active_all_ws;
   g2.W = wt->w_down;
   g2.Wscale = wt->w_down_scale;
   g2.w_stride = wf == W_MXFP4 ? H * I / 2 : H * I;
@@ -496,17 +511,13 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
     g2.weights = rb.weights;
   }
   HIP_TRY(profile_mark(MOE_STAGE_DOWN, true, st), "profile event");
-  if (tiled) {
+  if (wf == W_F32) {
+    HIP_TRY(launch_down_f32(g2, max_groups, st), "routed down launch");
+  } else if (plan.tiled) {
     TiledGemmArgs t2{g2, active_all_ws, n_active_all_ws, mtile_prefix_ws};
     HIP_TRY(launch_tiled(t2, false, wf, slots, max_groups, st), "routed down launch");
   } else {
-    HIP_TRY(launch_down(g2, wf, max_groups, std::min(c.T, kSmallRows), st), "routed down launch");
-    if (max_big > 0) {  // experts with more rows than one narrow tile holds
-      ExpertGemmArgs g2b = g2;
-      g2b.active = active_big_ws;
-      g2b.n_active = n_active_big_ws;
-      HIP_TRY(launch_down(g2b, wf, max_big, c.T, st), "routed down launch");
-    }
+    HIP_TRY(launch_stream(g2, false, wf, max_chunks, st), "routed down launch");
   }
   HIP_TRY(profile_mark(MOE_STAGE_DOWN, false, st), "profile event");
 
@@ -515,17 +526,20 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
     s2.A = ws + L.sh_h;
     if (hilo) s2.A_lo = sh_h_lo;
     s2.single_rows = c.T;
+    s2.chunk_rows = sh_chunk_rows;
     s2.W = wt->sh_down;
     s2.Kdim = c.shared_I;
     s2.N = c.H;
     s2.n_tiles = c.H / 32;
     s2.out = ws + L.sh_y;
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_DOWN, true, st), "profile event");
-    if (tiled_shared) {
+    if (af == W_F32) {
+      HIP_TRY(launch_down_f32(s2, 1, st), "shared down launch");
+    } else if (plan.tiled_shared) {
       TiledGemmArgs ts{s2, nullptr, nullptr, nullptr};
       HIP_TRY(launch_tiled(ts, false, af, c.T, 1, st), "shared down launch");
     } else {
-      HIP_TRY(launch_down(s2, af, 1, c.T, st), "shared down launch");
+      HIP_TRY(launch_stream(s2, false, af, sh_chunks, st), "shared down launch");
     }
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_DOWN, false, st), "profile event");
   }

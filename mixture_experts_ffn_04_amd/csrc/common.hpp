@@ -110,15 +110,13 @@ struct PermuteArgs {
   int32_t *counts;         // [E]
   int32_t *user_counts;    // [E] or null
   int32_t *offsets;        // [E+1]
-  int32_t *active;         // [E] experts with 1..small_rows rows, ascending
-  int32_t *n_active;       // [1]
-  int32_t *active_big;     // [E] experts with more than small_rows rows, ascending
-  int32_t *n_active_big;   // [1]
-  int small_rows;
   int32_t *active_all;     // [E] every expert with rows, ascending
   int32_t *n_active_all;   // [1]
   int32_t *mtile_prefix;   // [E+1] prefix over active_all of ceil(rows / tile_rows)
   int tile_rows;
+  int4 *chunks;            // [n_slots + E] chunks of <= chunk_rows rows (ExpertGemmArgs::chunks)
+  int32_t *n_chunks;       // [1]
+  int chunk_rows;
   int32_t *perm;           // [T*K] row -> slot
   int32_t *inv;            // [T*K] slot -> row
   int n_slots, E;
@@ -135,6 +133,12 @@ struct ExpertGemmArgs {
   const void *A;            // direct: [rows, Kdim]; gather: x [T, Kdim]
   const int32_t *perm;      // gather mode: row -> slot (token = slot / topk)
   int topk;
+  // row chunks (streaming kernels): {expert, first row, rows | (chunks of the
+  // expert << 16), first chunk of the expert} per chunk of at most chunk_rows
+  // rows; null = one group of single_rows rows cut into chunks of chunk_rows
+  const int4 *chunks;
+  const int32_t *n_chunks;  // [1]
+  int chunk_rows;
   // groups
   const int32_t *counts;    // [E] rows per expert; null = single group
   const int32_t *offsets;   // [E+1]

@@ -14,13 +14,16 @@ hipError_t launch_permute(const PermuteArgs &a, hipStream_t st);
 
 enum WFormat { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };
 
-// Routed or shared expert GEMMs.  `max_groups` bounds the number of active
-// groups (host-known), `max_rows` the rows of any group; the launchers size
-// their grids from these bounds and read the actual schedule on the device.
-hipError_t launch_gate_up(const ExpertGemmArgs &a, WFormat wf, int max_groups, int max_rows,
-                          hipStream_t st);
-hipError_t launch_down(const ExpertGemmArgs &a, WFormat wf, int max_groups, int max_rows,
-                       hipStream_t st);
+// f32 expert GEMMs (f32 weights and activations).  `max_groups` bounds the
+// number of active groups (host-known); the kernels read the actual list.
+hipError_t launch_gate_up_f32(const ExpertGemmArgs &a, int max_groups, hipStream_t st);
+hipError_t launch_down_f32(const ExpertGemmArgs &a, int max_groups, hipStream_t st);
+
+// LDS-staged weight-streaming grouped GEMM (small token counts).  Work items
+// are (row chunk, column tile); max_chunks bounds the chunk count.
+hipError_t launch_stream(const ExpertGemmArgs &a, bool gate_up, WFormat wf, long max_chunks, hipStream_t st);
+// rows per chunk (16 or 32) for `slots` (token, expert) pairs over E experts
+int stream_chunk_rows(long slots, int E);
 
 // Tiled grouped GEMM (large token counts).  max_rows_total bounds the rows of
 // all groups together, max_groups the number of groups.

@@ -1,8 +1,8 @@
 // Permutation of the T*K (token, k) slots by expert: per-expert counts (the
 // kept-slot counts of SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own
 // DSpark draft (stacked on #1035)", tokens_per_expert commit note), exclusive
-// offsets, the active experts split into two lists by row count (the grouped
-// GEMMs run narrow and wide row tiles as separate launches) and the row <->
+// offsets, the list of active experts with the prefix of their row tiles (the
+// tiled GEMM), the table of row chunks (the streaming GEMM) and the row <->
 // slot maps that the grouped expert GEMMs and the combine read.
 //
 // One workgroup of 1024 threads: LDS histogram (integer atomics, so the
@@ -56,32 +56,31 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) 
 
   const int v = tid < a.E ? hist[tid] : 0;
   const int incl = block_inclusive_scan(v, wsum);
-  const int small = (tid < a.E && v > 0 && v <= a.small_rows) ? 1 : 0;
-  const int big = (tid < a.E && v > a.small_rows) ? 1 : 0;
-  const int small_incl = block_inclusive_scan(small, wsum);
-  const int big_incl = block_inclusive_scan(big, wsum);
-  const int any = small | big;
+  const int any = (tid < a.E && v > 0) ? 1 : 0;
   const int any_incl = block_inclusive_scan(any, wsum);
   const int mtiles = (v + a.tile_rows - 1) / a.tile_rows;
   const int mt_incl = block_inclusive_scan(mtiles, wsum);
+  const int nch = (v + a.chunk_rows - 1) / a.chunk_rows;
+  const int ch_incl = block_inclusive_scan(nch, wsum);
   if (tid < a.E) {
     a.counts[tid] = v;
     if (a.user_counts) a.user_counts[tid] = v;
     a.offsets[tid] = incl - v;
-    if (small) a.active[small_incl - 1] = tid;
-    if (big) a.active_big[big_incl - 1] = tid;
     if (any) {
       a.active_all[any_incl - 1] = tid;
       a.mtile_prefix[any_incl] = mt_incl;
     }
+    // {expert, first row, rows | chunks of the expert << 16, first chunk of the expert}
+    for (int j = 0; j < nch; ++j)
+      a.chunks[ch_incl - nch + j] = make_int4(tid, incl - v + j * a.chunk_rows,
+                                              min(a.chunk_rows, v - j * a.chunk_rows) | (int)((unsigned)nch << 16), ch_incl - nch);
     hist[tid] = incl - v;  // becomes the scatter cursor
   }
   if (tid == kPermuteThreads - 1) {
     a.offsets[a.E] = incl;
-    a.n_active[0] = small_incl;
-    a.n_active_big[0] = big_incl;
     a.n_active_all[0] = any_incl;
     a.mtile_prefix[0] = 0;
+    a.n_chunks[0] = ch_incl;
   }
   __syncthreads();
 

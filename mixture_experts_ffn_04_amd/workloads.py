@@ -208,12 +208,15 @@ def _c2(T=72):
     return Workload("qwen3_8b_moe_draft_e8_top1", T=T, H=4096, E=8, I=1536, K=1)
 
 
-def _c3(T=72, logit_bias=False):
-    if logit_bias:
-        return Workload("qwen3_5_moe_drafter_e512_top10_logitbias", T=T, H=5120, E=512,
-                        I=512, K=10, shared_I=2048, shared_gated=True, router_bias_std=0.1)
+def _c3(T=72, selection_bias=False):
+    # router (logit) bias ~ N(0, 0.1).  The selection-only variant scales its
+    # bias to the spread of softmax scores over 512 experts (about 1/E): a
+    # bias far above the scores would pick the same experts for every token.
+    if selection_bias:
+        return Workload("qwen3_5_moe_drafter_e512_top10_selbias", T=T, H=5120, E=512,
+                        I=512, K=10, shared_I=2048, shared_gated=True, expert_bias_std=0.002)
     return Workload("qwen3_5_moe_drafter_e512_top10", T=T, H=5120, E=512, I=512, K=10,
-                    shared_I=2048, shared_gated=True, expert_bias_std=0.1)
+                    shared_I=2048, shared_gated=True, router_bias_std=0.1)
 
 
 def _c4(T=72, score_fn="sigmoid"):
@@ -241,8 +244,8 @@ FULL_CASES = [
     ("tiny_f32", {}),
     ("qwen3_8b_moe_draft", {"T": 72}), ("qwen3_8b_moe_draft", {"T": 8192}),
     ("qwen3_5_moe_drafter", {"T": 72}), ("qwen3_5_moe_drafter", {"T": 4096}),
-    ("qwen3_5_moe_drafter", {"T": 72, "logit_bias": True}),
-    ("qwen3_5_moe_drafter", {"T": 4096, "logit_bias": True}),
+    ("qwen3_5_moe_drafter", {"T": 72, "selection_bias": True}),
+    ("qwen3_5_moe_drafter", {"T": 4096, "selection_bias": True}),
     ("deepseek_v4_style", {"T": 72, "score_fn": "sigmoid"}),
     ("deepseek_v4_style", {"T": 4096, "score_fn": "sigmoid"}),
     ("deepseek_v4_style", {"T": 72, "score_fn": "sqrtsoftplus"}),
