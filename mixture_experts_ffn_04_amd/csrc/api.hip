@@ -61,25 +61,45 @@ int logits_ld(const moe_config &c) { return c.E + (has_shared_gate(c) ? 1 : 0); 
 
 // Which kernels run the routed expert GEMMs, and the rows per chunk of the
 // expert-sorted rows that the permutation cuts for them.
+//   streaming: experts hold a few rows; the GEMMs read each weight once
+//   tiled:     from kTiledMinTokens tokens; still bound by weight reads
+//   big tile:  experts hold >= kBigTileRows rows on average; matrix-core
+//              bound.  Runs gate_up; the down projection (which also
+//              multiplies the low halves of h) stays on the tiled kernel.
 struct GemmPlan {
-  bool tiled;       // routed experts on the LDS-tiled kernel
-  bool tiled_shared;
-  int chunk_rows;   // streaming kernel chunks (tiled: its row tile)
+  bool tiled, big;        // routed experts
+  bool tiled_shared, big_shared;
+  int chunk_rows;         // streaming kernel chunks, or the big-tile kernel's row tile
 };
 
+constexpr long kBigTileRows = 256;
+
+// 32-bit offsets of the big-tile kernel: activations, h and one expert's
+// weights below 4 GiB
+bool big_fits(const moe_config &c, long rows) {
+  const double lim = 4294967296.0 - 65536.0;
+  const double act = (double)rows * std::max(c.H, std::max(c.I, c.shared_I)) * 2.0;
+  const double w = 2.0 * std::max(c.I, c.shared_I) * (double)c.H * 2.0;
+  return act < lim && w < lim;
+}
+
 GemmPlan gemm_plan(const moe_config &c) {
-  GemmPlan p;
+  GemmPlan p{};
   const bool mfma = c.w_dtype != MOE_DTYPE_F32;
+  const long slots = (long)c.T * c.K;
+  const long active = std::max(1L, std::min<long>(c.E, slots));
   p.tiled = mfma && c.T >= kTiledMinTokens;
+  p.big = p.tiled && slots / active >= kBigTileRows && big_fits(c, slots);
   p.tiled_shared = c.act_dtype != MOE_DTYPE_F32 && c.T >= kTiledMinTokensShared;
-  p.chunk_rows = p.tiled ? tiled_tile_rows() : stream_chunk_rows((long)c.T * c.K, c.E);
+  p.big_shared = p.tiled_shared && c.T >= kBigTileRows && big_fits(c, c.T);
+  p.chunk_rows = p.big ? bigtile_rows() : p.tiled ? tiled_tile_rows() : stream_chunk_rows(slots, c.E);
   return p;
 }
 
 // Workspace carve-up; every buffer starts on a 256-byte boundary.
 struct Layout {
   size_t logits, gamma, scores, indices, weights, counts, offsets, active_all, n_active_all,
-      mtile_prefix, chunks, n_chunks, perm, inv;
+      mtile_prefix, mtile_prefix2, chunks, n_chunks, perm, inv;
   size_t h, y, sh_h, sh_y, total;
 };
 
@@ -104,6 +124,7 @@ Layout make_layout(const moe_config &c) {
   L.active_all = take(E * 4);
   L.n_active_all = take(4);
   L.mtile_prefix = take((E + 1) * 4);
+  L.mtile_prefix2 = take((E + 1) * 4);
   L.chunks = take((T * K + E) * 16);
   L.n_chunks = take(4);
   L.perm = take(T * K * 4);
@@ -216,10 +237,12 @@ int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const 
     pa.active_all = reinterpret_cast<int32_t *>(ws + L.active_all);
     pa.n_active_all = reinterpret_cast<int32_t *>(ws + L.n_active_all);
     pa.mtile_prefix = reinterpret_cast<int32_t *>(ws + L.mtile_prefix);
-    pa.tile_rows = tiled_tile_rows();
     pa.chunks = reinterpret_cast<int4 *>(ws + L.chunks);
     pa.n_chunks = reinterpret_cast<int32_t *>(ws + L.n_chunks);
     pa.chunk_rows = gemm_plan(c).chunk_rows;
+    pa.tile_rows = pa.chunk_rows;
+    pa.mtile_prefix2 = reinterpret_cast<int32_t *>(ws + L.mtile_prefix2);
+    pa.tile_rows2 = tiled_tile_rows();
     pa.perm = reinterpret_cast<int32_t *>(ws + L.perm);
     pa.inv = reinterpret_cast<int32_t *>(ws + L.inv);
     pa.n_slots = c.T * c.K;
@@ -407,6 +430,7 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   const int32_t *active_all_ws = reinterpret_cast<int32_t *>(ws + L.active_all);
   const int32_t *n_active_all_ws = reinterpret_cast<int32_t *>(ws + L.n_active_all);
   const int32_t *mtile_prefix_ws = reinterpret_cast<int32_t *>(ws + L.mtile_prefix);
+  const int32_t *mtile_prefix2_ws = reinterpret_cast<int32_t *>(ws + L.mtile_prefix2);
   const int4 *chunks_ws = reinterpret_cast<const int4 *>(ws + L.chunks);
   const int32_t *n_chunks_ws = reinterpret_cast<int32_t *>(ws + L.n_chunks);
   const int32_t *perm_ws = reinterpret_cast<int32_t *>(ws + L.perm);
@@ -451,7 +475,8 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
     HIP_TRY(launch_gate_up_f32(g1, max_groups, st), "routed gate_up launch");
   } else if (plan.tiled) {
     TiledGemmArgs t1{g1, active_all_ws, n_active_all_ws, mtile_prefix_ws};
-    HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
+    if (plan.big) HIP_TRY(launch_bigtile(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
+    else HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
   } else {
     HIP_TRY(launch_stream(g1, true, wf, max_chunks, st), "routed gate_up launch");
   }
@@ -474,7 +499,8 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
       HIP_TRY(launch_gate_up_f32(s1, 1, st), "shared gate_up launch");
     } else if (plan.tiled_shared) {
       TiledGemmArgs ts{s1, nullptr, nullptr, nullptr};
-      HIP_TRY(launch_tiled(ts, true, af, c.T, 1, st), "shared gate_up launch");
+      if (plan.big_shared) HIP_TRY(launch_bigtile(ts, true, af, c.T, 1, st), "shared gate_up launch");
+      else HIP_TRY(launch_tiled(ts, true, af, c.T, 1, st), "shared gate_up launch");
     } else {
       HIP_TRY(launch_stream(s1, true, af, sh_chunks, st), "shared gate_up launch");
     }
@@ -514,7 +540,7 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   if (wf == W_F32) {
     HIP_TRY(launch_down_f32(g2, max_groups, st), "routed down launch");
   } else if (plan.tiled) {
-    TiledGemmArgs t2{g2, active_all_ws, n_active_all_ws, mtile_prefix_ws};
+    TiledGemmArgs t2{g2, active_all_ws, n_active_all_ws, plan.big ? mtile_prefix2_ws : mtile_prefix_ws};
     HIP_TRY(launch_tiled(t2, false, wf, slots, max_groups, st), "routed down launch");
   } else {
     HIP_TRY(launch_stream(g2, false, wf, max_chunks, st), "routed down launch");

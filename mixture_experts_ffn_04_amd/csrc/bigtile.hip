@@ -1,0 +1,639 @@
+// Large-tile grouped expert GEMMs for experts that hold hundreds of rows
+// (matrix-core bound: every weight element meets >= 256 token rows).
+//
+// Same operations as the streaming and tiled kernels (gate_up + SwiGLU,
+// down + optional per-expert bias; bf16 or MXFP4 weights, bf16
+// activations).  A workgroup of four wavefronts computes a 256-token x
+// 256-weight-row tile; each wavefront a 128 x 128 sub-tile with 32x32x16 bf16
+// MFMAs (weights as operand A, tokens as operand B: lane l holds output
+// columns 8j + 4(l/32) + q, q < 4, of token l % 32 for j < 4).  Per
+// workgroup and 16-deep reduction step the wavefronts read 32 KB of operands
+// from LDS for 2 M multiply-adds, half the LDS traffic per MFMA of a
+// 128 x 64 sub-tile.
+//
+// Reduction slices of 64 (32 with the low halves of h) are staged in LDS,
+// double-buffered: the next slice's global loads are in flight while the
+// current one is multiplied.  Rows of the LDS tiles are 16-byte chunks with
+// an XOR swizzle, so the 16 lanes of an operand read (16 rows, one chunk)
+// and of a store (two rows, eight chunks) touch 64 different banks.  MXFP4
+// codes are decoded to bf16 on their way into LDS.
+//
+// gate_up tiles hold 128 gate rows and the matching 128 up rows; wavefront
+// column half wn takes gate rows 64 wn .. 64 wn + 63 and the same up rows, so
+// a SwiGLU pair meets in one lane.
+//
+// [SF1073] SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own DSpark draft
+// (stacked on #1035)": clamped SwiGLU; stacked gate_up_proj; FP4 experts two
+// codes per byte (low nibble first), one E8M0 scale per 32 inputs.  [MI143]
+// MoE-Infinity PR #143 "feat(dflash): converge DFlash spec-decode stack ->
+// dev (supersedes #140)": output-major MXFP4 blocks, per-expert biases.
+#include <type_traits>
+
+#include "kernels.hpp"
+#include "tile.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = 256;  // tokens per tile
+constexpr int BN = 256;  // weight rows per tile
+constexpr int kThreads = 256;
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float swiglu_b(float g, float u, float lim) {
+  g = fminf(g, lim);
+  u = fminf(fmaxf(u, -lim), lim);
+  return g / (1.f + expf(-g)) * u;
+}
+
+// 16-byte unit of (row, chunk) in a tile with CH chunks per row.  Rows
+// that share a 256-byte bank window get different chunk permutations.
+template <int CH>
+__device__ __forceinline__ int unit(int row, int ch) {
+  return row * CH + (ch ^ ((row / (16 / CH)) % CH));
+}
+
+struct BigCoord {
+  int g, nrows, row0, m0, n0;
+};
+
+// tile -> (group, first token row, column tile).  Tiles of one expert run
+// row tile fastest, so the workgroups sharing a weight tile are adjacent.
+__device__ __forceinline__ void big_coord(const TiledGemmArgs &t, int tile, int n_tiles, BigCoord &c) {
+  const ExpertGemmArgs &a = t.g;
+  if (!a.counts) {
+    const int mt = (a.single_rows + BM - 1) / BM;
+    c.g = 0;
+    c.nrows = a.single_rows;
+    c.row0 = 0;
+    c.m0 = (tile % mt) * BM;
+    c.n0 = tile / mt;
+    return;
+  }
+  const int q = tile / n_tiles;  // global row-tile index over all experts
+  int lo = 0, hi = t.n_active_all[0];
+  while (hi - lo > 1) {  // mtile_prefix[lo] <= q < mtile_prefix[lo + 1]
+    const int mid = (lo + hi) >> 1;
+    if (t.mtile_prefix[mid] <= q) lo = mid;
+    else hi = mid;
+  }
+  const int mt_e = t.mtile_prefix[lo + 1] - t.mtile_prefix[lo];
+  const int local = tile - t.mtile_prefix[lo] * n_tiles;
+  c.g = t.active_all[lo];
+  c.nrows = a.counts[c.g];
+  c.row0 = a.offsets[c.g];
+  c.m0 = (local % mt_e) * BM;
+  c.n0 = local / mt_e;
+}
+
+template <bool LO>
+struct BigPlan {
+  static constexpr int BK = LO ? 32 : 64;         // reduction slice
+  static constexpr int CH = BK / 8;               // 16-byte chunks per row
+  static constexpr int WU = BN * CH;              // units of the weight tile
+  static constexpr int XU = BM * CH;              // units of one activation tile
+  static constexpr int BUF = WU + XU * (LO ? 2 : 1);
+  static constexpr size_t LDS_BYTES = (size_t)2 * BUF * 16;
+};
+
+}  // namespace
+
+// Epilogue of a tile through LDS (the stage buffers must be free: at least
+// 4 x 32 x 132 floats).  Each wave writes one 32-token x 128-column fragment
+// row of its sub-tile to its own padded region, then reads it back one token
+// row at a time, so its stores cover contiguous column runs of one row.
+// gate_up: SwiGLU (+ bias) -> h (bf16 hi, and lo when out_lo is set);
+// down: (+ bias) -> y f32, or out[token] = weight * y with direct_out.
+template <bool GATE_UP>
+__device__ __forceinline__ void big_epilogue(const ExpertGemmArgs &a, const BigCoord &c, int col0,
+                                             f32x16_t (&acc)[4][4], float *lds) {
+  constexpr int EP = 128 + 4;  // padded row (floats): the 16 rows of a float4 write hit distinct banks
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  float *Ew = lds + wave * 32 * EP;
+    const int ccol0 = GATE_UP ? col0 + wn * 64 : col0 + wn * 128;  // first output column of the wave
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) {
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4 *>(Ew + l32 * EP + nf * 32 + 8 * j + 4 * lh) =
+              make_float4(acc[mf][nf][4 * j], acc[mf][nf][4 * j + 1], acc[mf][nf][4 * j + 2], acc[mf][nf][4 * j + 3]);
+      const int rbase = c.m0 + wm * 128 + mf * 32;  // token row (in the group) of fragment row 0
+      if constexpr (GATE_UP) {
+        // lanes 0..31 take even rows, 32..63 odd rows; lane l32 owns h columns 2 l32, 2 l32 + 1
+        const int col = ccol0 + 2 * l32;
+        const bool cok = col < a.N;
+        float gb0 = 0.f, gb1 = 0.f, ub0 = 0.f, ub1 = 0.f;
+        if (a.bias && cok) {
+          const uint16_t *bp = static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride;
+          gb0 = bf16_to_f32(bp[col]);
+          gb1 = bf16_to_f32(bp[col + 1]);
+          ub0 = bf16_to_f32(bp[a.N + col]);
+          ub1 = bf16_to_f32(bp[a.N + col + 1]);
+        }
+#pragma unroll 4
+        for (int r = lh; r < 32; r += 2) {
+          const int row = rbase + r;
+          if (!cok || row >= c.nrows) continue;
+          const float2 g = *reinterpret_cast<const float2 *>(Ew + r * EP + 2 * l32);
+          const float2 u = *reinterpret_cast<const float2 *>(Ew + r * EP + 64 + 2 * l32);
+          const float h0 = swiglu_b(g.x + gb0, u.x + ub0, a.limit);
+          const float h1 = swiglu_b(g.y + gb1, u.y + ub1, a.limit);
+          const uint32_t hb0 = f32_to_bf16(h0), hb1 = f32_to_bf16(h1);
+          const size_t off = (size_t)(c.row0 + row) * a.N + col;
+          *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + off) = hb0 | (hb1 << 16);
+          if (a.out_lo)  // h = hi + lo to ~16 bits
+            *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out_lo) + off) =
+                f32_to_bf16(h0 - bf16_to_f32(hb0)) | (f32_to_bf16(h1 - bf16_to_f32(hb1)) << 16);
+        }
+      } else {
+        // every lane owns output columns 2 lane, 2 lane + 1 of each row
+        const int col = ccol0 + 2 * lane;
+        const bool cok = col < a.N;
+        float b0 = 0.f, b1 = 0.f;
+        if (a.bias && cok) {
+          const uint16_t *bp = static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride;
+          b0 = bf16_to_f32(bp[col]);
+          b1 = bf16_to_f32(bp[col + 1]);
+        }
+#pragma unroll 4
+        for (int r = 0; r < 32; ++r) {
+          const int row = rbase + r;
+          if (!cok || row >= c.nrows) continue;
+          const float2 v = *reinterpret_cast<const float2 *>(Ew + r * EP + 2 * lane);
+          const float y0 = v.x + b0, y1 = v.y + b1;
+          if (a.direct_out) {  // one expert per token: out = weight * y
+            const int slot = a.perm[c.row0 + row];
+            const float wt = a.weights[slot];
+            *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.direct_out) + (size_t)slot * a.N + col) =
+                f32_to_bf16(wt * y0) | (f32_to_bf16(wt * y1) << 16);
+          } else {
+            *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + (size_t)(c.row0 + row) * a.N + col) =
+                make_float2(y0, y1);
+          }
+        }
+      }
+    }
+}
+
+template <bool GATE_UP, int WF, bool GATHER, bool LO>
+__global__ __launch_bounds__(kThreads, 1) void expert_bigtile(TiledGemmArgs ta) {
+  using P = BigPlan<LO>;
+  constexpr int BK = P::BK, CH = P::CH, WU = P::WU, XU = P::XU, BUF = P::BUF;
+  constexpr int XL = XU / kThreads;                        // activation loads per thread per tile
+  constexpr int WL = WF == W_MXFP4 ? BN * (BK / 32) / kThreads : WU / kThreads;  // weight loads
+  const ExpertGemmArgs &a = ta.g;
+  extern __shared__ u32x4_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  const int cols_per_tile = GATE_UP ? BN / 2 : BN;
+  const int n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
+  const int total = a.counts ? ta.mtile_prefix[ta.n_active_all[0]] * n_tiles
+                             : ((a.single_rows + BM - 1) / BM) * n_tiles;
+  const uint16_t *A = static_cast<const uint16_t *>(a.A);
+  const int nks = (a.Kdim + BK - 1) / BK;
+
+  // XCD-contiguous ranges of the tile list (workgroups go to the 8 XCDs
+  // round-robin), so the workgroups of one XCD share weight and token tiles
+  // through its L2.
+  const int nx = gridDim.x % 8 == 0 ? 8 : 1;
+  const int xcd = blockIdx.x % nx, per = gridDim.x / nx;
+  const int span = (total + nx - 1) / nx;
+  for (int local = blockIdx.x / nx; local < span; local += per) {
+    const int tile = xcd * span + local;
+    if (tile >= total) break;
+    BigCoord c;
+    big_coord(ta, tile, n_tiles, c);
+    const int col0 = c.n0 * cols_per_tile;
+
+    // ---- global sources of this thread's loads -----------------------------
+    // 32-bit byte offsets from workgroup-uniform bases (the launcher checks
+    // that activations and one expert's weights span less than 4 GiB).
+    // activation unit j*256 + tid -> tile row (j*256 + tid) / CH, chunk tid % CH
+    const int xc = tid % CH;
+    const char *xbase = static_cast<const char *>(a.A);
+    const char *xlbase = static_cast<const char *>(a.A_lo);
+    uint32_t xo[XL], xlo[LO ? XL : 1];
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int r = min(c.m0 + (j * kThreads + tid) / CH, c.nrows - 1);
+      uint32_t ar;
+      if constexpr (GATHER)
+        ar = (uint32_t)(a.perm[c.row0 + r] / a.topk);
+      else
+        ar = (uint32_t)(c.row0 + r);
+      xo[j] = (ar * (uint32_t)a.Kdim + xc * 8) * 2u;
+      if constexpr (LO) xlo[j] = ((uint32_t)(c.row0 + r) * (uint32_t)a.Kdim + xc * 8) * 2u;
+    }
+    // weight tile row -> weight row of the expert (clamped into the matrix)
+    auto wrow = [&](int r) {
+      int g, lim;
+      if constexpr (GATE_UP) {
+        g = r < BN / 2 ? col0 + r : a.N + col0 + (r - BN / 2);
+        lim = r < BN / 2 ? a.N - 1 : 2 * a.N - 1;
+      } else {
+        g = col0 + r;
+        lim = a.N - 1;
+      }
+      return (uint32_t)min(g, lim);
+    };
+    // bf16: unit j*256 + tid -> row (j*256 + tid) / CH, chunk tid % CH
+    // MXFP4: one 32-element block (16 code bytes + a scale) per load:
+    //        load j*256 + tid -> row (j*256 + tid) / (BK/32), block tid % (BK/32)
+    const char *wbase = static_cast<const char *>(a.W) + (size_t)c.g * a.w_stride * (WF == W_MXFP4 ? 1 : 2);
+    const uint8_t *sbase = WF == W_MXFP4 ? a.Wscale + (size_t)c.g * a.s_stride : nullptr;
+    uint32_t wo[WL], so[WF == W_MXFP4 ? WL : 1];
+    const int wb = tid % (BK / 32);
+#pragma unroll
+    for (int j = 0; j < WL; ++j) {
+      if constexpr (WF == W_MXFP4) {
+        const uint32_t gr = wrow((j * kThreads + tid) / (BK / 32));
+        wo[j] = gr * (uint32_t)(a.Kdim / 2) + wb * 16;
+        so[j] = gr * (uint32_t)(a.Kdim / 32) + wb;
+      } else {
+        wo[j] = (wrow((j * kThreads + tid) / CH) * (uint32_t)a.Kdim + xc * 8) * 2u;
+      }
+    }
+
+    u32x4_t xv[XL], xlv[LO ? XL : 1], wv[WL];
+    uint32_t sv[WF == W_MXFP4 ? WL : 1];
+    auto gload = [&](int ks) {
+      const int k0 = ks * BK;
+      const bool xin = k0 + xc * 8 < a.Kdim;
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        xv[j] = xin ? load16(xbase + xo[j] + k0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (LO) xlv[j] = xin ? load16(xlbase + xlo[j] + k0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      if constexpr (WF == W_MXFP4) {
+        const bool win = k0 + wb * 32 < a.Kdim;
+#pragma unroll
+        for (int j = 0; j < WL; ++j) {
+          wv[j] = win ? load16(wbase + wo[j] + k0 / 2) : u32x4_t{0u, 0u, 0u, 0u};
+          sv[j] = win ? sbase[so[j] + k0 / 32] : 127u;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < WL; ++j) wv[j] = xin ? load16(wbase + wo[j] + k0 * 2) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    auto lstore = [&](int buf) {
+      u32x4_t *Wt = smem + buf * BUF, *Xt = Wt + WU;
+#pragma unroll
+      for (int j = 0; j < XL; ++j) {
+        const int r = (j * kThreads + tid) / CH;
+        Xt[unit<CH>(r, xc)] = xv[j];
+        if constexpr (LO) Xt[XU + unit<CH>(r, xc)] = xlv[j];
+      }
+      if constexpr (WF == W_MXFP4) {
+#pragma unroll
+        for (int j = 0; j < WL; ++j) {
+          const int r = (j * kThreads + tid) / (BK / 32);
+          const float sc = e8m0_to_f32(sv[j]);
+          Wt[unit<CH>(r, 4 * wb + 0)] = decode_e2m1x8(wv[j].x, sc);
+          Wt[unit<CH>(r, 4 * wb + 1)] = decode_e2m1x8(wv[j].y, sc);
+          Wt[unit<CH>(r, 4 * wb + 2)] = decode_e2m1x8(wv[j].z, sc);
+          Wt[unit<CH>(r, 4 * wb + 3)] = decode_e2m1x8(wv[j].w, sc);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < WL; ++j) Wt[unit<CH>((j * kThreads + tid) / CH, xc)] = wv[j];
+      }
+    };
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mf][nf][i] = 0.f;
+
+    // LDS weight row of fragment nf of this wavefront
+    auto wfrag = [&](int nf) {
+      if constexpr (GATE_UP) return nf < 2 ? wn * 64 + nf * 32 : BN / 2 + wn * 64 + (nf - 2) * 32;
+      else return wn * 128 + nf * 32;
+    };
+    // 32-row token fragments of this wave that hold rows of the group (the
+    // others are skipped: a group's last row tile is often nearly empty)
+    const int mf_count = min(4, max(0, (c.nrows - c.m0 - wm * 128 + 31) / 32));
+    // Operand fragments of reduction step kk + 1 are read from LDS while the
+    // MFMAs of step kk run (two register sets).
+    // `full` (a std::bool_constant): every fragment holds rows, no guards (a
+    // guard per MFMA group becomes an exec-mask branch that stalls the
+    // matrix pipe, so full tiles, the common case, take an unguarded copy)
+    auto compute = [&](int buf, auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      const u32x4_t *Wt = smem + buf * BUF, *Xt = Wt + WU;
+      constexpr int KS = BK / 16;
+      constexpr int NB = LO ? 8 : 4;  // token fragments per step (hi, then lo)
+      u32x4_t af[2][4], bf[2][NB];
+      auto fetch = [&](int set, int kk) {
+        const int ch = 2 * kk + lh;
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          if (FULL || mf < mf_count) {
+            bf[set][mf] = Xt[unit<CH>(wm * 128 + mf * 32 + l32, ch)];
+            if constexpr (LO) bf[set][4 + mf] = Xt[XU + unit<CH>(wm * 128 + mf * 32 + l32, ch)];
+          }
+        }
+      };
+      fetch(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < KS) fetch(cur ^ 1, kk + 1);
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          if (FULL || mf < mf_count) {
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[cur][nf], bf[cur][mf], acc[mf][nf]);
+            if constexpr (LO) {  // the same weight fragments times the low halves of h
+#pragma unroll
+              for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[cur][nf], bf[cur][4 + mf], acc[mf][nf]);
+            }
+          }
+        }
+      }
+    };
+
+    auto run = [&](auto full) {
+      gload(0);
+      lstore(0);
+      __syncthreads();
+      for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nks) gload(ks + 1);
+        compute(buf, full);
+        if (ks + 1 < nks) lstore(buf ^ 1);
+        __syncthreads();
+      }
+    };
+    if (c.nrows - c.m0 >= BM) run(std::true_type{});
+    else run(std::false_type{});
+
+    big_epilogue<GATE_UP>(a, c, col0, acc, reinterpret_cast<float *>(smem));
+    __syncthreads();  // the next tile's first slice overwrites buffer 0
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 weights: the same tile fed by direct-to-LDS loads.  Each load
+// instruction of a wavefront writes 64 x 16 bytes to consecutive LDS
+// addresses without passing through registers, so the workgroup keeps three
+// 32-deep stages in flight (a ring of four; three with the low halves of h)
+// instead of one register-staged slice.  A lane chooses which global chunk it
+// fetches so that the data lands at its swizzled LDS position.  The compiler
+// does not track these loads: the waits on the vector-memory counter and the
+// barriers are explicit.
+// ---------------------------------------------------------------------------
+namespace {
+
+template <bool LO>
+struct DmaPlan {
+  static constexpr int BK = 32, CH = 4;
+  static constexpr int WUN = BN * CH, XUN = BM * CH;        // 16-byte units per operand tile
+  static constexpr int NXS = LO ? 2 : 1;
+  static constexpr int SLOT = WUN + NXS * XUN;
+  static constexpr int NSTAGE = LO ? 3 : 5;
+  static constexpr int OPS = 4 * (1 + NXS);                 // load instructions per wave and stage
+  static constexpr size_t LDS_BYTES = (size_t)NSTAGE * SLOT * 16;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(NSTAGE * SLOT * 16 >= 4 * 32 * 132 * 4, "epilogue staging fits the ring");
+};
+
+__device__ __forceinline__ void dma16(const char *g, u32x4_t *l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// workgroup barrier that the compiler does not move memory operations across
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace
+
+template <bool GATE_UP, bool GATHER, bool LO>
+__global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs ta) {
+  using P = DmaPlan<LO>;
+  constexpr int CH = P::CH, WUN = P::WUN, XUN = P::XUN, SLOT = P::SLOT, NSTAGE = P::NSTAGE, OPS = P::OPS;
+  const ExpertGemmArgs &a = ta.g;
+  extern __shared__ u32x4_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  const int cols_per_tile = GATE_UP ? BN / 2 : BN;
+  const int n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
+  const int total = a.counts ? ta.mtile_prefix[ta.n_active_all[0]] * n_tiles
+                             : ((a.single_rows + BM - 1) / BM) * n_tiles;
+  const int nst = a.Kdim / P::BK;  // the reduction is a multiple of 32
+
+  const int nx = gridDim.x % 8 == 0 ? 8 : 1;
+  const int xcd = blockIdx.x % nx, per = gridDim.x / nx;
+  const int span = (total + nx - 1) / nx;
+  for (int local = blockIdx.x / nx; local < span; local += per) {
+    const int tile = xcd * span + local;
+    if (tile >= total) break;
+    BigCoord c;
+    big_coord(ta, tile, n_tiles, c);
+    const int col0 = c.n0 * cols_per_tile;
+
+    // ---- this lane's chunk of each of the wave's load instructions ---------
+    // instruction i writes units (wave*4 + i)*64 + lane = row*4 + cs of a tile,
+    // row = (wave*4 + i)*16 + lane/4; the unit holds logical chunk cs ^ f(row)
+    const char *xbase = static_cast<const char *>(a.A);
+    const char *xlbase = static_cast<const char *>(a.A_lo);
+    const char *wbase = static_cast<const char *>(a.W) + (size_t)c.g * a.w_stride * 2;
+    uint32_t wof[4], xof[4], xlof[LO ? 4 : 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (wave * 4 + i) * 16 + (lane >> 2);
+      const int ch = (lane & 3) ^ ((row >> 2) & 3);
+      int wr, lim;
+      if constexpr (GATE_UP) {
+        wr = row < BN / 2 ? col0 + row : a.N + col0 + (row - BN / 2);
+        lim = row < BN / 2 ? a.N - 1 : 2 * a.N - 1;
+      } else {
+        wr = col0 + row;
+        lim = a.N - 1;
+      }
+      wof[i] = ((uint32_t)min(wr, lim) * (uint32_t)a.Kdim + ch * 8) * 2u;
+      const int r = min(c.m0 + row, c.nrows - 1);
+      uint32_t ar;
+      if constexpr (GATHER)
+        ar = (uint32_t)(a.perm[c.row0 + r] / a.topk);
+      else
+        ar = (uint32_t)(c.row0 + r);
+      xof[i] = (ar * (uint32_t)a.Kdim + ch * 8) * 2u;
+      if constexpr (LO) xlof[i] = ((uint32_t)(c.row0 + r) * (uint32_t)a.Kdim + ch * 8) * 2u;
+    }
+    auto issue = [&](int st) {  // stage st into ring slot st % NSTAGE
+      u32x4_t *sl = smem + (st % NSTAGE) * SLOT + wave * 4 * 64;
+      const uint32_t kb = (uint32_t)st * (P::BK * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(wbase + wof[i] + kb, sl + i * 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(xbase + xof[i] + kb, sl + WUN + i * 64);
+      if constexpr (LO) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(xlbase + xlof[i] + kb, sl + WUN + XUN + i * 64);
+      }
+    };
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mf][nf][i] = 0.f;
+
+    const int mf_count = min(4, max(0, (c.nrows - c.m0 - wm * 128 + 31) / 32));
+    auto wfrag = [&](int nf) {
+      if constexpr (GATE_UP) return nf < 2 ? wn * 64 + nf * 32 : BN / 2 + wn * 64 + (nf - 2) * 32;
+      else return wn * 128 + nf * 32;
+    };
+    auto compute = [&](int slot, auto full) {  // `full`: as in expert_bigtile
+      constexpr bool FULL = decltype(full)::value;
+      const u32x4_t *Wt = smem + slot * SLOT, *Xt = Wt + WUN;
+      constexpr int NB = LO ? 8 : 4;
+      u32x4_t af[2][4], bf[2][NB];
+      auto fetch = [&](int set, int kk) {
+        const int ch = 2 * kk + lh;
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          if (FULL || mf < mf_count) {
+            bf[set][mf] = Xt[unit<CH>(wm * 128 + mf * 32 + l32, ch)];
+            if constexpr (LO) bf[set][4 + mf] = Xt[XUN + unit<CH>(wm * 128 + mf * 32 + l32, ch)];
+          }
+        }
+      };
+      fetch(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (kk == 0) fetch(1, 1);
+#pragma unroll
+        for (int mf = 0; mf < 4; ++mf) {
+          if (FULL || mf < mf_count) {
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[kk][nf], bf[kk][mf], acc[mf][nf]);
+            if constexpr (LO) {
+#pragma unroll
+              for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[kk][nf], bf[kk][4 + mf], acc[mf][nf]);
+            }
+          }
+        }
+      }
+    };
+
+    // ---- pipeline: stage s waits for its own loads, one barrier, then the
+    // loads of stage s + NSTAGE - 1 go into the slot freed by stage s - 1
+    auto run = [&](auto full) {
+#pragma unroll
+      for (int d = 0; d < NSTAGE - 1; ++d)
+        if (d < nst) issue(d);
+      for (int s = 0; s < nst; ++s) {
+        const int after = min(NSTAGE - 2, nst - 1 - s);  // stages issued after stage s
+        if (after >= 3) wait_vmem<(NSTAGE >= 5 ? 3 : 2) * OPS>();
+        else if (after == 2) wait_vmem<2 * OPS>();
+        else if (after == 1) wait_vmem<OPS>();
+        else wait_vmem<0>();
+        barrier_lds();
+        if (s + NSTAGE - 1 < nst) issue(s + NSTAGE - 1);
+        compute(s % NSTAGE, full);
+      }
+    };
+    if (c.nrows - c.m0 >= BM) run(std::true_type{});
+    else run(std::false_type{});
+    barrier_lds();  // every wave is done with the ring
+    big_epilogue<GATE_UP>(a, c, col0, acc, reinterpret_cast<float *>(smem));
+    barrier_lds();  // the next tile's first loads overwrite the ring
+  }
+}
+
+namespace {
+
+template <bool GATE_UP, bool GATHER, bool LO>
+hipError_t launch_dma_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
+  auto kern = expert_bigtile_dma<GATE_UP, GATHER, LO>;
+  constexpr size_t lds = DmaPlan<LO>::LDS_BYTES;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));  // one per CU
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, t);
+  return hipGetLastError();
+}
+
+template <bool GATE_UP, int WF, bool GATHER, bool LO>
+hipError_t launch_big_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
+  if constexpr (WF == W_BF16) {
+    return launch_dma_t<GATE_UP, GATHER, LO>(t, tiles_bound, st);
+  } else {  // MXFP4: codes are decoded on their way into LDS (register-staged)
+    auto kern = expert_bigtile<GATE_UP, WF, GATHER, LO>;
+    constexpr size_t lds = BigPlan<LO>::LDS_BYTES;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));  // one per CU
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, t);
+    return hipGetLastError();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bigtile(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total, int max_groups,
+                          hipStream_t st) {
+  const ExpertGemmArgs &a = t.g;
+  const int cols_per_tile = gate_up ? BN / 2 : BN;
+  const long n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
+  const long tiles_bound = ((max_rows_total + BM - 1) / BM + max_groups) * n_tiles;
+  const bool gather = gate_up && a.perm != nullptr;
+  if (gate_up) {
+    if (wf == W_MXFP4)
+      return gather ? launch_big_t<true, W_MXFP4, true, false>(t, tiles_bound, st)
+                    : launch_big_t<true, W_MXFP4, false, false>(t, tiles_bound, st);
+    return gather ? launch_big_t<true, W_BF16, true, false>(t, tiles_bound, st)
+                  : launch_big_t<true, W_BF16, false, false>(t, tiles_bound, st);
+  }
+  if (a.A_lo) {
+    if (wf == W_MXFP4) return launch_big_t<false, W_MXFP4, false, true>(t, tiles_bound, st);
+    return launch_big_t<false, W_BF16, false, true>(t, tiles_bound, st);
+  }
+  if (wf == W_MXFP4) return launch_big_t<false, W_MXFP4, false, false>(t, tiles_bound, st);
+  return launch_big_t<false, W_BF16, false, false>(t, tiles_bound, st);
+}
+
+int bigtile_rows() { return BM; }
+
+}  // namespace moe

@@ -114,6 +114,8 @@ struct PermuteArgs {
   int32_t *n_active_all;   // [1]
   int32_t *mtile_prefix;   // [E+1] prefix over active_all of ceil(rows / tile_rows)
   int tile_rows;
+  int32_t *mtile_prefix2;  // [E+1] the same for tile_rows2
+  int tile_rows2;
   int4 *chunks;            // [n_slots + E] chunks of <= chunk_rows rows (ExpertGemmArgs::chunks)
   int32_t *n_chunks;       // [1]
   int chunk_rows;

@@ -31,6 +31,12 @@ hipError_t launch_tiled(const TiledGemmArgs &t, bool gate_up, WFormat wf, long m
                         int max_groups, hipStream_t st);
 int tiled_tile_rows();
 
+// Large-tile grouped GEMM (experts with hundreds of rows: matrix-core bound).
+// Activations, h and one expert's weights must each span less than 4 GiB.
+hipError_t launch_bigtile(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total,
+                          int max_groups, hipStream_t st);
+int bigtile_rows();
+
 hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t st);
 

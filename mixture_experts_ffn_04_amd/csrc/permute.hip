@@ -1,8 +1,9 @@
 // Permutation of the T*K (token, k) slots by expert: per-expert counts (the
 // kept-slot counts of SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own
 // DSpark draft (stacked on #1035)", tokens_per_expert commit note), exclusive
-// offsets, the list of active experts with the prefix of their row tiles (the
-// tiled GEMM), the table of row chunks (the streaming GEMM) and the row <->
+// offsets, the list of active experts with the prefixes of their row tiles
+// for two tile heights (the tiled GEMMs), the table of row chunks (the
+// streaming GEMM) and the row <->
 // slot maps that the grouped expert GEMMs and the combine read.
 //
 // One workgroup of 1024 threads: LDS histogram (integer atomics, so the
@@ -60,6 +61,8 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) 
   const int any_incl = block_inclusive_scan(any, wsum);
   const int mtiles = (v + a.tile_rows - 1) / a.tile_rows;
   const int mt_incl = block_inclusive_scan(mtiles, wsum);
+  const int mtiles2 = (v + a.tile_rows2 - 1) / a.tile_rows2;
+  const int mt2_incl = block_inclusive_scan(mtiles2, wsum);
   const int nch = (v + a.chunk_rows - 1) / a.chunk_rows;
   const int ch_incl = block_inclusive_scan(nch, wsum);
   if (tid < a.E) {
@@ -69,6 +72,7 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) 
     if (any) {
       a.active_all[any_incl - 1] = tid;
       a.mtile_prefix[any_incl] = mt_incl;
+      a.mtile_prefix2[any_incl] = mt2_incl;
     }
     // {expert, first row, rows | chunks of the expert << 16, first chunk of the expert}
     for (int j = 0; j < nch; ++j)
@@ -80,6 +84,7 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) 
     a.offsets[a.E] = incl;
     a.n_active_all[0] = any_incl;
     a.mtile_prefix[0] = 0;
+    a.mtile_prefix2[0] = 0;
     a.n_chunks[0] = ch_incl;
   }
   __syncthreads();

@@ -63,6 +63,14 @@ SMALL = [
        expert_linear_bias_std=0.02),
     Wl("tiled_top1_direct_t640", T=640, H=256, E=4, I=128, K=1),
     Wl("tiled_shared_only_t300", T=300, H=256, E=16, I=64, K=4, shared_I=320, expert_bias_std=0.05),
+    # large-tile kernels (>= 256 rows per expert on average, shared expert
+    # from 256 tokens): ragged 64-deep slices (352), partial column tiles
+    Wl("big_routed_t1100", T=1100, H=352, E=4, I=160, K=1, shared_I=96, shared_gated=True),
+    Wl("big_mxfp4_direct_t1030", T=1030, H=352, E=4, I=288, K=1, w_dtype="mxfp4", swiglu_limit=7.0,
+       expert_linear_bias_std=0.02),
+    Wl("big_top2_t800", T=800, H=256, E=4, I=128, K=2, shared_I=64, shared_gated=True),
+    Wl("big_bf16_direct_t1030", T=1030, H=352, E=4, I=288, K=1),
+    Wl("big_mxfp4_top2_t1100", T=1100, H=256, E=8, I=160, K=2, w_dtype="mxfp4"),
 ]
 
 
