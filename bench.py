@@ -13,6 +13,11 @@ loop of back-to-back forwards.  `roofline` covers the dominant kernel (routed
 gate_up + SwiGLU): algorithmic bytes (or flops) per launch divided by its mean
 duration, timed with HIP events recorded on the launch stream around that
 kernel in a second timed loop of the same forwards.
+The bracketed durations include the cost of an event pair, which is
+measured on the same stream with nothing between the events and subtracted
+(both numbers are reported).  `traffic` is the kernel's HBM bytes per launch
+from committed rocprofv3 counter runs, reported only while the kernel sources
+still hash to the value recorded with them.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 
@@ -51,6 +56,7 @@ class HipEvents:
                                                 ctypes.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.start = (ctypes.c_void_p * n)()
         self.stop = (ctypes.c_void_p * n)()
         for arr in (self.start, self.stop):
@@ -143,32 +149,80 @@ def run_gpu(wl, steps, warmup, copies=None):
     torch.cuda.synchronize()
     _lib.check(L.moe_profile_stage(-1, None, None, 0))
     k_ms = ev.elapsed_ms()
+    # cost of an event pair with nothing between it, on the same stream: the
+    # bracketed durations above include it, the kernel's own duration does not
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(steps):
+        assert ev.rt.hipEventRecord(ev.start[i], ctypes.c_void_p(stream)) == 0
+        assert ev.rt.hipEventRecord(ev.stop[i], ctypes.c_void_p(stream)) == 0
+    torch.cuda.synchronize()
+    pair_ms = ev.elapsed_ms()
     ev.close()
     counts = routing.counts.cpu().numpy()
     active = int((counts > 0).sum())
     log(f"timed {steps} steps: {total_ms / steps * 1e3:.1f} us/step, gate_up "
         f"{sum(k_ms) / len(k_ms) * 1e3:.1f} us, active experts {active}")
-    res = dict(ms_per_step=total_ms / steps, kernel_ms=sum(k_ms) / len(k_ms), active=active,
+    event_ms = sum(k_ms) / len(k_ms)
+    pair = sum(pair_ms) / len(pair_ms)
+    res = dict(ms_per_step=total_ms / steps, kernel_ms=max(event_ms - pair, 1e-6), event_ms=event_ms,
+               pair_ms=pair, active=active,
                max_count=int(counts.max()), copies=copies, expert_bytes=expert_bytes)
     host = dict(x=x, base=base, routing=routing)
     return res, host
+
+
+# HBM traffic of the dominant kernel, per launch, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE counter runs (scaled by a plain copy of known size), with the
+# hash of the kernel sources they were taken on: a changed kernel reports null.
+TRAFFIC_RECORDS = {
+    ("qwen3_8b_moe_draft_e8_top1", 72): "profiles/stream_gate_up_qwen3_8b_moe_draft_t72_pmc.md",
+}
+KERNEL_SOURCES = ["mixture_experts_ffn_04_amd/csrc/stream.hip", "mixture_experts_ffn_04_amd/csrc/common.hpp",
+                  "mixture_experts_ffn_04_amd/csrc/tile.hpp"]
+
+
+def kernel_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(wl):
+    path = TRAFFIC_RECORDS.get((wl.name, wl.T))
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    fields = {}
+    with open(os.path.join(ROOT, path)) as fh:
+        for ln in fh:
+            if ":" in ln and ln.strip().startswith(("traffic_", "kernel_sources_sha256")):
+                k, v = ln.strip().split(":", 1)
+                fields[k.strip()] = v.strip().replace(",", "")
+    if fields.get("kernel_sources_sha256") != kernel_sources_hash():
+        return None
+    try:
+        return int(fields["traffic_fetch_bytes_per_launch"]) + int(fields["traffic_write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def roofline(wl, res):
     b, f = gate_up_cost(wl, res["active"], wl.T)
     t = res["kernel_ms"] * 1e-3
     hbm_bound = b / (PEAK_HBM_GBS * 1e9) >= f / (PEAK_BF16_TFLOPS * 1e12)
+    timing = {"kernel_us": round(res["kernel_ms"] * 1e3, 2), "event_bracket_us": round(res["event_ms"] * 1e3, 2),
+              "empty_event_pair_us": round(res["pair_ms"] * 1e3, 2)}
     if hbm_bound:
         ach = b / t / 1e9
         return {"kernel": "routed gate_up + SwiGLU", "bound": "hbm", "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": b,
-                "kernel_us": round(res["kernel_ms"] * 1e3, 2)}
+                "traffic": recorded_traffic(wl), "algorithmic_bytes_per_launch": b, **timing}
     ach = f / t / 1e12
     return {"kernel": "routed gate_up + SwiGLU", "bound": "mfma", "achieved": round(ach, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None, "algorithmic_flops_per_launch": f,
-            "kernel_us": round(res["kernel_ms"] * 1e3, 2)}
+            "traffic": None, "algorithmic_flops_per_launch": f, **timing}
 
 
 def cpu_baseline(wl, host, budget_s):
