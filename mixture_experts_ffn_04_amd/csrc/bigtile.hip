@@ -66,14 +66,15 @@ struct BigCoord {
 
 // tile -> (group, first token row, column tile).  Tiles of one expert run
 // row tile fastest, so the workgroups sharing a weight tile are adjacent.
-__device__ __forceinline__ void big_coord(const TiledGemmArgs &t, int tile, int n_tiles, BigCoord &c) {
+__device__ __forceinline__ void big_coord(const TiledGemmArgs &t, int tile, int n_tiles, BigCoord &c,
+                                          int tm = BM) {
   const ExpertGemmArgs &a = t.g;
   if (!a.counts) {
-    const int mt = (a.single_rows + BM - 1) / BM;
+    const int mt = (a.single_rows + tm - 1) / tm;
     c.g = 0;
     c.nrows = a.single_rows;
     c.row0 = 0;
-    c.m0 = (tile % mt) * BM;
+    c.m0 = (tile % mt) * tm;
     c.n0 = tile / mt;
     return;
   }
@@ -89,7 +90,7 @@ __device__ __forceinline__ void big_coord(const TiledGemmArgs &t, int tile, int 
   c.g = t.active_all[lo];
   c.nrows = a.counts[c.g];
   c.row0 = a.offsets[c.g];
-  c.m0 = (local % mt_e) * BM;
+  c.m0 = (local % mt_e) * tm;
   c.n0 = local / mt_e;
 }
 
@@ -106,14 +107,15 @@ struct BigPlan {
 }  // namespace
 
 // Epilogue of a tile through LDS (the stage buffers must be free: at least
-// 4 x 32 x 132 floats).  Each wave writes one 32-token x 128-column fragment
-// row of its sub-tile to its own padded region, then reads it back one token
+// 4 x 32 x 132 floats).  The wave's sub-tile is MF fragment rows of 32
+// tokens x 128 columns.  Each wave writes one fragment row of its sub-tile
+// to its own padded region, then reads it back one token
 // row at a time, so its stores cover contiguous column runs of one row.
 // gate_up: SwiGLU (+ bias) -> h (bf16 hi, and lo when out_lo is set);
 // down: (+ bias) -> y f32, or out[token] = weight * y with direct_out.
-template <bool GATE_UP>
+template <bool GATE_UP, int MF = 4>
 __device__ __forceinline__ void big_epilogue(const ExpertGemmArgs &a, const BigCoord &c, int col0,
-                                             f32x16_t (&acc)[4][4], float *lds) {
+                                             f32x16_t (&acc)[MF][4], float *lds) {
   constexpr int EP = 128 + 4;  // padded row (floats): the 16 rows of a float4 write hit distinct banks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
@@ -121,14 +123,14 @@ __device__ __forceinline__ void big_epilogue(const ExpertGemmArgs &a, const BigC
   float *Ew = lds + wave * 32 * EP;
     const int ccol0 = GATE_UP ? col0 + wn * 64 : col0 + wn * 128;  // first output column of the wave
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf) {
+    for (int mf = 0; mf < MF; ++mf) {
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           *reinterpret_cast<float4 *>(Ew + l32 * EP + nf * 32 + 8 * j + 4 * lh) =
               make_float4(acc[mf][nf][4 * j], acc[mf][nf][4 * j + 1], acc[mf][nf][4 * j + 2], acc[mf][nf][4 * j + 3]);
-      const int rbase = c.m0 + wm * 128 + mf * 32;  // token row (in the group) of fragment row 0
+      const int rbase = c.m0 + wm * MF * 32 + mf * 32;  // token row (in the group) of fragment row 0
       if constexpr (GATE_UP) {
         // lanes 0..31 take even rows, 32..63 odd rows; lane l32 owns h columns 2 l32, 2 l32 + 1
         const int col = ccol0 + 2 * l32;
@@ -405,17 +407,19 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile(TiledGemmArgs ta) 
 // ---------------------------------------------------------------------------
 namespace {
 
-template <bool LO>
+template <bool LO, int TM>
 struct DmaPlan {
   static constexpr int BK = 32, CH = 4;
-  static constexpr int WUN = BN * CH, XUN = BM * CH;        // 16-byte units per operand tile
+  static constexpr int WUN = BN * CH, XUN = TM * CH;        // 16-byte units per operand tile
+  static constexpr int XI = XUN / 256;                      // activation load instructions per wave
   static constexpr int NXS = LO ? 2 : 1;
   static constexpr int SLOT = WUN + NXS * XUN;
-  static constexpr int NSTAGE = LO ? 3 : 5;
-  static constexpr int OPS = 4 * (1 + NXS);                 // load instructions per wave and stage
+  static constexpr int NSTAGE = std::min(6, (160 * 1024) / (SLOT * 16));
+  static constexpr int OPS = 4 + XI * NXS;                  // load instructions per wave and stage
   static constexpr size_t LDS_BYTES = (size_t)NSTAGE * SLOT * 16;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(NSTAGE >= 3 && LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(NSTAGE * SLOT * 16 >= 4 * 32 * 132 * 4, "epilogue staging fits the ring");
+  static_assert((NSTAGE - 2) * OPS < 64, "vmcnt range");
 };
 
 __device__ __forceinline__ void dma16(const char *g, u32x4_t *l) {
@@ -437,10 +441,11 @@ __device__ __forceinline__ void barrier_lds() {
 
 }  // namespace
 
-template <bool GATE_UP, bool GATHER, bool LO>
+template <bool GATE_UP, bool GATHER, bool LO, int TM>
 __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs ta) {
-  using P = DmaPlan<LO>;
+  using P = DmaPlan<LO, TM>;
   constexpr int CH = P::CH, WUN = P::WUN, XUN = P::XUN, SLOT = P::SLOT, NSTAGE = P::NSTAGE, OPS = P::OPS;
+  constexpr int XI = P::XI, MF = TM / 64;  // wave sub-tile: MF fragments of 32 tokens x 128 columns
   const ExpertGemmArgs &a = ta.g;
   extern __shared__ u32x4_t smem[];
 
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
   const int cols_per_tile = GATE_UP ? BN / 2 : BN;
   const int n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
   const int total = a.counts ? ta.mtile_prefix[ta.n_active_all[0]] * n_tiles
-                             : ((a.single_rows + BM - 1) / BM) * n_tiles;
+                             : ((a.single_rows + TM - 1) / TM) * n_tiles;
   const int nst = a.Kdim / P::BK;  // the reduction is a multiple of 32
 
   const int nx = gridDim.x % 8 == 0 ? 8 : 1;
@@ -462,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     const int tile = xcd * span + local;
     if (tile >= total) break;
     BigCoord c;
-    big_coord(ta, tile, n_tiles, c);
+    big_coord(ta, tile, n_tiles, c, TM);
     const int col0 = c.n0 * cols_per_tile;
 
     // ---- this lane's chunk of each of the wave's load instructions ---------
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     const char *xbase = static_cast<const char *>(a.A);
     const char *xlbase = static_cast<const char *>(a.A_lo);
     const char *wbase = static_cast<const char *>(a.W) + (size_t)c.g * a.w_stride * 2;
-    uint32_t wof[4], xof[4], xlof[LO ? 4 : 1];
+    uint32_t wof[4], xof[XI], xlof[LO ? XI : 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (wave * 4 + i) * 16 + (lane >> 2);
@@ -485,6 +490,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
         lim = a.N - 1;
       }
       wof[i] = ((uint32_t)min(wr, lim) * (uint32_t)a.Kdim + ch * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int row = (wave * XI + i) * 16 + (lane >> 2);
+      const int ch = (lane & 3) ^ ((row >> 2) & 3);
       const int r = min(c.m0 + row, c.nrows - 1);
       uint32_t ar;
       if constexpr (GATHER)
@@ -495,27 +505,27 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
       if constexpr (LO) xlof[i] = ((uint32_t)(c.row0 + r) * (uint32_t)a.Kdim + ch * 8) * 2u;
     }
     auto issue = [&](int st) {  // stage st into ring slot st % NSTAGE
-      u32x4_t *sl = smem + (st % NSTAGE) * SLOT + wave * 4 * 64;
+      u32x4_t *sl = smem + (st % NSTAGE) * SLOT;
       const uint32_t kb = (uint32_t)st * (P::BK * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(wbase + wof[i] + kb, sl + i * 64);
+      for (int i = 0; i < 4; ++i) dma16(wbase + wof[i] + kb, sl + (wave * 4 + i) * 64);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(xbase + xof[i] + kb, sl + WUN + i * 64);
+      for (int i = 0; i < XI; ++i) dma16(xbase + xof[i] + kb, sl + WUN + (wave * XI + i) * 64);
       if constexpr (LO) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(xlbase + xlof[i] + kb, sl + WUN + XUN + i * 64);
+        for (int i = 0; i < XI; ++i) dma16(xlbase + xlof[i] + kb, sl + WUN + XUN + (wave * XI + i) * 64);
       }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[MF][4];
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf)
+    for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mf][nf][i] = 0.f;
 
-    const int mf_count = min(4, max(0, (c.nrows - c.m0 - wm * 128 + 31) / 32));
+    const int mf_count = min(MF, max(0, (c.nrows - c.m0 - wm * (TM / 2) + 31) / 32));
     auto wfrag = [&](int nf) {
       if constexpr (GATE_UP) return nf < 2 ? wn * 64 + nf * 32 : BN / 2 + wn * 64 + (nf - 2) * 32;
       else return wn * 128 + nf * 32;
@@ -523,17 +533,17 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     auto compute = [&](int slot, auto full) {  // `full`: as in expert_bigtile
       constexpr bool FULL = decltype(full)::value;
       const u32x4_t *Wt = smem + slot * SLOT, *Xt = Wt + WUN;
-      constexpr int NB = LO ? 8 : 4;
+      constexpr int NB = LO ? 2 * MF : MF;
       u32x4_t af[2][4], bf[2][NB];
       auto fetch = [&](int set, int kk) {
         const int ch = 2 * kk + lh;
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
+        for (int mf = 0; mf < MF; ++mf) {
           if (FULL || mf < mf_count) {
-            bf[set][mf] = Xt[unit<CH>(wm * 128 + mf * 32 + l32, ch)];
-            if constexpr (LO) bf[set][4 + mf] = Xt[XUN + unit<CH>(wm * 128 + mf * 32 + l32, ch)];
+            bf[set][mf] = Xt[unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
+            if constexpr (LO) bf[set][MF + mf] = Xt[XUN + unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
           }
         }
       };
@@ -542,13 +552,13 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
       for (int kk = 0; kk < 2; ++kk) {
         if (kk == 0) fetch(1, 1);
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
+        for (int mf = 0; mf < MF; ++mf) {
           if (FULL || mf < mf_count) {
 #pragma unroll
             for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[kk][nf], bf[kk][mf], acc[mf][nf]);
             if constexpr (LO) {
 #pragma unroll
-              for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[kk][nf], bf[kk][4 + mf], acc[mf][nf]);
+              for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[kk][nf], bf[kk][MF + mf], acc[mf][nf]);
             }
           }
         }
@@ -563,29 +573,32 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
         if (d < nst) issue(d);
       for (int s = 0; s < nst; ++s) {
         const int after = min(NSTAGE - 2, nst - 1 - s);  // stages issued after stage s
-        if (after >= 3) wait_vmem<(NSTAGE >= 5 ? 3 : 2) * OPS>();
-        else if (after == 2) wait_vmem<2 * OPS>();
-        else if (after == 1) wait_vmem<OPS>();
-        else wait_vmem<0>();
+        switch (after) {  // wait until only those are outstanding
+          case 0: wait_vmem<0>(); break;
+          case 1: wait_vmem<OPS>(); break;
+          case 2: wait_vmem<(NSTAGE >= 4 ? 2 : 0) * OPS>(); break;
+          case 3: wait_vmem<(NSTAGE >= 5 ? 3 : 0) * OPS>(); break;
+          default: wait_vmem<(NSTAGE >= 6 ? 4 : 0) * OPS>(); break;
+        }
         barrier_lds();
         if (s + NSTAGE - 1 < nst) issue(s + NSTAGE - 1);
         compute(s % NSTAGE, full);
       }
     };
-    if (c.nrows - c.m0 >= BM) run(std::true_type{});
+    if (c.nrows - c.m0 >= TM) run(std::true_type{});
     else run(std::false_type{});
     barrier_lds();  // every wave is done with the ring
-    big_epilogue<GATE_UP>(a, c, col0, acc, reinterpret_cast<float *>(smem));
+    big_epilogue<GATE_UP, MF>(a, c, col0, acc, reinterpret_cast<float *>(smem));
     barrier_lds();  // the next tile's first loads overwrite the ring
   }
 }
 
 namespace {
 
-template <bool GATE_UP, bool GATHER, bool LO>
+template <bool GATE_UP, bool GATHER, bool LO, int TM = BM>
 hipError_t launch_dma_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
-  auto kern = expert_bigtile_dma<GATE_UP, GATHER, LO>;
-  constexpr size_t lds = DmaPlan<LO>::LDS_BYTES;
+  auto kern = expert_bigtile_dma<GATE_UP, GATHER, LO, TM>;
+  constexpr size_t lds = DmaPlan<LO, TM>::LDS_BYTES;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;

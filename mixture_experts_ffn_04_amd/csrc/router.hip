@@ -22,6 +22,130 @@ namespace moe {
 // (logits end within about one f32 ulp of the exactly rounded sum, which is
 // what keeps the GPU's top-k on the oracle's side of near-ties).
 // ---------------------------------------------------------------------------
+// Logits, bf16 inputs, many tokens: a workgroup computes 64 tokens x 128
+// columns over the whole hidden dimension, so each token row is read once
+// per 128 columns (the narrow kernel above reads it once per 16).  Stages of
+// 128 hidden elements of both operands go through LDS (XOR-swizzled 16-byte
+// chunks); the next stage's loads are in registers while the current one is
+// multiplied.  Wave w takes columns 32w .. 32w + 31 of the tile for all 64
+// tokens.  Same arithmetic as the narrow kernel: every MFMA step (32 exact
+// bf16 products in a fresh f32 accumulator) is added in fp64.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kLT = 64, kLC = 128, kLK = 128;  // tokens, columns, hidden elements per stage
+__device__ __forceinline__ int lunit(int row, int ch) { return row * 16 + (ch ^ (row & 15)); }
+}  // namespace
+
+__global__ __launch_bounds__(256) void router_logits_tiled(LogitsArgs a) {
+  __shared__ u32x4_t Xs[kLT * 16];   // 16 KB
+  __shared__ u32x4_t Gs[kLC * 16];   // 32 KB
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int ncols = a.E + (a.sh_gate ? 1 : 0);
+  const int c0 = blockIdx.x * kLC, m0 = blockIdx.y * kLT;
+  const uint16_t *gate = static_cast<const uint16_t *>(a.gate);
+  const uint16_t *x = static_cast<const uint16_t *>(a.x);
+
+  // loads: unit j*256 + tid -> row (j*256 + tid) / 16, chunk tid % 16
+  const int ch = tid & 15;
+  const uint16_t *xs[kLT * 16 / 256], *gs[kLC * 16 / 256];
+#pragma unroll
+  for (int j = 0; j < kLT * 16 / 256; ++j)
+    xs[j] = x + (size_t)min(m0 + j * 16 + (tid >> 4), a.T - 1) * a.H + ch * 8;
+#pragma unroll
+  for (int j = 0; j < kLC * 16 / 256; ++j) {
+    const int c = c0 + j * 16 + (tid >> 4);
+    const uint16_t *row;
+    if (c < a.E) row = gate + (size_t)c * a.H;
+    else if (c == a.E && a.sh_gate) row = static_cast<const uint16_t *>(a.sh_gate);
+    else row = gate;  // padding column: any valid row, result discarded
+    gs[j] = row + ch * 8;
+  }
+  u32x4_t xv[kLT * 16 / 256], gv[kLC * 16 / 256];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < kLT * 16 / 256; ++j) xv[j] = load16(xs[j] + k0);
+#pragma unroll
+    for (int j = 0; j < kLC * 16 / 256; ++j) gv[j] = load16(gs[j] + k0);
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int j = 0; j < kLT * 16 / 256; ++j) Xs[lunit(j * 16 + (tid >> 4), ch)] = xv[j];
+#pragma unroll
+    for (int j = 0; j < kLC * 16 / 256; ++j) Gs[lunit(j * 16 + (tid >> 4), ch)] = gv[j];
+  };
+
+  double acc[2][4][4];  // [column fragment][token fragment][q]
+#pragma unroll
+  for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+    for (int tf = 0; tf < 4; ++tf)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[cf][tf][q] = 0.0;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+
+  const int nst = a.H / kLK;  // whole 128-element stages; the 32-element tail below
+  if (nst > 0) gload(0);
+  for (int s = 0; s < nst; ++s) {
+    __syncthreads();  // the previous stage's operands are consumed
+    lstore();
+    __syncthreads();
+    if (s + 1 < nst) gload((s + 1) * kLK);
+#pragma unroll
+    for (int q = 0; q < kLK / 32; ++q) {
+      u32x4_t af[2], bf[4];
+#pragma unroll
+      for (int cf = 0; cf < 2; ++cf) af[cf] = Gs[lunit(wave * 32 + cf * 16 + lr, 4 * q + lg)];
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) bf[tf] = Xs[lunit(tf * 16 + lr, 4 * q + lg)];
+#pragma unroll
+      for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf) {
+          const f32x4_t p = mfma_16x16x32(af[cf], bf[tf], zero);
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) acc[cf][tf][q2] += (double)p[q2];
+        }
+    }
+  }
+  // hidden-dimension tail (H % 128, a multiple of 32): one MFMA step per
+  // 32 elements straight from global memory
+  for (int k = nst * kLK; k < a.H; k += 32) {
+    u32x4_t af[2], bf[4];
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+      const int c = c0 + wave * 32 + cf * 16 + lr;
+      const uint16_t *row = c < a.E ? gate + (size_t)c * a.H
+                                    : (c == a.E && a.sh_gate ? static_cast<const uint16_t *>(a.sh_gate) : gate);
+      af[cf] = load16(row + k + 8 * lg);
+    }
+#pragma unroll
+    for (int tf = 0; tf < 4; ++tf) bf[tf] = load16(x + (size_t)min(m0 + tf * 16 + lr, a.T - 1) * a.H + k + 8 * lg);
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) {
+        const f32x4_t p = mfma_16x16x32(af[cf], bf[tf], zero);
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) acc[cf][tf][q2] += (double)p[q2];
+      }
+  }
+  // lane holds columns c0 + 32 wave + 16 cf + 4 lg + q2 of token m0 + 16 tf + lr
+#pragma unroll
+  for (int tf = 0; tf < 4; ++tf) {
+    const int t = m0 + tf * 16 + lr;
+    if (t >= a.T) continue;
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const int c = c0 + wave * 32 + cf * 16 + 4 * lg + q2;
+        if (c < ncols) a.partial[(size_t)t * a.ldl + c] = acc[cf][tf][q2];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int MT>
 __global__ __launch_bounds__(kBlockThreads) void router_logits_bf16(LogitsArgs a) {
   __shared__ double red[kSplitWaves * MT * 64 * 4];
@@ -328,12 +452,23 @@ __global__ __launch_bounds__(256) void router_select(SelectArgs a) {
 // launchers
 // ---------------------------------------------------------------------------
 
+// The 64 x 128 tiled kernel from 256 tokens when there are at least 64
+// columns; narrower problems keep the 16-column kernel with its split over
+// the hidden dimension (it fills the chip where tiles would be few).
+static bool router_logits_use_tiled(int T, int ncols) { return T >= 256 && ncols >= 64; }
+
 // Row-tile width and number of hidden-dimension slices of the bf16 logits
 // kernel for a problem (host side; the same numbers size the workspace).
 void router_logits_plan(int T, int H, int ncols, bool bf16, int *mt, int *n_split,
                         int *blocks_per_split) {
   if (!bf16) {
     *mt = 1;
+    *n_split = 1;
+    *blocks_per_split = H / kKBlock + 1;
+    return;
+  }
+  if (router_logits_use_tiled(T, ncols)) {  // one pass over the hidden dimension
+    *mt = 0;
     *n_split = 1;
     *blocks_per_split = H / kKBlock + 1;
     return;
@@ -355,6 +490,12 @@ hipError_t launch_router_logits(const LogitsArgs &a, bool bf16, hipStream_t st) 
   if (!bf16) {
     const long n = (long)a.T * ncols;
     hipLaunchKernelGGL(router_logits_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  if (router_logits_use_tiled(a.T, ncols)) {
+    if (a.n_split != 1) return hipErrorInvalidValue;
+    const dim3 grid((ncols + kLC - 1) / kLC, (a.T + kLT - 1) / kLT);
+    hipLaunchKernelGGL(router_logits_tiled, grid, dim3(256), 0, st, a);
     return hipGetLastError();
   }
   int mt, n_split, per;
