@@ -201,8 +201,10 @@ int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const 
   int mt;
   router_logits_plan(c.T, c.H, la.ldl, c.act_dtype == MOE_DTYPE_BF16, &mt, &la.n_split,
                      &la.blocks_per_split);
+  // few columns and tokens: the select kernel computes the logits itself
+  const bool fused = router_fused_applies(c.T, c.H, c.E, la.sh_gate != nullptr);
   HIP_TRY(profile_mark(MOE_STAGE_ROUTER_LOGITS, true, st), "profile event");
-  HIP_TRY(launch_router_logits(la, c.act_dtype == MOE_DTYPE_BF16, st), "router logits launch");
+  if (!fused) HIP_TRY(launch_router_logits(la, c.act_dtype == MOE_DTYPE_BF16, st), "router logits launch");
   HIP_TRY(profile_mark(MOE_STAGE_ROUTER_LOGITS, false, st), "profile event");
 
   SelectArgs sa{};
@@ -224,6 +226,13 @@ int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const 
   sa.norm = c.norm_topk_prob;
   sa.route_scale = c.route_scale;
   sa.has_shared_gate = la.sh_gate != nullptr;
+  if (fused) {
+    sa.x = x;
+    sa.gate = gate_w;
+    sa.sh_gate = la.sh_gate;
+    sa.H = c.H;
+    sa.x_bf16 = c.act_dtype == MOE_DTYPE_BF16;
+  }
   HIP_TRY(profile_mark(MOE_STAGE_ROUTER_SELECT, true, st), "profile event");
   HIP_TRY(launch_router_select(sa, st), "router select launch");
   HIP_TRY(profile_mark(MOE_STAGE_ROUTER_SELECT, false, st), "profile event");

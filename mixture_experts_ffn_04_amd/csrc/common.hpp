@@ -92,6 +92,11 @@ struct LogitsArgs {
 struct SelectArgs {
   const double *partial;     // [n_split][T][ldl] logit partial sums
   int n_split;
+  // fused path (few columns and tokens): logits computed by the select
+  // kernel itself from x, the gate and the shared-expert gate row; null x =
+  // read the partial sums
+  const void *x, *gate, *sh_gate;
+  int H, x_bf16;
   const float *router_bias;  // [E] or null
   const float *expert_bias;  // [E] or null
   float *scores;             // [T, E]

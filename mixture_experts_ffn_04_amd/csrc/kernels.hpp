@@ -10,6 +10,9 @@ void router_logits_plan(int T, int H, int ncols, bool bf16, int *mt, int *n_spli
                         int *blocks_per_split);
 hipError_t launch_router_logits(const LogitsArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_router_select(const SelectArgs &a, hipStream_t st);
+// logits fused into the select kernel: up to 512 tokens, 64 columns and
+// next_pow2(columns) x H <= 32K
+bool router_fused_applies(int T, int H, int E, bool shared_gate);
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t st);
 
 enum WFormat { W_F32 = 0, W_BF16 = 1, W_MXFP4 = 2 };

@@ -279,33 +279,21 @@ __device__ __forceinline__ void wave_argmax(float &v, int &idx, float &aux) {
   }
 }
 
+// Score, select and routing weights of token t, one wavefront: v[j] is the
+// fp64 logit sum of expert lane + 64 j (valid ones), gate_logit the fp64
+// logit of the shared-expert gate column.
 template <int J>
-__global__ __launch_bounds__(256) void router_select(SelectArgs a) {
+__device__ __forceinline__ void select_token(const SelectArgs &a, int t, const double (&v)[J],
+                                             double gate_logit) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;  // whole wavefront leaves together
   const float NEG_INF = -__builtin_inff();
-  const size_t slice = (size_t)a.T * a.ldl;
-  const double *prow = a.partial + (size_t)t * a.ldl;
 
-  // fp32 logits: the slices' fp64 partial sums added in order, rounded once;
-  // the optional logit bias is one f32 add after that ([SF941] "What")
+  // fp32 logits: the fp64 sum rounded once; the optional logit bias is one
+  // f32 add after that ([SF941] "What")
   float l[J], s[J], c[J];
   bool valid[J];
-  double v[J];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    valid[j] = lane + 64 * j < a.E;
-    v[j] = valid[j] ? prow[lane + 64 * j] : 0.0;
-  }
-#pragma unroll 4
-  for (int sp = 1; sp < a.n_split; ++sp) {
-    double p[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) p[j] = valid[j] ? prow[sp * slice + lane + 64 * j] : 0.0;
-#pragma unroll
-    for (int j = 0; j < J; ++j) v[j] += p[j];
-  }
+  for (int j = 0; j < J; ++j) valid[j] = lane + 64 * j < a.E;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
@@ -441,11 +429,130 @@ __global__ __launch_bounds__(256) void router_select(SelectArgs a) {
     a.indices[(size_t)t * a.K + lane] = my_idx;
     a.weights[(size_t)t * a.K + lane] = w;
   }
-  if (a.has_shared_gate && lane == 0) {
-    double v = prow[a.E];
-    for (int sp = 1; sp < a.n_split; ++sp) v += prow[sp * slice + a.E];
-    a.gamma[t] = (float)(1.0 / (1.0 + exp(-v)));
+  if (a.has_shared_gate && lane == 0) a.gamma[t] = (float)(1.0 / (1.0 + exp(-gate_logit)));
+}
+
+// Select from the logits kernel's fp64 partial sums (n_split slices of the
+// hidden dimension, added in slice order).
+template <int J>
+__global__ __launch_bounds__(256) void router_select(SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;  // whole wavefront leaves together
+  const size_t slice = (size_t)a.T * a.ldl;
+  const double *prow = a.partial + (size_t)t * a.ldl;
+  double v[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) v[j] = lane + 64 * j < a.E ? prow[lane + 64 * j] : 0.0;
+#pragma unroll 4
+  for (int sp = 1; sp < a.n_split; ++sp) {
+    double p[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) p[j] = lane + 64 * j < a.E ? prow[sp * slice + lane + 64 * j] : 0.0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] += p[j];
   }
+  double g = 0.0;
+  if (a.has_shared_gate) {
+    g = prow[a.E];
+    for (int sp = 1; sp < a.n_split; ++sp) g += prow[sp * slice + a.E];
+  }
+  select_token<J>(a, t, v, g);
+}
+
+// Logits and select in one kernel for few columns (E + gate <= 64) and few
+// tokens: a workgroup of NT threads per token.  Lane groups of
+// L = NT / next_pow2(columns) threads each own one column and split the hidden dimension in 8-element
+// chunks, four chunks per step with independent accumulators (so several
+// loads are in flight); every product of two bf16 (or f32) values is exact
+// in fp64 and the sums are fp64.  Groups reduce through shuffles and LDS,
+// then wave 0 scores and selects.  The fp32 logit is the fp64 sum rounded
+// once.
+template <bool BF16, int NT>
+__global__ __launch_bounds__(NT) void router_fused(SelectArgs a) {
+  constexpr int NW = NT / 64;
+  __shared__ double colsum[NW][64];  // per wave, per column
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  const int ncols = a.E + (a.has_shared_gate ? 1 : 0);
+  int G = 1;
+  while (G < ncols) G <<= 1;
+  const int L = NT / G;  // threads per column
+  const int col = tid / L, sub = tid % L;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  if (col < ncols) {
+    const int step = L * 8;  // elements between a thread's chunks
+    if constexpr (BF16) {
+      const uint16_t *xr = static_cast<const uint16_t *>(a.x) + (size_t)t * a.H;
+      const uint16_t *wr = col < a.E ? static_cast<const uint16_t *>(a.gate) + (size_t)col * a.H
+                                     : static_cast<const uint16_t *>(a.sh_gate);
+      int k = sub * 8;
+      // U chunks per step: all loads issued before the first product
+      auto steps = [&](auto unroll) {
+        constexpr int U = decltype(unroll)::value;
+        for (; k + (U - 1) * step < a.H; k += U * step) {
+          u32x4_t xv[U], wv[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            xv[u] = load16(xr + k + u * step);
+            wv[u] = load16(wr + k + u * step);
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[u & 3] = fma((double)bf16_lo(xv[u][q]), (double)bf16_lo(wv[u][q]), acc[u & 3]);
+              acc[u & 3] = fma((double)bf16_hi(xv[u][q]), (double)bf16_hi(wv[u][q]), acc[u & 3]);
+            }
+        }
+      };
+      steps(std::integral_constant<int, 8>{});
+      steps(std::integral_constant<int, 4>{});
+      for (; k < a.H; k += step) {
+        const u32x4_t xv = load16(xr + k), wv = load16(wr + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[0] = fma((double)bf16_lo(xv[q]), (double)bf16_lo(wv[q]), acc[0]);
+          acc[0] = fma((double)bf16_hi(xv[q]), (double)bf16_hi(wv[q]), acc[0]);
+        }
+      }
+    } else {
+      const float *xr = static_cast<const float *>(a.x) + (size_t)t * a.H;
+      const float *wr = col < a.E ? static_cast<const float *>(a.gate) + (size_t)col * a.H
+                                  : static_cast<const float *>(a.sh_gate);
+      for (int k = sub * 8; k < a.H; k += step) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q & 3] = fma((double)xr[k + q], (double)wr[k + q], acc[q & 3]);
+      }
+    }
+  }
+  double v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  // reduce the column's threads: within a wave, then (columns wider than a
+  // wave) across waves in LDS
+  for (int off = 1; off < min(L, 64); off <<= 1) v += __shfl_xor(v, off, kWave);
+  if (L >= 64) {
+    if (lane == 0) colsum[wave][0] = v;
+  } else if (sub == 0) {
+    colsum[wave][(tid % 64) / L] = v;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // column c's sum: waves own 64 / L columns each when L < 64, or one column
+  // spread over L / 64 waves
+  double cs = 0.0;
+  if (lane < ncols) {
+    if (L >= 64) {
+      const int wpc = L / 64;  // waves per column
+      for (int w = 0; w < wpc; ++w) cs += colsum[lane * wpc + w][0];
+    } else {
+      const int cpw = 64 / L;  // columns per wave
+      cs = colsum[lane / cpw][lane % cpw];
+    }
+  }
+  double vv[1];
+  vv[0] = cs;
+  const double g = a.has_shared_gate ? __shfl(cs, a.E, kWave) : 0.0;
+  select_token<1>(a, t, vv, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -511,9 +618,35 @@ hipError_t launch_router_logits(const LogitsArgs &a, bool bf16, hipStream_t st) 
   return hipGetLastError();
 }
 
+// Fused when a token's padded row of products is short (next_pow2(columns)
+// x H <= 32K elements): wider rows make each thread's load chain long enough
+// that the split logits kernel plus select is faster.
+bool router_fused_applies(int T, int H, int E, bool shared_gate) {
+  const int ncols = E + (shared_gate ? 1 : 0);
+  int G = 1;
+  while (G < ncols) G <<= 1;
+  return T <= 512 && ncols <= 64 && (long)G * H <= 32768;
+}
+
 hipError_t launch_router_select(const SelectArgs &a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const dim3 grid((a.T + 3) / 4), block(256);
+  if (a.x) {  // logits computed here, a workgroup per token
+    if (!router_fused_applies(a.T, a.H, a.E, a.has_shared_gate)) return hipErrorInvalidValue;
+    // wide rows (padded columns x hidden > 16K elements): 1024 threads, so a
+    // thread's chain of dependent loads stays short
+    int G = 1;
+    while (G < a.E + (a.has_shared_gate ? 1 : 0)) G <<= 1;
+    const bool wide = (long)G * a.H > 16384;
+    if (a.x_bf16) {
+      if (wide) hipLaunchKernelGGL((router_fused<true, 1024>), dim3(a.T), dim3(1024), 0, st, a);
+      else hipLaunchKernelGGL((router_fused<true, 256>), dim3(a.T), block, 0, st, a);
+    } else {
+      if (wide) hipLaunchKernelGGL((router_fused<false, 1024>), dim3(a.T), dim3(1024), 0, st, a);
+      else hipLaunchKernelGGL((router_fused<false, 256>), dim3(a.T), block, 0, st, a);
+    }
+    return hipGetLastError();
+  }
   if (a.E <= 64)
     hipLaunchKernelGGL(router_select<1>, grid, block, 0, st, a);
   else if (a.E <= 128)
