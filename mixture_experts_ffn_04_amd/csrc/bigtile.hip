@@ -398,9 +398,10 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile(TiledGemmArgs ta) 
 // ---------------------------------------------------------------------------
 // bf16 weights: the same tile fed by direct-to-LDS loads.  Each load
 // instruction of a wavefront writes 64 x 16 bytes to consecutive LDS
-// addresses without passing through registers, so the workgroup keeps three
-// 32-deep stages in flight (a ring of four; three with the low halves of h)
-// instead of one register-staged slice.  A lane chooses which global chunk it
+// addresses without passing through registers, so the workgroup keeps up to
+// four 32-deep stages in flight beyond the one being multiplied (a ring of
+// five; of three with the low halves of h) instead of one register-staged
+// slice.  A lane chooses which global chunk it
 // fetches so that the data lands at its swizzled LDS position.  The compiler
 // does not track these loads: the waits on the vector-memory counter and the
 // barriers are explicit.
@@ -419,7 +420,7 @@ struct DmaPlan {
   static constexpr size_t LDS_BYTES = (size_t)NSTAGE * SLOT * 16;
   static_assert(NSTAGE >= 3 && LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(NSTAGE * SLOT * 16 >= 4 * 32 * 132 * 4, "epilogue staging fits the ring");
-  static_assert((NSTAGE - 2) * OPS < 64, "vmcnt range");
+  static_assert((NSTAGE - 1) * OPS < 64, "vmcnt range");
 };
 
 __device__ __forceinline__ void dma16(const char *g, u32x4_t *l) {
@@ -432,6 +433,21 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Scheduling order of a region with NREAD LDS reads (next step's operands)
+// and NMFMA MFMAs (this step's): an MFMA, then two reads, until every read is
+// issued, then the remaining MFMAs.  The reads go out early, behind a
+// single MFMA each, so their latency is covered by the rest of the step.
+template <int NREAD, int NMFMA, int I = 0>
+__device__ __forceinline__ void interleave_reads() {
+  if constexpr (I < NREAD) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD - I >= 2 ? 2 : 1, 0);  // up to two LDS reads
+    interleave_reads<NREAD, NMFMA - 1, I + 2>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);                   // the other MFMAs
+  }
 }
 
 // workgroup barrier that the compiler does not move memory operations across
@@ -530,60 +546,81 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
       if constexpr (GATE_UP) return nf < 2 ? wn * 64 + nf * 32 : BN / 2 + wn * 64 + (nf - 2) * 32;
       else return wn * 128 + nf * 32;
     };
-    auto compute = [&](int slot, auto full) {  // `full`: as in expert_bigtile
+    // Operand fragments of one 16-deep step, two register sets: the MFMAs of
+    // step t run while the fragments of step t + 1 are read from LDS.
+    constexpr int NB = LO ? 2 * MF : MF;
+    u32x4_t af[2][4], bf[2][NB];
+    auto fetch = [&](int set, int slot, int kk, auto full) {
       constexpr bool FULL = decltype(full)::value;
       const u32x4_t *Wt = smem + slot * SLOT, *Xt = Wt + WUN;
-      constexpr int NB = LO ? 2 * MF : MF;
-      u32x4_t af[2][4], bf[2][NB];
-      auto fetch = [&](int set, int kk) {
-        const int ch = 2 * kk + lh;
+      const int ch = 2 * kk + lh;
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
+      for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf) {
-          if (FULL || mf < mf_count) {
-            bf[set][mf] = Xt[unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
-            if constexpr (LO) bf[set][MF + mf] = Xt[XUN + unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
-          }
+      for (int mf = 0; mf < MF; ++mf) {
+        if (FULL || mf < mf_count) {
+          bf[set][mf] = Xt[unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
+          if constexpr (LO) bf[set][MF + mf] = Xt[XUN + unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
         }
-      };
-      fetch(0, 0);
+      }
+    };
+    auto mma = [&](int set, auto full) {
+      constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk == 0) fetch(1, 1);
+      for (int mf = 0; mf < MF; ++mf) {
+        if (FULL || mf < mf_count) {
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf) {
-          if (FULL || mf < mf_count) {
+          for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[set][nf], bf[set][mf], acc[mf][nf]);
+          if constexpr (LO) {
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[kk][nf], bf[kk][mf], acc[mf][nf]);
-            if constexpr (LO) {
-#pragma unroll
-              for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[kk][nf], bf[kk][MF + mf], acc[mf][nf]);
-            }
+            for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[set][nf], bf[set][MF + mf], acc[mf][nf]);
           }
         }
       }
     };
+    // fetch of the next step and MFMAs of this one in one scheduling region,
+    // the reads spread between the MFMAs (full tiles: no guards, so one region)
+    auto step = [&](int next_set, int next_slot, int next_kk, int set, auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      fetch(next_set, next_slot, next_kk, full);
+      mma(set, full);
+      if constexpr (FULL) interleave_reads<4 + NB, MF * 4 * (LO ? 2 : 1)>();
+    };
+    // wait until the stage `after` stages before the newest issued one has landed
+    auto wait_stage = [&](int after) {
+      switch (after) {
+        case 0: wait_vmem<0>(); break;
+        case 1: wait_vmem<OPS>(); break;
+        case 2: wait_vmem<(NSTAGE >= 3 ? 2 : 0) * OPS>(); break;
+        case 3: wait_vmem<(NSTAGE >= 4 ? 3 : 0) * OPS>(); break;
+        case 4: wait_vmem<(NSTAGE >= 5 ? 4 : 0) * OPS>(); break;
+        default: wait_vmem<(NSTAGE >= 6 ? 5 : 0) * OPS>(); break;
+      }
+    };
 
-    // ---- pipeline: stage s waits for its own loads, one barrier, then the
-    // loads of stage s + NSTAGE - 1 go into the slot freed by stage s - 1
+    // ---- pipeline over 32-deep stages (two 16-deep steps each).  The ring
+    // holds NSTAGE stages.  In the second step of stage s every wave waits
+    // for stage s + 1, one barrier follows (after it nobody reads slot s any
+    // more), stage s + NSTAGE is issued into slot s, and the first fragments
+    // of stage s + 1 are read while the second step's MFMAs run.
     auto run = [&](auto full) {
 #pragma unroll
-      for (int d = 0; d < NSTAGE - 1; ++d)
+      for (int d = 0; d < NSTAGE; ++d)
         if (d < nst) issue(d);
-      for (int s = 0; s < nst; ++s) {
-        const int after = min(NSTAGE - 2, nst - 1 - s);  // stages issued after stage s
-        switch (after) {  // wait until only those are outstanding
-          case 0: wait_vmem<0>(); break;
-          case 1: wait_vmem<OPS>(); break;
-          case 2: wait_vmem<(NSTAGE >= 4 ? 2 : 0) * OPS>(); break;
-          case 3: wait_vmem<(NSTAGE >= 5 ? 3 : 0) * OPS>(); break;
-          default: wait_vmem<(NSTAGE >= 6 ? 4 : 0) * OPS>(); break;
-        }
+      wait_stage(min(NSTAGE - 1, nst - 1));
+      barrier_lds();
+      fetch(0, 0, 0, full);
+      for (int s = 0; s < nst - 1; ++s) {
+        const int slot = s % NSTAGE;
+        step(1, slot, 1, 0, full);
+        wait_stage(min(NSTAGE - 2, nst - 2 - s));
         barrier_lds();
-        if (s + NSTAGE - 1 < nst) issue(s + NSTAGE - 1);
-        compute(s % NSTAGE, full);
+        if (s + NSTAGE < nst) issue(s + NSTAGE);
+        step(0, (s + 1) % NSTAGE, 0, 1, full);
       }
+      fetch(1, (nst - 1) % NSTAGE, 1, full);
+      mma(0, full);
+      mma(1, full);
     };
     if (c.nrows - c.m0 >= TM) run(std::true_type{});
     else run(std::false_type{});
