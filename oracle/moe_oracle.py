@@ -491,3 +491,70 @@ def token_output(x_row64, indices_row, weights_row32, get_expert, limit,
     if sh_gate_up64 is not None:
         acc = acc + shared_expert(x1, sh_gate_up64, sh_down64, limit, sh_gate64)[0]
     return acc
+
+
+# ----------------------------------------------------------------------------
+# Load-balancing state ([SF1073] commit notes on tokens_per_expert, on
+# MoEBalancing's moe/step_balance and on update_expert_bias)
+# ----------------------------------------------------------------------------
+def masked_expert_counts(indices: np.ndarray, n_experts: int,
+                         token_mask: Optional[np.ndarray] = None) -> np.ndarray:
+    """Kept slots per expert, int64 [E].
+
+    [SF1073] commit note on tokens_per_expert: each training forward adds its
+    kept slots, those of tokens that moe_token_mask keeps, to an int64 count
+    per expert.  READING: the mask is one flag per token (the kept-block mask
+    expanded to draft tokens, per the note on moe_token_mask) and a kept token
+    contributes all K of its slots; no mask keeps every token.
+    """
+    idx = np.asarray(indices)
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for t in range(idx.shape[0]):
+        if token_mask is not None and not bool(token_mask[t]):
+            continue
+        for k in range(idx.shape[1]):
+            counts[int(idx[t, k])] += 1
+    return counts
+
+
+def step_balance(counts: np.ndarray) -> float:
+    """moe/step_balance of pooled counts, as fp32.
+
+    [SF1073] commit note on MoEBalancing: 1 when the load is uniform, E / K
+    when it has collapsed onto K experts.  READING: the largest count over the
+    mean count, E * max(c) / sum(c) (the only plain ratio with both stated
+    values); evaluated in fp64, rounded once to fp32.  READING: with no kept
+    slot the load counts as uniform, 1.
+    """
+    c = np.asarray(counts, dtype=np.int64)
+    total = int(c.sum())
+    if total == 0:
+        return float(F32(1.0))
+    return float(F32(F64(c.size) * F64(int(c.max())) / F64(total)))
+
+
+def update_expert_bias(expert_bias32: np.ndarray, counts: np.ndarray, rate: float) -> np.ndarray:
+    """One DeepSeek-V3 sign step of the selection-only expert bias, fp32 [E].
+
+    [SF1073] commit note on update_expert_bias: one sign step with a
+    zero-mean delta, fed the step's pooled kept-slot counts; rate 0 keeps the
+    bias fixed.  The step raises the bias of experts below the mean load and
+    lowers it for those above: s_e = sign(mean(c) - c_e), decided exactly on
+    integers as sign(sum(c) - E * c_e).  READING of "zero-mean": the delta is
+    rate * (s_e - mean(s)), with mean(s) = sum(s) / E; fp32 arithmetic in this
+    order: m = f32(sum s) / f32(E); d_e = f32(rate) * (f32(s_e) - m);
+    bias_e + d_e.
+    """
+    b = np.asarray(expert_bias32, dtype=F32).copy()
+    if rate == 0.0:
+        return b
+    c = np.asarray(counts, dtype=np.int64)
+    n = c.size
+    total = int(c.sum())
+    s = np.array([(total > n * int(ce)) - (total < n * int(ce)) for ce in c], dtype=np.int64)
+    m = F32(F32(int(s.sum())) / F32(n))
+    r = F32(rate)
+    for e in range(n):
+        d = F32(r * F32(F32(int(s[e])) - m))
+        b[e] = F32(b[e] + d)
+    return b

@@ -551,3 +551,70 @@ def test_selection_margins():
     idx = O.select(c, 2)
     m = O.selection_margins(c, idx)
     assert abs(m[0] - (0.5 - 0.4)) < 1e-7
+
+
+# ----------------------------------------------------------------------------
+# Load-balancing state ([SF1073] commit notes on tokens_per_expert,
+# moe/step_balance and update_expert_bias)
+# ----------------------------------------------------------------------------
+def test_masked_counts_match_bincount_of_kept_tokens():
+    rng = np.random.default_rng(11)
+    idx = rng.integers(0, 12, size=(50, 3)).astype(np.int32)
+    mask = rng.random(50) < 0.6
+    got = O.masked_expert_counts(idx, 12, mask)
+    want = np.bincount(idx[mask].ravel(), minlength=12)
+    assert np.array_equal(got, want)
+    assert got.dtype == np.int64
+    assert int(got.sum()) == 3 * int(mask.sum())
+    # no mask keeps every token; an all-false mask keeps none
+    assert np.array_equal(O.masked_expert_counts(idx, 12), O.expert_counts(idx, 12))
+    assert not O.masked_expert_counts(idx, 12, np.zeros(50, bool)).any()
+
+
+def test_step_balance_closed_forms():
+    # uniform load -> 1; load collapsed onto K of E experts -> E / K
+    assert O.step_balance(np.full(8, 5)) == 1.0
+    E, K, T = 8, 2, 40
+    collapsed = np.zeros(E, np.int64)
+    collapsed[[3, 6]] = T
+    assert O.step_balance(collapsed) == E / K
+    # hand-worked: E * max / sum = 4 * 3 / 4
+    assert O.step_balance(np.array([3, 1, 0, 0])) == 3.0
+    # no kept slot: reported as uniform
+    assert O.step_balance(np.zeros(6, np.int64)) == 1.0
+
+
+def test_bias_sign_step_hand_worked():
+    # counts [3, 1, 0, 0]: mean 1 -> s = [-1, 0, +1, +1], mean(s) = 1/4;
+    # with rate 2^-10 every step is exact in fp32
+    r = 2.0 ** -10
+    b0 = np.array([0.5, -0.25, 0.0, 1.0], np.float32)
+    got = O.update_expert_bias(b0, np.array([3, 1, 0, 0]), r)
+    want = b0 + np.array([-1.25, -0.25, 0.75, 0.75], np.float32) * np.float32(r)
+    assert np.array_equal(got, want)
+    # zero-mean delta: the bias sum is unchanged (exact here)
+    assert float(got.astype(np.float64).sum()) == float(b0.astype(np.float64).sum())
+
+
+def test_bias_sign_step_invariants():
+    rng = np.random.default_rng(5)
+    b0 = rng.standard_normal(16).astype(np.float32) * np.float32(0.01)
+    # rate 0 keeps a loaded bias fixed, bitwise (negative zeros included)
+    b0[3] = np.float32(-0.0)
+    counts = rng.integers(0, 100, 16)
+    same = O.update_expert_bias(b0, counts, 0.0)
+    assert same.tobytes() == b0.tobytes()
+    # uniform load: every sign is 0, nothing moves
+    assert np.array_equal(O.update_expert_bias(b0, np.full(16, 7), 0.01), b0)
+    # overloaded experts go down, underloaded go up, ties with the mean stay
+    counts = np.array([10, 0, 5, 5] * 4)
+    new = O.update_expert_bias(np.zeros(16, np.float32), counts, 0.01)
+    assert new[counts > 5].max() < new[counts == 5].min() and new[counts < 5].min() > new[counts == 5].max()
+    # mean 5 exactly: the ties get -rate * mean(s) = 0
+    assert (new[counts == 5] == 0).all()
+    # the sign is decided on integers even when the mean is not an integer
+    c = np.array([1, 2, 2])  # mean 5/3
+    s = np.sign(c.mean() - c)
+    new = O.update_expert_bias(np.zeros(3, np.float32), c, 1.0)
+    want = (s - s.mean()).astype(np.float32)
+    assert np.allclose(new, want, rtol=0, atol=1e-7)
