@@ -171,6 +171,37 @@ def run_gpu(wl, steps, warmup, copies=None):
     return res, host
 
 
+def time_balance(wl, routing, steps):
+    """Per-call time of the load-balancing state on this batch's routing: the
+    masked kept-slot count (one per forward) and the step balance + bias sign
+    step + reset (one per optimizer step)."""
+    import torch
+    from mixture_experts_ffn_04_amd import api
+    from mixture_experts_ffn_04_amd import workloads as W
+
+    dev = routing.indices.device
+    _, mask, bias = W.gen_balance_inputs(0, wl.T, wl.K, wl.E, keep=0.8)
+    mask, bias = mask.to(dev), bias.to(dev)
+    counts = torch.zeros(wl.E, dtype=torch.int64, device=dev)
+    sb = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        api.balance_count(routing.indices, counts, mask)
+        api.balance_update(counts, bias, 1e-3, sb)
+    t = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    t[0].record()
+    for _ in range(steps):
+        api.balance_count(routing.indices, counts, mask)
+    t[1].record()
+    for _ in range(steps):
+        api.balance_update(counts, bias, 1e-3, sb)
+    t[2].record()
+    torch.cuda.synchronize()
+    return {"count_us": round(t[0].elapsed_time(t[1]) / steps * 1e3, 2),
+            "update_us": round(t[1].elapsed_time(t[2]) / steps * 1e3, 2),
+            "slots": wl.T * wl.K, "experts": wl.E}
+
+
 # HBM traffic of the dominant kernel, per launch, from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE counter runs (scaled by a plain copy of known size), with the
 # hash of the kernel sources they were taken on: a changed kernel reports null.
@@ -340,6 +371,7 @@ def main(argv=None):
                    "expert_weights": wl.w_dtype, "weight_copies": res["copies"],
                    "active_experts": res["active"], "max_tokens_per_expert": res["max_count"]},
         "roofline": roofline(wl, res),
+        "balance": time_balance(wl, host["routing"], args.steps),
     }
     extra = []
     if args.extra_T and args.extra_T != wl.T and args.workload != "tiny_f32":

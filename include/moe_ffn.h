@@ -18,7 +18,9 @@
  *              route_scale, clamped SwiGLU, one ungated shared expert), on the
  *              V4.1 converter (FP4 experts: two e2m1 codes per byte, low
  *              nibble first, one e8m0 scale per 32 inputs; w1/w3 fused into
- *              gate_up_proj, w2 into down_proj).
+ *              gate_up_proj, w2 into down_proj); on the load balancing
+ *              (int64 tokens_per_expert over kept slots, moe/step_balance,
+ *              update_expert_bias as one DeepSeek-V3 sign step).
  *   [SGL48763] sglang PR #48763 "[Feat] dflash: Serve MoE FFN drafts for
  *              DFlash and DSpark" -- commit notes on the DraftMoE forward
  *              (fp32 router logits, sigmoid-gated shared expert, a rank with
@@ -235,6 +237,44 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
                     void *out, float *scores, int32_t *indices, float *weights,
                     int32_t *counts, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * Load-balancing state ([SF1073] commit notes on tokens_per_expert, on
+ * MoEBalancing and on update_expert_bias).
+ *
+ * moe_balance_count adds one forward's kept slots to the running counts:
+ *   tokens_per_expert[e] += #{(t, k) : indices[t,k] = e and token_mask[t] != 0}
+ *   indices            [T, K] int32 (e.g. the `indices` output of a forward);
+ *                      ids outside [0, E) are not counted
+ *   token_mask         [T] uint8, nullable (NULL keeps every token): the
+ *                      per-token kept flag (moe_token_mask)
+ *   tokens_per_expert  [E] int64, accumulated in place (integer adds; the
+ *                      result does not depend on their order)
+ * T = 0 enqueues nothing.  MOE_ERR_INVALID for T < 0, K or E <= 0, a NULL or
+ * misaligned pointer; MOE_ERR_UNSUPPORTED for E > MOE_MAX_EXPERTS.
+ */
+MOE_API int moe_balance_count(const int32_t *indices, const uint8_t *token_mask, int32_t T,
+                              int32_t K, int32_t E, int64_t *tokens_per_expert, void *stream);
+
+/*
+ * moe_balance_update ends a balancing step on the pooled counts c = the
+ * current tokens_per_expert [E]:
+ *   step_balance[0] = E * max(c) / sum(c) as fp32 (evaluated in fp64; 1 when
+ *                     sum(c) = 0): 1 for a uniform load, E / K when the load
+ *                     has collapsed onto K experts; nullable
+ *   expert_bias[e] += rate * (s_e - sum(s) / E), s_e = sign(sum(c) - E * c_e)
+ *                     (the DeepSeek-V3 sign step: underloaded experts go up,
+ *                     overloaded ones down; the delta has zero mean); fp32 in
+ *                     that order, no fused multiply-add; skipped when
+ *                     bias_update_rate is 0 (a loaded bias stays fixed), and
+ *                     expert_bias may then be NULL
+ *   tokens_per_expert[e] = 0 afterwards.
+ * Pooling counts across ranks (an all-reduce) is the caller's, before this
+ * call.  MOE_ERR_INVALID for E <= 0, a non-finite rate, a NULL or misaligned
+ * required pointer; MOE_ERR_UNSUPPORTED for E > MOE_MAX_EXPERTS.
+ */
+MOE_API int moe_balance_update(int64_t *tokens_per_expert, float *expert_bias, int32_t E,
+                               float bias_update_rate, float *step_balance, void *stream);
 
 /* Static text for a status code. */
 MOE_API const char *moe_status_string(int status);

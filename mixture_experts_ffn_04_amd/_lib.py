@@ -19,7 +19,8 @@ MOE_SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route", "moe_ffn_forward",
-            "moe_status_string", "moe_last_error", "moe_abi_version", "moe_profile_stage")
+            "moe_status_string", "moe_last_error", "moe_abi_version", "moe_profile_stage",
+            "moe_balance_count", "moe_balance_update")
 
 STAGES = ("router_logits", "router_select", "permute", "gate_up", "shared_gate_up", "down",
           "shared_down", "combine")
@@ -86,6 +87,10 @@ def lib() -> ctypes.CDLL:
     L.moe_profile_stage.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     L.moe_profile_stage.restype = ctypes.c_int
+    L.moe_balance_count.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P]
+    L.moe_balance_count.restype = ctypes.c_int
+    L.moe_balance_update.argtypes = [P, P, ctypes.c_int32, ctypes.c_float, P, P]
+    L.moe_balance_update.restype = ctypes.c_int
     L.moe_abi_version.argtypes = []
     L.moe_abi_version.restype = ctypes.c_int
     if L.moe_abi_version() != ABI_VERSION:

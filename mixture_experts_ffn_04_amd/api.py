@@ -182,6 +182,45 @@ def ffn_forward(cfg: MoeConfig, x: torch.Tensor, weights: LayerWeights, *, out=N
     return out
 
 
+def balance_count(indices: torch.Tensor, tokens_per_expert: torch.Tensor, token_mask=None, *,
+                  stream=None) -> torch.Tensor:
+    """moe_balance_count: tokens_per_expert [E] int64 += the kept slots of
+    `indices` [T, K] int32 (token_mask [T] bool/uint8 keeps tokens; None keeps
+    all).  Returns tokens_per_expert."""
+    dev = indices.device
+    if indices.dim() != 2:
+        raise ValueError("indices must be [T, K]")
+    T, K = indices.shape
+    E = tokens_per_expert.numel()
+    if token_mask is not None and token_mask.dtype == torch.bool:
+        token_mask = token_mask.view(torch.uint8)
+    check(lib().moe_balance_count(
+        _ptr(indices, "indices", dtype=torch.int32, device=dev),
+        _ptr(token_mask, "token_mask", dtype=torch.uint8, shape=(T,), device=dev),
+        T, K, E, _ptr(tokens_per_expert, "tokens_per_expert", dtype=torch.int64, shape=(E,), device=dev),
+        _stream(stream)))
+    return tokens_per_expert
+
+
+def balance_update(tokens_per_expert: torch.Tensor, expert_bias: Optional[torch.Tensor],
+                   bias_update_rate: float, step_balance: Optional[torch.Tensor] = None, *,
+                   stream=None) -> Optional[torch.Tensor]:
+    """moe_balance_update: step balance into step_balance [1] f32 (allocated
+    when None), the bias sign step on expert_bias [E] f32 in place, and the
+    counts zeroed.  Returns step_balance."""
+    dev = tokens_per_expert.device
+    E = tokens_per_expert.numel()
+    if step_balance is None:
+        step_balance = torch.empty(1, dtype=torch.float32, device=dev)
+    check(lib().moe_balance_update(
+        _ptr(tokens_per_expert, "tokens_per_expert", dtype=torch.int64, shape=(E,), device=dev),
+        _ptr(expert_bias, "expert_bias", dtype=torch.float32, shape=(E,), device=dev),
+        E, ctypes.c_float(bias_update_rate),
+        _ptr(step_balance, "step_balance", dtype=torch.float32, shape=(1,), device=dev),
+        _stream(stream)))
+    return step_balance
+
+
 def empty_routing(cfg: MoeConfig, device="cuda") -> Routing:
     return Routing(torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=device),
                    torch.empty(cfg.T, cfg.K, dtype=torch.int32, device=device),

@@ -601,4 +601,40 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   return MOE_OK;
 }
 
+MOE_API int moe_balance_count(const int32_t *indices, const uint8_t *token_mask, int32_t T, int32_t K,
+                              int32_t E, int64_t *tokens_per_expert, void *stream) {
+  if (T < 0) return fail(MOE_ERR_INVALID, "T = %d < 0", T);
+  if (K <= 0 || E <= 0) return fail(MOE_ERR_INVALID, "K = %d and E = %d must be positive", K, E);
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", E, MOE_MAX_EXPERTS);
+  if ((double)T * K > 2.0e9) return fail(MOE_ERR_UNSUPPORTED, "T * K = %.0f slots is too many", (double)T * K);
+  if (!tokens_per_expert) return fail(MOE_ERR_INVALID, "tokens_per_expert is NULL");
+  if (reinterpret_cast<uintptr_t>(tokens_per_expert) & 7)
+    return fail(MOE_ERR_INVALID, "tokens_per_expert is not 8-byte aligned");
+  if (T == 0) return MOE_OK;
+  if (!indices) return fail(MOE_ERR_INVALID, "indices is NULL");
+  if (reinterpret_cast<uintptr_t>(indices) & 3) return fail(MOE_ERR_INVALID, "indices is not 4-byte aligned");
+  BalanceCountArgs a{indices, token_mask, tokens_per_expert, T, K, E};
+  HIP_TRY(launch_balance_count(a, reinterpret_cast<hipStream_t>(stream)), "balance count launch");
+  return MOE_OK;
+}
+
+MOE_API int moe_balance_update(int64_t *tokens_per_expert, float *expert_bias, int32_t E,
+                               float bias_update_rate, float *step_balance, void *stream) {
+  if (E <= 0) return fail(MOE_ERR_INVALID, "E = %d must be positive", E);
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", E, MOE_MAX_EXPERTS);
+  if (!std::isfinite(bias_update_rate)) return fail(MOE_ERR_INVALID, "bias_update_rate is not finite");
+  if (!tokens_per_expert) return fail(MOE_ERR_INVALID, "tokens_per_expert is NULL");
+  if (reinterpret_cast<uintptr_t>(tokens_per_expert) & 7)
+    return fail(MOE_ERR_INVALID, "tokens_per_expert is not 8-byte aligned");
+  if (bias_update_rate != 0.f && !expert_bias)
+    return fail(MOE_ERR_INVALID, "expert_bias is NULL with a non-zero bias_update_rate");
+  if (expert_bias && (reinterpret_cast<uintptr_t>(expert_bias) & 3))
+    return fail(MOE_ERR_INVALID, "expert_bias is not 4-byte aligned");
+  if (step_balance && (reinterpret_cast<uintptr_t>(step_balance) & 3))
+    return fail(MOE_ERR_INVALID, "step_balance is not 4-byte aligned");
+  BalanceUpdateArgs a{tokens_per_expert, expert_bias, step_balance, bias_update_rate, E};
+  HIP_TRY(launch_balance_update(a, reinterpret_cast<hipStream_t>(stream)), "balance update launch");
+  return MOE_OK;
+}
+
 }  // extern "C"

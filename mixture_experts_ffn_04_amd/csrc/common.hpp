@@ -193,4 +193,21 @@ struct CombineArgs {
   int T, H, K;
 };
 
+// counts[e] += #{(t, k) : indices[t,k] = e, mask[t] != 0}
+struct BalanceCountArgs {
+  const int32_t *indices;  // [T, K]
+  const uint8_t *mask;     // [T] or null (every token kept)
+  int64_t *counts;         // [E], accumulated
+  int T, K, E;
+};
+
+// step balance, bias sign step, counts reset
+struct BalanceUpdateArgs {
+  int64_t *counts;  // [E], zeroed
+  float *bias;      // [E] or null
+  float *balance;   // [1] or null
+  float rate;
+  int E;
+};
+
 }  // namespace moe

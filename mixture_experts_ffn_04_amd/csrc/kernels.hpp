@@ -43,4 +43,7 @@ int bigtile_rows();
 hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t st);
 
+hipError_t launch_balance_count(const BalanceCountArgs &a, hipStream_t st);
+hipError_t launch_balance_update(const BalanceUpdateArgs &a, hipStream_t st);
+
 }  // namespace moe

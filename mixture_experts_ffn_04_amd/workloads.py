@@ -38,6 +38,7 @@ TID = {
     "w_gate_up": 5, "w_down": 6, "b_gate_up": 7, "b_down": 8,
     "sh_gate_up": 9, "sh_down": 10, "sh_gate": 11,
     "codes_gate_up": 12, "codes_down": 13, "scales_gate_up": 14, "scales_down": 15,
+    "balance_indices": 16, "token_mask": 17, "balance_bias": 18,
 }
 
 
@@ -393,3 +394,18 @@ def algorithmic_flops(w: Workload) -> dict:
     return {"gate_up": 4 * T * K * H * I, "down": 2 * T * K * H * I,
             "routed": routed, "shared": shared, "router": router,
             "total": routed + shared + router}
+
+
+def gen_balance_inputs(seed: int, T: int, K: int, E: int, skew: float = 1.0, keep: float = 1.0,
+                       sid: int = 0):
+    """Synthetic routing for the load-balancing state: expert ids [T, K] int32
+    (id = floor(E * u^skew) for uniform u, so skew > 1 crowds the low ids, as a
+    collapsing router would), a kept-token mask [T] bool (keep = fraction
+    kept; 1 keeps all) and an fp32 bias [E] ~ N(0, 0.01).  CPU tensors."""
+    u = draw_u32(seed, TID["balance_indices"], sid, T * K).double() / 4294967296.0
+    idx = torch.clamp((E * u.pow(skew)).floor(), max=E - 1).to(torch.int32).view(T, K)
+    m = draw_u32(seed, TID["token_mask"], sid, T).double() / 4294967296.0
+    mask = m < keep
+    bias = draw_normal_f32(seed, TID["balance_bias"], sid, E, 0.01)
+    return idx, mask, bias
+

@@ -191,3 +191,26 @@ def test_route_refuses_bad_arguments(L):
     args[4] = None
     assert L.moe_route(ctypes.byref(c), *args, P(FAKE), ctypes.c_size_t(1 << 40), None) == -1
     assert L.moe_status_string(-3).decode() == "workspace missing or too small"
+
+
+def test_balance_refuses_bad_arguments(L):
+    P = ctypes.c_void_p
+    f = ctypes.c_float
+    # moe_balance_count(indices, mask, T, K, E, counts, stream): refused before any GPU work
+    assert L.moe_balance_count(P(FAKE), None, -1, 2, 8, P(FAKE), None) == -1       # T < 0
+    assert L.moe_balance_count(P(FAKE), None, 10, 0, 8, P(FAKE), None) == -1       # K = 0
+    assert L.moe_balance_count(P(FAKE), None, 10, 2, 0, P(FAKE), None) == -1       # E = 0
+    assert L.moe_balance_count(P(FAKE), None, 10, 2, 2048, P(FAKE), None) == -2    # E above the limit
+    assert L.moe_balance_count(None, None, 10, 2, 8, P(FAKE), None) == -1          # NULL indices
+    assert L.moe_balance_count(P(FAKE), None, 10, 2, 8, None, None) == -1          # NULL counts
+    assert L.moe_balance_count(P(FAKE), None, 10, 2, 8, P(FAKE + 4), None) == -1   # counts misaligned
+    assert "8-byte" in L.moe_last_error().decode()
+    assert L.moe_balance_count(None, None, 0, 2, 8, P(FAKE), None) == 0            # T = 0: no work
+    # moe_balance_update(counts, bias, E, rate, balance, stream)
+    assert L.moe_balance_update(P(FAKE), P(FAKE), 0, f(0.1), None, None) == -1     # E = 0
+    assert L.moe_balance_update(P(FAKE), P(FAKE), 4096, f(0.1), None, None) == -2  # E above the limit
+    assert L.moe_balance_update(None, P(FAKE), 8, f(0.1), None, None) == -1        # NULL counts
+    assert L.moe_balance_update(P(FAKE), None, 8, f(0.1), None, None) == -1        # rate without a bias
+    assert "expert_bias" in L.moe_last_error().decode()
+    assert L.moe_balance_update(P(FAKE), P(FAKE), 8, f(math.nan), None, None) == -1
+    assert L.moe_balance_update(P(FAKE), P(FAKE + 2), 8, f(0.1), None, None) == -1  # bias misaligned
