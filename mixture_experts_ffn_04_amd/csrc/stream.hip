@@ -38,6 +38,8 @@
 // of each bf16 stage (two steps each of an MXFP4 stage) and merge their
 // partial sums in LDS in wave order at the end, so results do not depend on
 // timing.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "tile.hpp"
 
@@ -141,7 +143,7 @@ struct Plan {
   static constexpr int NXS = LO ? 2 : 1;           // activation streams (hi, lo)
   static constexpr int LOADS = G::W_LOADS + NXS * X_LOADS + (G::S_LOADS > 0 ? 1 : 0);
   static constexpr int DEPTH = (WF == W_MXFP4 && NS == 4) ? 2 : (16 / LOADS >= 4 ? 4 : (16 / LOADS >= 3 ? 3 : 2));
-  static constexpr int S_UNITS = (2 * G::S_BYTES + 15) / 16;
+  static constexpr int S_UNITS = (2 * G::S_BYTES * 4 + 15) / 16;  // f32 scales, two buffers
   static constexpr int MAIN_UNITS = 2 * G::W_UNITS + 2 * NXS * X_UNITS;
   static constexpr int RED_UNITS = 4 * MT * NS * 64;
   static constexpr size_t LDS_BYTES = (size_t)(MAIN_UNITS + S_UNITS) * 16;
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
   extern __shared__ u32x4_t lds[];
   u32x4_t *Wl = lds;                                // [2][W_UNITS]
   u32x4_t *Xl = lds + 2 * G::W_UNITS;               // [2][NXS][X_UNITS]
-  uint8_t *Sl = reinterpret_cast<uint8_t *>(lds + MAIN_UNITS);  // [2][S_BYTES]
+  float *Sl = reinterpret_cast<float *>(lds + MAIN_UNITS);      // [2][S_BYTES] block scales as f32
   f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
 #pragma unroll
         for (int j = 0; j < G::W_LOADS; ++j) Wl[buf * G::W_UNITS + unit8(j * 32 + (tid >> 3), wch)] = wv[d][j];
 #pragma unroll
-        for (int j = 0; j < G::S_LOADS; ++j) Sl[buf * G::S_BYTES + j * kThreads + tid] = (uint8_t)sv[d][j];
+        for (int j = 0; j < G::S_LOADS; ++j) Sl[buf * G::S_BYTES + j * kThreads + tid] = e8m0_to_f32(sv[d][j] & 0xffu);
       }
 #pragma unroll
       for (int j = 0; j < X_LOADS; ++j) {
@@ -299,13 +301,16 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
 #pragma unroll
       for (int sx = 0; sx < NS; ++sx) acc[mt][sx] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf, int s) {
+    // `full` (a std::bool_constant): the stage spans SK reduction elements,
+    // so no step is skipped (no exec-mask branches around the MFMAs)
+    auto compute = [&](int buf, int s, auto full) {
+      constexpr bool FULL = decltype(full)::value;
       const int kv = min(SK, a.Kdim - s * SK);
       constexpr int STEPS = SK / 32 / 4;  // MFMA steps per wave per stage
 #pragma unroll
       for (int i = 0; i < STEPS; ++i) {
         const int q = wave * STEPS + i;
-        if (32 * q < kv) {
+        if (FULL || 32 * q < kv) {
           u32x4_t wa[NS];
 #pragma unroll
           for (int sx = 0; sx < NS; ++sx) {
@@ -314,12 +319,12 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
               wa[sx] = Wl[buf * G::W_UNITS + unit16(row, 4 * q + lg)];
             } else {
               const uint32_t *u = reinterpret_cast<const uint32_t *>(&Wl[buf * G::W_UNITS + unit8(row, q)]);
-              wa[sx] = decode_e2m1x8(u[lg], e8m0_to_f32(Sl[buf * G::S_BYTES + row * 8 + q]));
+              wa[sx] = decode_e2m1x8(u[lg], Sl[buf * G::S_BYTES + row * 8 + q]);
             }
           }
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            if (mt < mt_count) {
+            if ((WF == W_MXFP4 && MT == 1) || mt < mt_count) {  // a chunk holds at least one row
               const int u = XCH == 16 ? unit16(mt * 16 + lr, 4 * q + lg) : unit32(mt * 16 + lr, 4 * q + lg);
 #pragma unroll
               for (int h = 0; h < NXS; ++h) {
@@ -348,7 +353,9 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
         stash(d, s & 1);
         issue(d, s + kDepth);
         __syncthreads();
-        compute(s & 1, s);
+        // stages before the last are whole; the unguarded copy pays off for
+        // MXFP4 (its decode sits between the guards), not for bf16
+        compute(s & 1, s, std::integral_constant<bool, WF == W_MXFP4>{});
       }
     }
 #pragma unroll
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
         stash(d, s & 1);
         if (s + kDepth < nst) issue(d, s + kDepth);
         __syncthreads();
-        compute(s & 1, s);
+        compute(s & 1, s, std::false_type{});
       }
     }
 
