@@ -7,8 +7,8 @@
 // slot maps that the grouped expert GEMMs and the combine read.
 //
 // One workgroup of 1024 threads: LDS histogram (integer atomics, so the
-// counts are exact and order independent), block scan over the experts,
-// scatter through per-expert LDS cursors.  The order of the rows inside one
+// counts are exact and order independent), one block scan of the five
+// per-expert quantities, scatter through per-expert LDS cursors.  The order of the rows inside one
 // expert depends on atomic timing; every row is computed independently of
 // its position, and the combine reads rows through the slot -> row map, so
 // the layer's results do not.
@@ -20,51 +20,74 @@ namespace moe {
 constexpr int kPermuteThreads = 1024;
 static_assert(MOE_MAX_EXPERTS <= kPermuteThreads, "one expert per thread in the scan");
 
-// Inclusive scan of one int per thread over the block (1024 threads).
-__device__ __forceinline__ int block_inclusive_scan(int v, int *wsum) {
+// Inclusive scans of N ints per thread over the block (1024 threads), all N
+// in one pass (one set of barriers).
+template <int N>
+__device__ __forceinline__ void block_inclusive_scan(int (&v)[N], int (*wsum)[kPermuteThreads / 64]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int n = __shfl_up(v, off, kWave);
-    if (lane >= off) v += n;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int n = __shfl_up(v[i], off, kWave);
+      if (lane >= off) v[i] += n;
+    }
   }
-  if (lane == 63) wsum[wave] = v;
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) wsum[i][wave] = v[i];
+  }
   __syncthreads();
-  if (wave == 0) {
-    int w = lane < kPermuteThreads / 64 ? wsum[lane] : 0;
+  if (wave < N) {  // wave i scans the wave totals of value i
+    int w = lane < kPermuteThreads / 64 ? wsum[wave][lane] : 0;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
       const int n = __shfl_up(w, off, kWave);
       if (lane >= off) w += n;
     }
-    if (lane < kPermuteThreads / 64) wsum[lane] = w;
+    if (lane < kPermuteThreads / 64) wsum[wave][lane] = w;
   }
   __syncthreads();
-  if (wave > 0) v += wsum[wave - 1];
-  __syncthreads();
-  return v;
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += wsum[i][wave - 1];
+  }
 }
 
 __global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) {
   __shared__ int hist[MOE_MAX_EXPERTS];
-  __shared__ int wsum[kPermuteThreads / 64];
+  __shared__ int wsum[5][kPermuteThreads / 64];
   const int tid = threadIdx.x;
 
   if (tid < a.E) hist[tid] = 0;
+  // up to kHeld slots per thread keep their expert ids in registers for the
+  // scatter below (no second read)
+  constexpr int kHeld = 4;
+  const bool held = a.n_slots <= kHeld * kPermuteThreads;
+  int ids[kHeld];
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) {
+    const int s = tid + j * kPermuteThreads;
+    ids[j] = held && s < a.n_slots ? a.indices[s] : -1;
+  }
   __syncthreads();
-  for (int s = tid; s < a.n_slots; s += kPermuteThreads) atomicAdd(&hist[a.indices[s]], 1);
+  if (held) {
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j)
+      if (ids[j] >= 0) atomicAdd(&hist[ids[j]], 1);
+  } else {
+    for (int s = tid; s < a.n_slots; s += kPermuteThreads) atomicAdd(&hist[a.indices[s]], 1);
+  }
   __syncthreads();
 
   const int v = tid < a.E ? hist[tid] : 0;
-  const int incl = block_inclusive_scan(v, wsum);
   const int any = (tid < a.E && v > 0) ? 1 : 0;
-  const int any_incl = block_inclusive_scan(any, wsum);
   const int mtiles = (v + a.tile_rows - 1) / a.tile_rows;
-  const int mt_incl = block_inclusive_scan(mtiles, wsum);
   const int mtiles2 = (v + a.tile_rows2 - 1) / a.tile_rows2;
-  const int mt2_incl = block_inclusive_scan(mtiles2, wsum);
   const int nch = (v + a.chunk_rows - 1) / a.chunk_rows;
-  const int ch_incl = block_inclusive_scan(nch, wsum);
+  int sc[5] = {v, any, mtiles, mtiles2, nch};
+  block_inclusive_scan<5>(sc, wsum);
+  const int incl = sc[0], any_incl = sc[1], mt_incl = sc[2], mt2_incl = sc[3], ch_incl = sc[4];
   if (tid < a.E) {
     a.counts[tid] = v;
     if (a.user_counts) a.user_counts[tid] = v;
@@ -89,10 +112,22 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_slots(PermuteArgs a) 
   }
   __syncthreads();
 
-  for (int s = tid; s < a.n_slots; s += kPermuteThreads) {
-    const int row = atomicAdd(&hist[a.indices[s]], 1);
-    a.perm[row] = s;
-    a.inv[s] = row;
+  if (held) {
+#pragma unroll
+    for (int j = 0; j < kHeld; ++j) {
+      if (ids[j] >= 0) {
+        const int s = tid + j * kPermuteThreads;
+        const int row = atomicAdd(&hist[ids[j]], 1);
+        a.perm[row] = s;
+        a.inv[s] = row;
+      }
+    }
+  } else {
+    for (int s = tid; s < a.n_slots; s += kPermuteThreads) {
+      const int row = atomicAdd(&hist[a.indices[s]], 1);
+      a.perm[row] = s;
+      a.inv[s] = row;
+    }
   }
 }
 

@@ -480,11 +480,15 @@ void launch_ns(const ExpertGemmArgs &a, bool gather, bool lo, long max_chunks, h
 
 template <int MT, bool GATE_UP>
 void launch_mt(const ExpertGemmArgs &a, WFormat wf, bool gather, bool lo, long max_chunks, hipStream_t st) {
-  // MXFP4 items span 64 weight rows when the output columns allow it
+  // MXFP4 items span 64 weight rows when the output columns allow it; so do
+  // bf16 down items of 16-row chunks (half as many items, each streaming
+  // twice the weight rows: measured 8-13% faster on down, slower on gate_up)
   if (wf == W_MXFP4 && a.N % (GATE_UP ? 32 : 64) == 0)
     launch_ns<MT, W_MXFP4, 4, GATE_UP>(a, gather, lo, max_chunks, st);
   else if (wf == W_MXFP4)
     launch_ns<MT, W_MXFP4, 2, GATE_UP>(a, gather, lo, max_chunks, st);
+  else if (!GATE_UP && MT == 1 && a.N % 64 == 0)
+    launch_ns<MT, W_BF16, 4, GATE_UP>(a, gather, lo, max_chunks, st);
   else
     launch_ns<MT, W_BF16, 2, GATE_UP>(a, gather, lo, max_chunks, st);
 }
