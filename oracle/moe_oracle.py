@@ -558,3 +558,190 @@ def update_expert_bias(expert_bias32: np.ndarray, counts: np.ndarray, rate: floa
         d = F32(r * F32(F32(int(s[e])) - m))
         b[e] = F32(b[e] + d)
     return b
+
+
+# ----------------------------------------------------------------------------
+# Backward of the layer ([SF1033] "Router" section: forward returns scores,
+# indices, weights and the MoE FFN trains with grouped GEMMs; [SF1073] commit
+# note on the V4.1 port: the forward output and every gradient are compared;
+# the expert bias shifts the picks, never the weights)
+# ----------------------------------------------------------------------------
+@dataclass
+class LayerGrads:
+    """Gradients of sum(out * dout) with respect to every input, fp64."""
+    dx: np.ndarray                      # [T, H]
+    dgate: np.ndarray                   # [E, H]
+    drouter_bias: Optional[np.ndarray]  # [E] (logit-bias variant only)
+    dw_gate_up: dict                    # e -> [2I, H], experts with slots only
+    dw_down: dict                       # e -> [H, I]
+    db_gate_up: dict                    # e -> [2I] (experts with linear biases)
+    db_down: dict                       # e -> [H]
+    dsh_gate_up: Optional[np.ndarray]   # [2Is, H]
+    dsh_down: Optional[np.ndarray]      # [H, Is]
+    dsh_gate: Optional[np.ndarray]      # [H]
+
+
+def swiglu_backward(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float,
+                    dh: np.ndarray):
+    """(d gate_pre, d up_pre) of h = silu(min(g, L)) * clip(u, -L, L).
+
+    silu'(z) = sigma(z) * (1 + z * (1 - sigma(z))).  READING: where the clamp
+    binds the gradient is cut; on the boundary itself (g = L, u = +-L) it
+    passes, as for a clamp whose gradient mask is inclusive.
+    """
+    g = np.asarray(gate_pre, dtype=F64)
+    u = np.asarray(up_pre, dtype=F64)
+    if math.isinf(limit):
+        gc, uc = g, u
+        g_pass = np.ones_like(g, dtype=bool)
+        u_pass = np.ones_like(u, dtype=bool)
+    else:
+        gc, uc = np.minimum(g, limit), np.clip(u, -limit, limit)
+        g_pass = g <= limit
+        u_pass = (u >= -limit) & (u <= limit)
+    sig = 1.0 / (1.0 + np.exp(-gc))
+    silu_g = gc * sig
+    dsilu = sig * (1.0 + gc * (1.0 - sig))
+    dg = np.where(g_pass, dh * uc * dsilu, 0.0)
+    du = np.where(u_pass, dh * silu_g, 0.0)
+    return dg, du
+
+
+def score_backward(logits64: np.ndarray, scores64: np.ndarray, dscores: np.ndarray,
+                   fn: str) -> np.ndarray:
+    """d logits [E] of one token's scores [E] (fp64 values).
+
+    softmax: ds -> s * (ds - sum(ds * s)); sigmoid: ds * s * (1 - s);
+    sqrt(softplus(l)): ds * sigma(l) / (2 s).
+    """
+    l = np.asarray(logits64, dtype=F64)
+    s = np.asarray(scores64, dtype=F64)
+    ds = np.asarray(dscores, dtype=F64)
+    if fn == "softmax":
+        return s * (ds - np.dot(ds, s))
+    if fn == "sigmoid":
+        return ds * s * (1.0 - s)
+    if fn == "sqrtsoftplus":
+        return ds * (1.0 / (1.0 + np.exp(-l))) / (2.0 * s)
+    raise ValueError(fn)
+
+
+def weights_backward(picked64: np.ndarray, dweights: np.ndarray, norm_topk_prob: bool,
+                     route_scale: float, eps: float = float(RENORM_EPS)) -> np.ndarray:
+    """d picked scores [K] of w_k = rs * s_k / (sum_j s_j + eps) (renormalised)
+    or w_k = rs * s_k."""
+    s = np.asarray(picked64, dtype=F64)
+    dw = np.asarray(dweights, dtype=F64)
+    rs = float(route_scale)
+    if not norm_topk_prob:
+        return rs * dw
+    d = s.sum() + eps
+    return rs * dw / d - rs * np.dot(dw, s) / (d * d)
+
+
+def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="softmax",
+                 n_group=1, topk_group=1, norm_topk_prob=True, route_scale=1.0,
+                 expert_bias=None, router_bias=None, limit=math.inf,
+                 sh_gate_up64=None, sh_down64=None, sh_gate64=None) -> LayerGrads:
+    """Gradients of the layer at (x, weights) for the output gradient dout.
+
+    The selection (indices) is the forward's (route(), fp32 decisions) and is
+    held fixed: it is piecewise constant, and the expert bias that shifts it
+    gets no gradient.  Everything else is differentiated exactly in fp64 at
+    fp64 values (logits, scores, weights and pre-activations are not rounded
+    here).  Steps, the forward's in reverse: combine -> routed experts (down,
+    SwiGLU, gate_up) and shared expert (with its sigmoid gate) -> routing
+    weights -> scores -> logits -> gate and x.
+    """
+    x = np.asarray(x64, dtype=F64)
+    gate = np.asarray(gate64, dtype=F64)
+    dout = np.asarray(dout64, dtype=F64)
+    r = route(x, gate, k=k, score_fn=score_fn, n_group=n_group, topk_group=topk_group,
+              norm_topk_prob=norm_topk_prob, route_scale=route_scale,
+              expert_bias=expert_bias, router_bias=router_bias)
+    idx = r.indices
+    t_count, h_dim = x.shape
+    logits = x @ gate.T
+    if router_bias is not None:
+        logits = logits + np.asarray(router_bias, dtype=F64)
+    if score_fn == "softmax":
+        z = np.exp(logits - logits.max(axis=-1, keepdims=True))
+        scores = z / z.sum(axis=-1, keepdims=True)
+    elif score_fn == "sigmoid":
+        scores = 1.0 / (1.0 + np.exp(-logits))
+    else:
+        scores = np.sqrt(np.maximum(logits, 0.0) + np.log1p(np.exp(-np.abs(logits))))
+
+    dx = np.zeros_like(x)
+    dgate = np.zeros_like(gate)
+    drb = np.zeros(n_experts) if router_bias is not None else None
+    dwgu, dwd, dbgu, dbd = {}, {}, {}, {}
+    has_sh = sh_gate_up64 is not None
+    if has_sh:
+        wsgu = np.asarray(sh_gate_up64, dtype=F64)
+        wsd = np.asarray(sh_down64, dtype=F64)
+        dsgu, dsd = np.zeros_like(wsgu), np.zeros_like(wsd)
+        dsg = np.zeros(h_dim) if sh_gate64 is not None else None
+    for t in range(t_count):
+        xt, dt = x[t], dout[t]
+        picked = scores[t, idx[t]]
+        if norm_topk_prob:
+            w = route_scale * picked / (picked.sum() + float(RENORM_EPS))
+        else:
+            w = route_scale * picked
+        dweights = np.zeros(k)
+        for kk in range(k):
+            e = int(idx[t, kk])
+            ew = get_expert(e)
+            wgu, wd = np.asarray(ew.w_gate_up, dtype=F64), np.asarray(ew.w_down, dtype=F64)
+            inter = wgu.shape[0] // 2
+            pre = wgu @ xt
+            if ew.b_gate_up is not None:
+                pre = pre + ew.b_gate_up
+            h = swiglu(pre[:inter], pre[inter:], limit)
+            y = wd @ h
+            if ew.b_down is not None:
+                y = y + ew.b_down
+            # combine: out_t += w_k * y_k
+            dweights[kk] = np.dot(dt, y)
+            dy = w[kk] * dt
+            # down: y = Wd h (+ b)
+            dh = wd.T @ dy
+            dwd[e] = dwd.get(e, 0.0) + np.outer(dy, h)
+            if ew.b_down is not None:
+                dbd[e] = dbd.get(e, 0.0) + dy
+            # SwiGLU and gate_up: pre = Wgu x (+ b)
+            dg, du = swiglu_backward(pre[:inter], pre[inter:], limit, dh)
+            dpre = np.concatenate([dg, du])
+            dwgu[e] = dwgu.get(e, 0.0) + np.outer(dpre, xt)
+            if ew.b_gate_up is not None:
+                dbgu[e] = dbgu.get(e, 0.0) + dpre
+            dx[t] += wgu.T @ dpre
+        if has_sh:
+            inter_s = wsgu.shape[0] // 2
+            pre_s = wsgu @ xt
+            h_s = swiglu(pre_s[:inter_s], pre_s[inter_s:], limit)
+            sh = wsd @ h_s
+            gam = 1.0 / (1.0 + np.exp(-np.dot(xt, sh_gate64))) if sh_gate64 is not None else 1.0
+            dsh = gam * dt
+            dh_s = wsd.T @ dsh
+            dsd += np.outer(dsh, h_s)
+            dg_s, du_s = swiglu_backward(pre_s[:inter_s], pre_s[inter_s:], limit, dh_s)
+            dpre_s = np.concatenate([dg_s, du_s])
+            dsgu += np.outer(dpre_s, xt)
+            dx[t] += wsgu.T @ dpre_s
+            if sh_gate64 is not None:
+                dz = np.dot(dt, sh) * gam * (1.0 - gam)
+                dx[t] += dz * np.asarray(sh_gate64, dtype=F64)
+                dsg += dz * xt
+        # routing weights -> scores -> logits
+        ds = np.zeros(n_experts)
+        ds[idx[t]] = weights_backward(picked, dweights, norm_topk_prob, route_scale)
+        dl = score_backward(logits[t], scores[t], ds, score_fn)
+        if drb is not None:
+            drb += dl
+        dgate += np.outer(dl, xt)
+        dx[t] += gate.T @ dl
+    return LayerGrads(dx, dgate, drb, dwgu, dwd, dbgu, dbd,
+                      dsgu if has_sh else None, dsd if has_sh else None,
+                      dsg if has_sh and sh_gate64 is not None else None)
