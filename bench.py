@@ -171,6 +171,50 @@ def run_gpu(wl, steps, warmup, copies=None):
     return res, host
 
 
+def time_backward(wl, host, steps):
+    """Per-call time of the layer's backward (moe_ffn_backward) on this
+    batch, with the HBM floor it is measured against: expert weights read
+    (active experts; gate_up twice, down once), every expert's f32 weight
+    gradient written (experts without rows get zeros), x, dout read and dx
+    written.  The backward is for training; the serving step above does not
+    include it."""
+    import torch
+    from mixture_experts_ffn_04_amd import api
+    from mixture_experts_ffn_04_amd import workloads as W
+
+    if wl.w_dtype == "mxfp4":
+        return None
+    cfg = api.config_from_workload(wl)
+    x, lw, r = host["x"], host["base"], host["routing"]
+    dout = W.gen_dout(wl, x.device)
+    ws = torch.empty(max(api.backward_workspace_bytes(cfg), 256), dtype=torch.uint8, device=x.device)
+    for _ in range(2):
+        api.ffn_backward(cfg, x, lw, dout, r, workspace=ws)
+    n = max(3, steps // 20)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(n):
+        api.ffn_backward(cfg, x, lw, dout, r, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / n * 1e3
+    active = int((r.counts > 0).sum().item())
+    wb = 2 if wl.w_dtype == "bf16" else 4
+    ab = 2 if wl.act_dtype == "bf16" else 4
+    per_expert = wl.H * wl.I
+    weight_reads = active * (2 * 2 * per_expert + per_expert) * wb
+    grad_writes = wl.E * 3 * per_expert * 4 + wl.E * wl.H * 4
+    if wl.shared_I:
+        weight_reads += 3 * wl.H * wl.shared_I * ab
+        grad_writes += 3 * wl.H * wl.shared_I * 4
+    act = wl.T * wl.H * (2 * ab + 4) + wl.T * wl.E * 4
+    nbytes = weight_reads + grad_writes + act
+    return {"us": round(us, 2), "bound": "hbm", "algorithmic_bytes": nbytes,
+            "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def time_balance(wl, routing, steps):
     """Per-call time of the load-balancing state on this batch's routing: the
     masked kept-slot count (one per forward) and the step balance + bias sign
@@ -372,6 +416,7 @@ def main(argv=None):
                    "active_experts": res["active"], "max_tokens_per_expert": res["max_count"]},
         "roofline": roofline(wl, res),
         "balance": time_balance(wl, host["routing"], args.steps),
+        "backward": time_backward(wl, host, args.steps),
     }
     extra = []
     if args.extra_T and args.extra_T != wl.T and args.workload != "tiny_f32":

@@ -276,6 +276,49 @@ MOE_API int moe_balance_count(const int32_t *indices, const uint8_t *token_mask,
 MOE_API int moe_balance_update(int64_t *tokens_per_expert, float *expert_bias, int32_t E,
                                float bias_update_rate, float *step_balance, void *stream);
 
+/*
+ * Backward of the layer ([SF1033] "Router" section: forward returns scores,
+ * indices, weights, and the MoE FFN trains; [SF1073] commit note on the V4.1
+ * port: the output and every gradient are compared; the expert bias shifts
+ * the picks, never the weights).
+ *
+ * Gradients of sum(out * dout) for the forward of `cfg` at (x, w), with the
+ * selection held at the forward's `indices` (it is piecewise constant; the
+ * selection-only expert_bias gets no gradient) and the routing weights taken
+ * from the forward's unshifted `scores`:
+ *   x, w     as in moe_ffn_forward (w_dtype f32 or bf16; MXFP4 experts are
+ *            MOE_ERR_UNSUPPORTED here)
+ *   dout     [T, H] act_dtype
+ *   scores   [T, E] f32, indices [T, K] int32: the forward's outputs
+ *   g        gradient outputs, all f32, overwritten (not accumulated):
+ *            dx [T,H] (when T > 0), dgate [E,H], dw_gate_up [E,2I,H],
+ *            dw_down [E,H,I] required; drouter_bias [E] iff w->router_bias; db_gate_up
+ *            [E,2I] and db_down [E,H] iff the expert biases are given;
+ *            dsh_gate_up [2Is,H], dsh_down [H,Is] iff a shared expert;
+ *            dsh_gate [H] iff it is gated.  Experts with no slot get zeros.
+ * Arithmetic is fp32 (inputs widened exactly), fixed summation orders: the
+ * result is bitwise reproducible.  Workspace: moe_backward_workspace_bytes.
+ */
+typedef struct {
+  float *dx;
+  float *dgate;
+  float *drouter_bias;
+  float *dw_gate_up;
+  float *dw_down;
+  float *db_gate_up;
+  float *db_down;
+  float *dsh_gate_up;
+  float *dsh_down;
+  float *dsh_gate;
+} moe_grads;
+
+MOE_API int moe_backward_workspace_bytes(const moe_config *cfg, size_t *bytes);
+
+MOE_API int moe_ffn_backward(const moe_config *cfg, const void *x, const moe_weights *w,
+                             const void *dout, const float *scores, const int32_t *indices,
+                             const moe_grads *g, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
 /* Static text for a status code. */
 MOE_API const char *moe_status_string(int status);
 

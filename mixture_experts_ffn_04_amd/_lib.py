@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0
 
 EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route", "moe_ffn_forward",
             "moe_status_string", "moe_last_error", "moe_abi_version", "moe_profile_stage",
-            "moe_balance_count", "moe_balance_update")
+            "moe_balance_count", "moe_balance_update", "moe_backward_workspace_bytes", "moe_ffn_backward")
 
 STAGES = ("router_logits", "router_select", "permute", "gate_up", "shared_gate_up", "down",
           "shared_down", "combine")
@@ -47,6 +47,12 @@ class MoeWeights(ctypes.Structure):
         ("b_down", ctypes.c_void_p), ("sh_gate_up", ctypes.c_void_p),
         ("sh_down", ctypes.c_void_p), ("sh_gate", ctypes.c_void_p),
     ]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in (
+        "dx", "dgate", "drouter_bias", "dw_gate_up", "dw_down", "db_gate_up", "db_down",
+        "dsh_gate_up", "dsh_down", "dsh_gate")]
 
 
 class MoeError(RuntimeError):
@@ -91,6 +97,11 @@ def lib() -> ctypes.CDLL:
     L.moe_balance_count.restype = ctypes.c_int
     L.moe_balance_update.argtypes = [P, P, ctypes.c_int32, ctypes.c_float, P, P]
     L.moe_balance_update.restype = ctypes.c_int
+    L.moe_backward_workspace_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_backward_workspace_bytes.restype = ctypes.c_int
+    L.moe_ffn_backward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, P, P, ctypes.POINTER(MoeGrads), P,
+                                   ctypes.c_size_t, P]
+    L.moe_ffn_backward.restype = ctypes.c_int
     L.moe_abi_version.argtypes = []
     L.moe_abi_version.restype = ctypes.c_int
     if L.moe_abi_version() != ABI_VERSION:

@@ -16,7 +16,7 @@ from typing import Dict, Optional
 import torch
 
 from . import _lib
-from ._lib import MoeConfig, MoeWeights, check, lib
+from ._lib import MoeConfig, MoeGrads, MoeWeights, check, lib
 
 
 def make_config(T, H, E, I, K, *, act_dtype="bf16", w_dtype="bf16", score_fn="softmax",
@@ -219,6 +219,63 @@ def balance_update(tokens_per_expert: torch.Tensor, expert_bias: Optional[torch.
         _ptr(step_balance, "step_balance", dtype=torch.float32, shape=(1,), device=dev),
         _stream(stream)))
     return step_balance
+
+
+@dataclass
+class Grads:
+    """f32 gradients of sum(out * dout) (moe_ffn_backward); None where the
+    layer has no such input."""
+    dx: torch.Tensor
+    dgate: torch.Tensor
+    dw_gate_up: torch.Tensor
+    dw_down: torch.Tensor
+    drouter_bias: Optional[torch.Tensor] = None
+    db_gate_up: Optional[torch.Tensor] = None
+    db_down: Optional[torch.Tensor] = None
+    dsh_gate_up: Optional[torch.Tensor] = None
+    dsh_down: Optional[torch.Tensor] = None
+    dsh_gate: Optional[torch.Tensor] = None
+
+
+def backward_workspace_bytes(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t()
+    check(lib().moe_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def ffn_backward(cfg: MoeConfig, x: torch.Tensor, weights: LayerWeights, dout: torch.Tensor,
+                 routing: Routing, *, workspace=None, stream=None) -> Grads:
+    """moe_ffn_backward: gradients of sum(out * dout) at the forward whose
+    scores and indices are in `routing`."""
+    dev = x.device
+    T, H, E, I, K, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.K, cfg.shared_I
+    ad = _act_dtype(cfg)
+    w = weights.check(cfg, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = Grads(torch.empty(T, H, **f32), torch.empty(E, H, **f32), torch.empty(E, 2 * I, H, **f32),
+              torch.empty(E, H, I, **f32))
+    if weights.router_bias is not None:
+        g.drouter_bias = torch.empty(E, **f32)
+    if weights.b_gate_up is not None:
+        g.db_gate_up = torch.empty(E, 2 * I, **f32)
+    if weights.b_down is not None:
+        g.db_down = torch.empty(E, H, **f32)
+    if Is > 0:
+        g.dsh_gate_up = torch.empty(2 * Is, H, **f32)
+        g.dsh_down = torch.empty(H, Is, **f32)
+        if cfg.shared_gated:
+            g.dsh_gate = torch.empty(H, **f32)
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_bytes(cfg), 256), dtype=torch.uint8, device=dev)
+    cg = MoeGrads(**{f: (_ptr(getattr(g, f), f).value if getattr(g, f) is not None else None)
+                     for f, _ in MoeGrads._fields_})
+    check(lib().moe_ffn_backward(
+        ctypes.byref(cfg), _ptr(x, "x", dtype=ad, shape=(T, H), device=dev), ctypes.byref(w),
+        _ptr(dout, "dout", dtype=ad, shape=(T, H), device=dev),
+        _ptr(routing.scores, "scores", dtype=torch.float32, shape=(T, E), device=dev),
+        _ptr(routing.indices, "indices", dtype=torch.int32, shape=(T, K), device=dev),
+        ctypes.byref(cg), _ptr(workspace, "workspace"), ctypes.c_size_t(workspace.numel()), _stream(stream)))
+    return g
 
 
 def empty_routing(cfg: MoeConfig, device="cuda") -> Routing:

@@ -601,6 +601,102 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   return MOE_OK;
 }
 
+MOE_API int moe_backward_workspace_bytes(const moe_config *cfg, size_t *bytes) {
+  const int v = moe_validate(cfg);
+  if (v != MOE_OK) return v;
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+  const moe_config &c = *cfg;
+  *bytes = backward_layout(c.T, c.K, c.E, c.H, c.I, c.shared_I, nullptr, nullptr);
+  return ok();
+}
+
+MOE_API int moe_ffn_backward(const moe_config *cfg, const void *x, const moe_weights *wt, const void *dout,
+                             const float *scores, const int32_t *indices, const moe_grads *g, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  const int v = moe_validate(cfg);
+  if (v != MOE_OK) return v;
+  const moe_config &c = *cfg;
+  if (c.w_dtype == MOE_DTYPE_MXFP4) return fail(MOE_ERR_UNSUPPORTED, "the backward takes f32 or bf16 experts");
+  if (!wt) return fail(MOE_ERR_INVALID, "weights is NULL");
+  if (!g) return fail(MOE_ERR_INVALID, "grads is NULL");
+  REQUIRE_PTR(g->dgate, "dgate");
+  REQUIRE_PTR(g->dw_gate_up, "dw_gate_up");
+  REQUIRE_PTR(g->dw_down, "dw_down");
+  if (!wt->router_bias != !g->drouter_bias)
+    return fail(MOE_ERR_INVALID, "drouter_bias is required exactly when router_bias is given");
+  if (!wt->b_gate_up != !g->db_gate_up)
+    return fail(MOE_ERR_INVALID, "db_gate_up is required exactly when b_gate_up is given");
+  if (!wt->b_down != !g->db_down) return fail(MOE_ERR_INVALID, "db_down is required exactly when b_down is given");
+  OPTIONAL_PTR(g->drouter_bias, "drouter_bias");
+  OPTIONAL_PTR(g->db_gate_up, "db_gate_up");
+  OPTIONAL_PTR(g->db_down, "db_down");
+  if (has_shared(c)) {
+    REQUIRE_PTR(wt->sh_gate_up, "sh_gate_up");
+    REQUIRE_PTR(wt->sh_down, "sh_down");
+    REQUIRE_PTR(g->dsh_gate_up, "dsh_gate_up");
+    REQUIRE_PTR(g->dsh_down, "dsh_down");
+    if (c.shared_gated) {
+      REQUIRE_PTR(wt->sh_gate, "sh_gate");
+      REQUIRE_PTR(g->dsh_gate, "dsh_gate");
+    }
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const size_t E = c.E, H = c.H, I = c.I, Is = c.shared_I;
+  if (c.T == 0) {  // no tokens: every gradient is zero
+    auto zero = [&](float *p, size_t n) { return p ? launch_fill_i32(reinterpret_cast<int32_t *>(p), 0, n, st) : hipSuccess; };
+    HIP_TRY(zero(g->dgate, E * H), "fill launch");
+    HIP_TRY(zero(g->dw_gate_up, E * 2 * I * H), "fill launch");
+    HIP_TRY(zero(g->dw_down, E * H * I), "fill launch");
+    HIP_TRY(zero(g->drouter_bias, E), "fill launch");
+    HIP_TRY(zero(g->db_gate_up, E * 2 * I), "fill launch");
+    HIP_TRY(zero(g->db_down, E * H), "fill launch");
+    if (has_shared(c)) {
+      HIP_TRY(zero(g->dsh_gate_up, 2 * Is * H), "fill launch");
+      HIP_TRY(zero(g->dsh_down, H * Is), "fill launch");
+      HIP_TRY(zero(c.shared_gated ? g->dsh_gate : nullptr, H), "fill launch");
+    }
+    return ok();
+  }
+  REQUIRE_PTR(g->dx, "dx");  // [T, H]: only with tokens
+  REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(dout, "dout");
+  REQUIRE_PTR(scores, "scores");
+  REQUIRE_PTR(indices, "indices");
+  REQUIRE_PTR(wt->gate_w, "gate_w");
+  REQUIRE_PTR(wt->w_gate_up, "w_gate_up");
+  REQUIRE_PTR(wt->w_down, "w_down");
+  OPTIONAL_PTR(wt->b_gate_up, "b_gate_up");
+  OPTIONAL_PTR(wt->b_down, "b_down");
+  const size_t need = backward_layout(c.T, c.K, c.E, c.H, c.I, c.shared_I, nullptr, nullptr);
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  BackwardArgs a{};
+  a.T = c.T; a.K = c.K; a.E = c.E; a.H = c.H; a.I = c.I; a.Is = c.shared_I;
+  a.act_bf16 = c.act_dtype == MOE_DTYPE_BF16;
+  a.w_bf16 = c.w_dtype == MOE_DTYPE_BF16;
+  a.norm = c.norm_topk_prob;
+  a.score_fn = c.score_fn;
+  a.limit = c.swiglu_limit;
+  a.route_scale = c.route_scale;
+  a.x = x; a.dout = dout; a.gate_w = wt->gate_w; a.w_gate_up = wt->w_gate_up; a.w_down = wt->w_down;
+  a.b_gate_up = wt->b_gate_up; a.b_down = wt->b_down;
+  if (has_shared(c)) {
+    a.sh_gate_up = wt->sh_gate_up;
+    a.sh_down = wt->sh_down;
+    a.sh_gate = c.shared_gated ? wt->sh_gate : nullptr;
+  }
+  a.scores = scores;
+  a.indices = indices;
+  a.g = GradPtrs{g->dx, g->dgate, g->drouter_bias, g->dw_gate_up, g->dw_down, g->db_gate_up, g->db_down,
+                 g->dsh_gate_up, g->dsh_down, g->dsh_gate};
+  backward_layout(c.T, c.K, c.E, c.H, c.I, c.shared_I, &a, static_cast<char *>(workspace));
+  HIP_TRY(launch_backward(a, st), "backward launch");
+  return ok();
+}
+
 MOE_API int moe_balance_count(const int32_t *indices, const uint8_t *token_mask, int32_t T, int32_t K,
                               int32_t E, int64_t *tokens_per_expert, void *stream) {
   if (T < 0) return fail(MOE_ERR_INVALID, "T = %d < 0", T);

@@ -1,0 +1,620 @@
+// Backward of the layer: gradients of sum(out * dout) with the selection held
+// at the forward's indices.
+//
+// [SF1033] = SpecForge PR #1033 "MoE FFN for DFlash-family drafts: the
+// module", "Router" section (forward returns scores, indices, weights; the
+// weights gather the unshifted scores, renormalise with the 1e-20 guard and
+// scale).  [SF1073] = SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own
+// DSpark draft (stacked on #1035)": the expert bias shifts the picks, never
+// the weights; clamped SwiGLU; the V4.1 port's output and every gradient are
+// compared.  [SGL48763] = sglang PR #48763: sigmoid-gated shared expert.
+//
+// Plan (the forward in reverse; every step fp32, bf16 inputs widened exactly):
+//   1. stable permutation: rows of each expert in slot order (so every sum
+//      over an expert's rows has a fixed order), row -> token, row -> weight
+//   2. routing weights per slot from the forward's scores (as the forward)
+//   3. pre = x Wgu^T (+ b), h = SwiGLU(pre)           grouped GEMM, elementwise
+//   4. gd = dout Wd  (so dh = w gd and dout . y = gd . h + dout . b_down)
+//   5. dweights, dpre = SwiGLU'(pre, w gd)           elementwise, row dots
+//   6. dx_rows = dpre Wgu; dWd = sum_r (w dout)^T h; dWgu = sum_r dpre^T x;
+//      expert bias gradients by ordered row sums
+//   7. the shared expert the same way over all tokens, with its gate
+//   8. router: d weights -> d scores (renormalisation) -> d logits (score
+//      function) -> dgate = dl^T x, drouter_bias = sum_t dl, dx += dl gate
+//   9. dx = sum_k dx_rows (k order) + shared + router + gate terms
+// One generic grouped GEMM (64 x 64 f32 tiles staged in LDS, fixed k order per
+// output) serves every contraction through operand descriptors.
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBT = 64;       // output tile (rows and columns)
+constexpr int kBK = 16;       // reduction slice
+constexpr int kGThreads = 256;
+
+// expert ids index memory: keep them in range whatever the caller passed
+__device__ __forceinline__ int clamp_id(int e, int E) { return min(max(e, 0), E - 1); }
+
+__device__ __forceinline__ float ld_elem(const void *p, int bf16, size_t i) {
+  return bf16 ? bf16_to_f32(static_cast<const uint16_t *>(p)[i]) : static_cast<const float *>(p)[i];
+}
+
+// Element (i, k) of an operand, i = row of the output (A) or column (B).
+// kmajor = 0: element at row(i) * ld + k; kmajor = 1: at row(k) * ld + i.
+// The "row" index runs along i (kmajor 0) or k (kmajor 1); it is offset by
+// the group's first row when token_rows is set, mapped through gather and
+// scaled by scale[] when those are given.  Weight operands use gstride: the
+// group's matrix starts at group * gstride.
+struct GOp {
+  const void *p;
+  int bf16, kmajor, token_rows;
+  long ld, gstride;
+  const int32_t *gather;
+  const float *scale;
+};
+
+// C[m, n] = sum_k A(m, k) B(n, k) for each group.
+//   mode 0: one group of M x N x K.
+//   mode 1: group e has counts[e] rows (M), row base offsets[e]; the row tiles
+//           of all groups are listed by mtile_prefix (64-row tiles); C rows
+//           are the global rows.
+//   mode 2: group e has counts[e] reduction steps (K), row base offsets[e];
+//           C of group e starts at e * cgstride.  Groups with no rows write 0.
+struct GGemm {
+  GOp A, B;
+  float *C;
+  long ldc, cgstride;
+  int M, N, K, mode, E;
+  const int32_t *counts, *offsets, *mtile_prefix;
+};
+
+__device__ __forceinline__ float fetch(const GOp &o, int i, int k, int grp, int r0) {
+  const int rix = (o.token_rows ? r0 : 0) + (o.kmajor ? k : i);
+  const int other = o.kmajor ? i : k;
+  const long src = o.gather ? o.gather[rix] : rix;
+  float v = ld_elem(o.p, o.bf16, (size_t)grp * o.gstride + (size_t)src * o.ld + other);
+  if (o.scale) v *= o.scale[rix];
+  return v;
+}
+
+__global__ __launch_bounds__(kGThreads) void grouped_gemm_f32(GGemm g) {
+  __shared__ float As[kBK][kBT + 4], Bs[kBK][kBT + 4];
+  const int tid = threadIdx.x;
+  const int n0 = blockIdx.x * kBT;
+  int grp = 0, m0, M, K, r0 = 0;
+  if (g.mode == 0) {
+    m0 = blockIdx.y * kBT;
+    M = g.M;
+    K = g.K;
+  } else if (g.mode == 1) {
+    const int q = blockIdx.y;
+    if (q >= g.mtile_prefix[g.E]) return;
+    int lo = 0, hi = g.E;  // mtile_prefix[lo] <= q < mtile_prefix[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g.mtile_prefix[mid] <= q) lo = mid;
+      else hi = mid;
+    }
+    grp = lo;
+    m0 = (q - g.mtile_prefix[lo]) * kBT;
+    M = g.counts[lo];
+    K = g.K;
+    r0 = g.offsets[lo];
+  } else {
+    const int mtiles = (g.M + kBT - 1) / kBT;
+    grp = blockIdx.y / mtiles;
+    m0 = (blockIdx.y - grp * mtiles) * kBT;
+    M = g.M;
+    K = g.counts[grp];
+    r0 = g.offsets[grp];
+  }
+  if (m0 >= M || n0 >= g.N) return;  // whole workgroup leaves together
+
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += kBK) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + u * kGThreads;
+      // k-major operands: consecutive threads walk i (contiguous in memory)
+      const int ai = g.A.kmajor ? idx % kBT : idx / kBK, ak = g.A.kmajor ? idx / kBT : idx % kBK;
+      const int bi = g.B.kmajor ? idx % kBT : idx / kBK, bk = g.B.kmajor ? idx / kBT : idx % kBK;
+      As[ak][ai] = (m0 + ai < M && k0 + ak < K) ? fetch(g.A, m0 + ai, k0 + ak, grp, r0) : 0.f;
+      Bs[bk][bi] = (n0 + bi < g.N && k0 + bk < K) ? fetch(g.B, n0 + bi, k0 + bk, grp, r0) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kBK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float *C = g.C + (g.mode == 2 ? (size_t)grp * g.cgstride : 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+    const size_t row = g.mode == 1 ? (size_t)(r0 + m) : (size_t)m;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n < g.N) C[row * g.ldc + n] = acc[i][j];
+    }
+  }
+}
+
+// ---- 1. stable permutation --------------------------------------------------
+// One workgroup of 1024 threads; wave w owns the slot range [w L, (w+1) L).
+// Per-wave histograms give each wave its first row inside every expert; each
+// wave then ranks its slots in slot order (ballots over 64-slot chunks), so
+// the rows of an expert are its slots in increasing order.
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
+
+__global__ __launch_bounds__(kPermThreads) void stable_permute(BackwardArgs a) {
+  extern __shared__ int hist[];  // [kPermWaves][E]: counts, then each wave's base
+  __shared__ int wsum[kPermWaves][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.T * a.K;
+  const int L = (n + kPermWaves - 1) / kPermWaves;
+  for (int i = tid; i < kPermWaves * a.E; i += kPermThreads) hist[i] = 0;
+  __syncthreads();
+  const int s0 = wave * L, s1 = min(n, s0 + L);
+  for (int s = s0 + lane; s < s1; s += 64) atomicAdd(&hist[wave * a.E + clamp_id(a.indices[s], a.E)], 1);
+  __syncthreads();
+  // per expert: bases of the waves, the total, then a scan over experts
+  int total = 0, tiles = 0;
+  if (tid < a.E) {
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = hist[w * a.E + tid];
+      hist[w * a.E + tid] = total;
+      total += c;
+    }
+    tiles = (total + kBT - 1) / kBT;
+  }
+  int v0 = total, v1 = tiles;  // inclusive scans of (count, tiles) over experts
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int p0 = __shfl_up(v0, off, 64), p1 = __shfl_up(v1, off, 64);
+    if (lane >= off) {
+      v0 += p0;
+      v1 += p1;
+    }
+  }
+  if (lane == 63) {
+    wsum[wave][0] = v0;
+    wsum[wave][1] = v1;
+  }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    v0 += wsum[w][0];
+    v1 += wsum[w][1];
+  }
+  if (tid < a.E) {
+    a.counts[tid] = total;
+    a.offsets[tid] = v0 - total;
+    a.mtile_prefix[tid + 1] = v1;
+    if (tid == 0) a.mtile_prefix[0] = 0;
+    if (tid == a.E - 1) a.offsets[a.E] = v0;
+  }
+  __syncthreads();
+  // rank the wave's slots in order
+  for (int c0 = s0; c0 < s1; c0 += 64) {
+    const int s = c0 + lane;
+    const bool valid = s < s1;
+    const int id = valid ? clamp_id(a.indices[s], a.E) : -1;
+    uint64_t left = __ballot(valid);
+    while (left) {
+      const int leader = __ffsll((unsigned long long)left) - 1;
+      const int lid = __shfl(id, leader, 64);
+      const uint64_t m = __ballot(valid && id == lid);
+      if (valid && id == lid) {
+        const int rank = __popcll(m & ((1ull << lane) - 1ull));
+        const int row = a.offsets[lid] + hist[wave * a.E + lid] + rank;
+        a.row_slot[row] = s;
+        a.row_token[row] = s / a.K;
+        a.row_expert[row] = lid;
+        a.slot_row[s] = row;
+      }
+      left &= ~m;
+      if (lane == leader) hist[wave * a.E + lid] += __popcll(m);
+    }
+  }
+}
+
+// ---- 2. routing weights per slot (the forward's arithmetic) ------------------
+__global__ void slot_weights(BackwardArgs a) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.T) return;
+  float tot = 0.f;
+  for (int k = 0; k < a.K; ++k) tot += a.scores[(size_t)t * a.E + clamp_id(a.indices[t * a.K + k], a.E)];
+  for (int k = 0; k < a.K; ++k) {
+    const float s = a.scores[(size_t)t * a.E + clamp_id(a.indices[t * a.K + k], a.E)];
+    a.slot_w[t * a.K + k] = a.norm ? (s / (tot + 1e-20f)) * a.route_scale : s * a.route_scale;
+  }
+}
+
+__global__ void rows_weight(BackwardArgs a) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < a.T * a.K) a.row_w[r] = a.slot_w[a.row_slot[r]];
+}
+
+// ---- 3. SwiGLU (and the pre-activation bias) --------------------------------
+// pre [rows, 2I] gets the per-group bias added in place; h [rows, I].
+// group = row_expert[r] (routed) or 0 (shared: one group, no bias).
+__global__ void swiglu_fwd(float *pre, float *h, const int32_t *row_group, const void *bias, int bias_bf16,
+                           int rows, int I, float limit) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * I) return;
+  const size_t r = i / I, j = i - r * I;
+  float g = pre[r * 2 * I + j], u = pre[r * 2 * I + I + j];
+  if (bias) {
+    const size_t e = row_group ? (size_t)row_group[r] : 0;
+    g += ld_elem(bias, bias_bf16, e * 2 * I + j);
+    u += ld_elem(bias, bias_bf16, e * 2 * I + I + j);
+    pre[r * 2 * I + j] = g;
+    pre[r * 2 * I + I + j] = u;
+  }
+  const float gc = fminf(g, limit), uc = fminf(fmaxf(u, -limit), limit);
+  h[i] = gc / (1.f + expf(-gc)) * uc;
+}
+
+// ---- 5. dpre = SwiGLU'(pre, w * gd) -------------------------------------------
+// silu'(z) = sigma(z) (1 + z (1 - sigma(z))); the clamp cuts the gradient
+// where it binds (it passes on the boundary itself).
+__global__ void swiglu_bwd(const float *pre, const float *gd, const float *row_scale, float *dpre, int rows, int I,
+                           float limit) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * I) return;
+  const size_t r = i / I, j = i - r * I;
+  const float g = pre[r * 2 * I + j], u = pre[r * 2 * I + I + j];
+  const float dh = (row_scale ? row_scale[r] : 1.f) * gd[i];
+  const float gc = fminf(g, limit), uc = fminf(fmaxf(u, -limit), limit);
+  const float sg = 1.f / (1.f + expf(-gc));
+  const float silu = gc * sg, dsilu = sg * (1.f + gc * (1.f - sg));
+  dpre[r * 2 * I + j] = g <= limit ? dh * uc * dsilu : 0.f;
+  dpre[r * 2 * I + I + j] = (u >= -limit && u <= limit) ? dh * silu : 0.f;
+}
+
+// Row dot products, one wavefront per row, lanes strided then a fixed
+// butterfly: out[r] = sum_i a[r, i] * b[r, i] (+ sum_h dout[tok(r), h] *
+// bias[group(r), h] when bias is set).
+__global__ void row_dots(const float *a, const float *b, int rows, int n, const void *dout, int dout_bf16,
+                         const int32_t *row_token, const int32_t *row_group, const void *bias, int bias_bf16, int H,
+                         float *out, const int32_t *out_index) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  float s = 0.f;
+  for (int i = lane; i < n; i += 64) s = fmaf(a[(size_t)r * n + i], b[(size_t)r * n + i], s);
+  if (bias) {
+    const size_t t = row_token ? (size_t)row_token[r] : (size_t)r, e = row_group ? (size_t)row_group[r] : 0;
+    for (int h = lane; h < H; h += 64)
+      s = fmaf(ld_elem(dout, dout_bf16, t * H + h), ld_elem(bias, bias_bf16, e * H + h), s);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) out[out_index ? out_index[r] : r] = s;
+}
+
+// ---- expert bias gradients: ordered sums over each expert's rows ------------
+// db_down[e, h] = sum_r w_r dout[tok(r), h]; db_gate_up[e, j] = sum_r dpre[r, j]
+__global__ void bias_grads(BackwardArgs a) {
+  const int e = blockIdx.y;
+  const int r0 = a.offsets[e], n = a.counts[e];
+  const int H = a.H, I2 = 2 * a.I;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < H + I2; c += gridDim.x * blockDim.x) {
+    float s = 0.f;
+    if (c < H) {
+      for (int r = r0; r < r0 + n; ++r)
+        s = fmaf(a.row_w[r], ld_elem(a.dout, a.act_bf16, (size_t)a.row_token[r] * H + c), s);
+      if (a.g.db_down) a.g.db_down[(size_t)e * H + c] = s;
+    } else {
+      const int j = c - H;
+      for (int r = r0; r < r0 + n; ++r) s += a.dpre[(size_t)r * I2 + j];
+      if (a.g.db_gate_up) a.g.db_gate_up[(size_t)e * I2 + j] = s;
+    }
+  }
+}
+
+// ---- 7. shared-expert gate: gamma, d gamma -> dz ------------------------------
+// gamma_t = sigmoid(x_t . sh_gate) (the forward's gate, f32 dot in a fixed
+// order); dz_t = (dout_t . sh_t) gamma (1 - gamma), dout_t . sh_t being
+// gd_s[t] . h_s[t] (row_dots into dgam)
+__global__ void shared_gamma(BackwardArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= a.T) return;
+  float s = 0.f;
+  for (int h = lane; h < a.H; h += 64)
+    s = fmaf(ld_elem(a.x, a.act_bf16, (size_t)t * a.H + h), ld_elem(a.sh_gate, a.act_bf16, h), s);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) a.gamma[t] = 1.f / (1.f + expf(-s));
+}
+
+__global__ void shared_dz(BackwardArgs a) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.T) return;
+  const float g = a.gamma[t];
+  a.dz[t] = a.dgam[t] * g * (1.f - g);
+}
+
+// ---- 8. router: d weights -> d scores -> d logits ----------------------------
+// w_k = rs s_k / (S + eps): ds_j = rs dw_j / D - rs (sum_k dw_k s_k) / D^2,
+// D = S + eps (or ds_j = rs dw_j without renormalisation).  Scores:
+// softmax dl = s (ds - sum ds s); sigmoid ds s (1 - s); sqrt(softplus):
+// ds sigma(l) / (2 s) with sigma(l) = 1 - exp(-softplus(l)) = 1 - exp(-s^2).
+__global__ void router_bwd(BackwardArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= a.T) return;
+  const float *s = a.scores + (size_t)t * a.E;
+  // selected scores and their d weights (K <= 16: every lane holds all)
+  float S = 0.f, dws = 0.f;
+  for (int k = 0; k < a.K; ++k) {
+    const float sk = s[clamp_id(a.indices[t * a.K + k], a.E)];
+    S += sk;
+    dws = fmaf(a.dweights[t * a.K + k], sk, dws);
+  }
+  const float D = S + 1e-20f;
+  float dot = 0.f;  // softmax: sum_e ds_e s_e (ds is zero off the selection)
+  for (int k = 0; k < a.K; ++k) {
+    const int e = clamp_id(a.indices[t * a.K + k], a.E);
+    const float dw = a.dweights[t * a.K + k];
+    const float ds = a.norm ? a.route_scale * dw / D - a.route_scale * dws / (D * D) : a.route_scale * dw;
+    dot = fmaf(ds, s[e], dot);
+  }
+  for (int e = lane; e < a.E; e += 64) {
+    float ds = 0.f;
+    for (int k = 0; k < a.K; ++k)
+      if (clamp_id(a.indices[t * a.K + k], a.E) == e) {
+        const float dw = a.dweights[t * a.K + k];
+        ds = a.norm ? a.route_scale * dw / D - a.route_scale * dws / (D * D) : a.route_scale * dw;
+      }
+    const float se = s[e];
+    float dl;
+    if (a.score_fn == 0) dl = se * (ds - dot);
+    else if (a.score_fn == 1) dl = ds * se * (1.f - se);
+    else dl = se > 0.f ? ds * (1.f - expf(-se * se)) / (2.f * se) : 0.f;
+    a.dl[(size_t)t * a.E + e] = dl;
+  }
+}
+
+// drouter_bias[e] = sum_t dl[t, e] (token order)
+__global__ void column_sums(const float *m, int rows, int cols, float *out) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int r = 0; r < rows; ++r) s += m[(size_t)r * cols + c];
+  out[c] = s;
+}
+
+// dsh_gate[h] = sum_t dz[t] x[t, h] (token order)
+__global__ void gate_grad(BackwardArgs a) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= a.H) return;
+  float s = 0.f;
+  for (int t = 0; t < a.T; ++t) s = fmaf(a.dz[t], ld_elem(a.x, a.act_bf16, (size_t)t * a.H + h), s);
+  a.g.dsh_gate[h] = s;
+}
+
+// ---- 9. dx --------------------------------------------------------------------
+__global__ void dx_combine(BackwardArgs a) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)a.T * a.H) return;
+  const size_t t = i / a.H, h = i - t * a.H;
+  float s = 0.f;
+  for (int k = 0; k < a.K; ++k) s += a.dx_rows[(size_t)a.slot_row[t * a.K + k] * a.H + h];
+  if (a.dx_sh) s += a.dx_sh[i];
+  s += a.dx_router[i];
+  if (a.dz && a.sh_gate) s = fmaf(a.dz[t], ld_elem(a.sh_gate, a.act_bf16, h), s);
+  a.g.dx[i] = s;
+}
+
+hipError_t gemm(const GGemm &g, int grid_rows, hipStream_t st) {
+  if (grid_rows <= 0 || g.N <= 0) return hipSuccess;
+  const dim3 grid((g.N + kBT - 1) / kBT, grid_rows);
+  hipLaunchKernelGGL(grouped_gemm_f32, grid, dim3(kGThreads), 0, st, g);
+  return hipGetLastError();
+}
+
+GOp op(const void *p, bool bf16, bool kmajor, long ld, long gstride = 0, bool token_rows = false,
+       const int32_t *gather = nullptr, const float *scale = nullptr) {
+  return GOp{p, bf16 ? 1 : 0, kmajor ? 1 : 0, token_rows ? 1 : 0, ld, gstride, gather, scale};
+}
+
+unsigned blocks(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *a, char *ws) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *p = ws ? ws + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  const size_t rows = (size_t)T * K;
+  BackwardArgs b{};
+  b.row_slot = reinterpret_cast<int32_t *>(take(rows * 4));
+  b.row_token = reinterpret_cast<int32_t *>(take(rows * 4));
+  b.row_expert = reinterpret_cast<int32_t *>(take(rows * 4));
+  b.slot_row = reinterpret_cast<int32_t *>(take(rows * 4));
+  b.counts = reinterpret_cast<int32_t *>(take((size_t)E * 4));
+  b.offsets = reinterpret_cast<int32_t *>(take((size_t)(E + 1) * 4));
+  b.mtile_prefix = reinterpret_cast<int32_t *>(take((size_t)(E + 1) * 4));
+  b.slot_w = reinterpret_cast<float *>(take(rows * 4));
+  b.row_w = reinterpret_cast<float *>(take(rows * 4));
+  b.pre = reinterpret_cast<float *>(take(rows * 2 * I * 4));
+  b.hact = reinterpret_cast<float *>(take(rows * I * 4));
+  b.gd = reinterpret_cast<float *>(take(rows * I * 4));
+  b.dpre = reinterpret_cast<float *>(take(rows * 2 * I * 4));
+  b.dx_rows = reinterpret_cast<float *>(take(rows * H * 4));
+  b.dweights = reinterpret_cast<float *>(take(rows * 4));
+  b.dl = reinterpret_cast<float *>(take((size_t)T * E * 4));
+  b.dx_router = reinterpret_cast<float *>(take((size_t)T * H * 4));
+  if (Is > 0) {
+    b.pre_s = reinterpret_cast<float *>(take((size_t)T * 2 * Is * 4));
+    b.hact_s = reinterpret_cast<float *>(take((size_t)T * Is * 4));
+    b.gd_s = reinterpret_cast<float *>(take((size_t)T * Is * 4));
+    b.dpre_s = reinterpret_cast<float *>(take((size_t)T * 2 * Is * 4));
+    b.dx_sh = reinterpret_cast<float *>(take((size_t)T * H * 4));
+    b.gamma = reinterpret_cast<float *>(take((size_t)T * 4));
+    b.dgam = reinterpret_cast<float *>(take((size_t)T * 4));
+    b.dz = reinterpret_cast<float *>(take((size_t)T * 4));
+  }
+  if (a) {
+    // keep the caller's inputs, outputs and sizes; fill in the scratch
+    BackwardArgs c = *a;
+    c.row_slot = b.row_slot; c.row_token = b.row_token; c.row_expert = b.row_expert; c.slot_row = b.slot_row;
+    c.counts = b.counts; c.offsets = b.offsets; c.mtile_prefix = b.mtile_prefix;
+    c.slot_w = b.slot_w; c.row_w = b.row_w; c.pre = b.pre; c.hact = b.hact; c.gd = b.gd; c.dpre = b.dpre;
+    c.dx_rows = b.dx_rows; c.dweights = b.dweights; c.dl = b.dl; c.dx_router = b.dx_router;
+    c.pre_s = b.pre_s; c.hact_s = b.hact_s; c.gd_s = b.gd_s; c.dpre_s = b.dpre_s; c.dx_sh = b.dx_sh;
+    c.gamma = b.gamma; c.dgam = b.dgam; c.dz = b.dz;
+    if (!c.sh_gate) c.dz = nullptr;
+    *a = c;
+  }
+  return off;
+}
+
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
+#define BW_TRY(x)                         \
+  do {                                    \
+    const hipError_t e_ = (x);            \
+    if (e_ != hipSuccess) return e_;      \
+  } while (0)
+  const int T = a.T, K = a.K, E = a.E, H = a.H, I = a.I, Is = a.Is;
+  const int rows = T * K;
+  const bool ab = a.act_bf16, wb = a.w_bf16;
+  const float lim = a.limit;
+
+  // 1-2. permutation and weights
+  hipLaunchKernelGGL(stable_permute, dim3(1), dim3(kPermThreads), (size_t)kPermWaves * E * 4, st, a);
+  BW_TRY(hipGetLastError());
+  hipLaunchKernelGGL(slot_weights, dim3(blocks(T, 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(rows_weight, dim3(blocks(rows, 256)), dim3(256), 0, st, a);
+  BW_TRY(hipGetLastError());
+  const int mtile_bound = (rows + kBT - 1) / kBT + E;
+
+  // 3. pre = x_rows Wgu^T, h = SwiGLU(pre + b)
+  GGemm g{};
+  g.mode = 1; g.E = E; g.counts = a.counts; g.offsets = a.offsets; g.mtile_prefix = a.mtile_prefix;
+  g.A = op(a.x, ab, false, H, 0, true, a.row_token);
+  g.B = op(a.w_gate_up, wb, false, H, (long)2 * I * H);
+  g.C = a.pre; g.ldc = 2 * I; g.N = 2 * I; g.K = H;
+  BW_TRY(gemm(g, mtile_bound, st));
+  hipLaunchKernelGGL(swiglu_fwd, dim3(blocks((size_t)rows * I, 256)), dim3(256), 0, st, a.pre, a.hact, a.row_expert,
+                     a.b_gate_up, ab ? 1 : 0, rows, I, lim);
+  // 4. gd = dout_rows Wd
+  g.A = op(a.dout, ab, false, H, 0, true, a.row_token);
+  g.B = op(a.w_down, wb, true, I, (long)H * I);
+  g.C = a.gd; g.ldc = I; g.N = I; g.K = H;
+  BW_TRY(gemm(g, mtile_bound, st));
+  // 5. dweights (slot order) and dpre
+  hipLaunchKernelGGL(row_dots, dim3(blocks(rows, 4)), dim3(256), 0, st, a.gd, a.hact, rows, I, a.dout, ab ? 1 : 0,
+                     a.row_token, a.row_expert, a.b_down, ab ? 1 : 0, H, a.dweights, a.row_slot);
+  hipLaunchKernelGGL(swiglu_bwd, dim3(blocks((size_t)rows * I, 256)), dim3(256), 0, st, a.pre, a.gd, a.row_w, a.dpre,
+                     rows, I, lim);
+  BW_TRY(hipGetLastError());
+  // 6. dx_rows = dpre Wgu; dWd = sum_r (w dout)^T h; dWgu = sum_r dpre^T x
+  g.A = op(a.dpre, false, false, 2 * I, 0, true);
+  g.B = op(a.w_gate_up, wb, true, H, (long)2 * I * H);
+  g.C = a.dx_rows; g.ldc = H; g.N = H; g.K = 2 * I;
+  BW_TRY(gemm(g, mtile_bound, st));
+  GGemm w{};
+  w.mode = 2; w.E = E; w.counts = a.counts; w.offsets = a.offsets;
+  w.A = op(a.dout, ab, true, H, 0, true, a.row_token, a.row_w);
+  w.B = op(a.hact, false, true, I, 0, true);
+  w.C = a.g.dw_down; w.ldc = I; w.cgstride = (long)H * I; w.M = H; w.N = I;
+  BW_TRY(gemm(w, E * ((H + kBT - 1) / kBT), st));
+  w.A = op(a.dpre, false, true, 2 * I, 0, true);
+  w.B = op(a.x, ab, true, H, 0, true, a.row_token);
+  w.C = a.g.dw_gate_up; w.ldc = H; w.cgstride = (long)2 * I * H; w.M = 2 * I; w.N = H;
+  BW_TRY(gemm(w, E * ((2 * I + kBT - 1) / kBT), st));
+  if (a.g.db_down || a.g.db_gate_up) {
+    hipLaunchKernelGGL(bias_grads, dim3(blocks(H + 2 * I, 256), E), dim3(256), 0, st, a);
+    BW_TRY(hipGetLastError());
+  }
+
+  // 7. shared expert over all tokens (gamma = 1 when ungated)
+  if (Is > 0) {
+    GGemm s{};
+    s.mode = 0; s.M = T;
+    s.A = op(a.x, ab, false, H);
+    s.B = op(a.sh_gate_up, ab, false, H);
+    s.C = a.pre_s; s.ldc = 2 * Is; s.N = 2 * Is; s.K = H;
+    BW_TRY(gemm(s, (T + kBT - 1) / kBT, st));
+    hipLaunchKernelGGL(swiglu_fwd, dim3(blocks((size_t)T * Is, 256)), dim3(256), 0, st, a.pre_s, a.hact_s,
+                       (const int32_t *)nullptr, (const void *)nullptr, 0, T, Is, lim);
+    s.A = op(a.dout, ab, false, H);
+    s.B = op(a.sh_down, ab, true, Is);
+    s.C = a.gd_s; s.ldc = Is; s.N = Is; s.K = H;
+    BW_TRY(gemm(s, (T + kBT - 1) / kBT, st));
+    const float *gam = nullptr;
+    if (a.sh_gate) {
+      hipLaunchKernelGGL(shared_gamma, dim3(blocks(T, 4)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(row_dots, dim3(blocks(T, 4)), dim3(256), 0, st, a.gd_s, a.hact_s, T, Is, (const void *)nullptr,
+                         0, (const int32_t *)nullptr, (const int32_t *)nullptr, (const void *)nullptr, 0, H, a.dgam,
+                         (const int32_t *)nullptr);
+      hipLaunchKernelGGL(shared_dz, dim3(blocks(T, 256)), dim3(256), 0, st, a);
+      BW_TRY(hipGetLastError());
+      gam = a.gamma;
+    }
+    hipLaunchKernelGGL(swiglu_bwd, dim3(blocks((size_t)T * Is, 256)), dim3(256), 0, st, a.pre_s, a.gd_s, gam, a.dpre_s,
+                       T, Is, lim);
+    s.A = op(a.dpre_s, false, false, 2 * Is);
+    s.B = op(a.sh_gate_up, ab, true, H);
+    s.C = a.dx_sh; s.ldc = H; s.N = H; s.K = 2 * Is;
+    BW_TRY(gemm(s, (T + kBT - 1) / kBT, st));
+    s.M = H; s.K = T;
+    s.A = op(a.dout, ab, true, H, 0, false, nullptr, gam);
+    s.B = op(a.hact_s, false, true, Is);
+    s.C = a.g.dsh_down; s.ldc = Is; s.N = Is;
+    BW_TRY(gemm(s, (H + kBT - 1) / kBT, st));
+    s.M = 2 * Is;
+    s.A = op(a.dpre_s, false, true, 2 * Is);
+    s.B = op(a.x, ab, true, H);
+    s.C = a.g.dsh_gate_up; s.ldc = H; s.N = H;
+    BW_TRY(gemm(s, (2 * Is + kBT - 1) / kBT, st));
+    if (a.sh_gate) {
+      hipLaunchKernelGGL(gate_grad, dim3(blocks(H, 256)), dim3(256), 0, st, a);
+      BW_TRY(hipGetLastError());
+    }
+  }
+
+  // 8. router
+  hipLaunchKernelGGL(router_bwd, dim3(blocks(T, 4)), dim3(256), 0, st, a);
+  BW_TRY(hipGetLastError());
+  GGemm r{};
+  r.mode = 0;
+  r.M = E; r.N = H; r.K = T;
+  r.A = op(a.dl, false, true, E);
+  r.B = op(a.x, ab, true, H);
+  r.C = a.g.dgate; r.ldc = H;
+  BW_TRY(gemm(r, (E + kBT - 1) / kBT, st));
+  r.M = T; r.N = H; r.K = E;
+  r.A = op(a.dl, false, false, E);
+  r.B = op(a.gate_w, ab, true, H);
+  r.C = a.dx_router; r.ldc = H;
+  BW_TRY(gemm(r, (T + kBT - 1) / kBT, st));
+  if (a.g.drouter_bias) {
+    hipLaunchKernelGGL(column_sums, dim3(blocks(E, 256)), dim3(256), 0, st, a.dl, T, E, a.g.drouter_bias);
+    BW_TRY(hipGetLastError());
+  }
+
+  // 9. dx
+  hipLaunchKernelGGL(dx_combine, dim3(blocks((size_t)T * H, 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+#undef BW_TRY
+}
+
+}  // namespace moe

@@ -201,6 +201,26 @@ struct BalanceCountArgs {
   int T, K, E;
 };
 
+// Backward of the layer (csrc/backward.hip).  Inputs, gradient outputs and
+// the scratch arrays that backward_layout() carves from the workspace.
+struct GradPtrs {
+  float *dx, *dgate, *drouter_bias, *dw_gate_up, *dw_down, *db_gate_up, *db_down, *dsh_gate_up, *dsh_down,
+      *dsh_gate;
+};
+struct BackwardArgs {
+  int T, K, E, H, I, Is;
+  int act_bf16, w_bf16, norm, score_fn;
+  float limit, route_scale;
+  const void *x, *dout, *gate_w, *w_gate_up, *w_down, *b_gate_up, *b_down, *sh_gate_up, *sh_down, *sh_gate;
+  const float *scores;
+  const int32_t *indices;
+  GradPtrs g;
+  // scratch
+  int32_t *row_slot, *row_token, *row_expert, *slot_row, *counts, *offsets, *mtile_prefix;
+  float *slot_w, *row_w, *pre, *hact, *gd, *dpre, *dx_rows, *dweights, *dl, *dx_router;
+  float *pre_s, *hact_s, *gd_s, *dpre_s, *dx_sh, *gamma, *dgam, *dz;
+};
+
 // step balance, bias sign step, counts reset
 struct BalanceUpdateArgs {
   int64_t *counts;  // [E], zeroed

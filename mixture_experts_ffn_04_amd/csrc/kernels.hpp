@@ -44,6 +44,11 @@ hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t st);
 
 hipError_t launch_balance_count(const BalanceCountArgs &a, hipStream_t st);
+
+// Workspace bytes of the backward; with `a` and `ws`, also points a's scratch
+// arrays into ws.
+size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *a, char *ws);
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t st);
 hipError_t launch_balance_update(const BalanceUpdateArgs &a, hipStream_t st);
 
 }  // namespace moe

@@ -38,7 +38,7 @@ TID = {
     "w_gate_up": 5, "w_down": 6, "b_gate_up": 7, "b_down": 8,
     "sh_gate_up": 9, "sh_down": 10, "sh_gate": 11,
     "codes_gate_up": 12, "codes_down": 13, "scales_gate_up": 14, "scales_down": 15,
-    "balance_indices": 16, "token_mask": 17, "balance_bias": 18,
+    "balance_indices": 16, "token_mask": 17, "balance_bias": 18, "dout": 19,
 }
 
 
@@ -408,4 +408,9 @@ def gen_balance_inputs(seed: int, T: int, K: int, E: int, skew: float = 1.0, kee
     mask = m < keep
     bias = draw_normal_f32(seed, TID["balance_bias"], sid, E, 0.01)
     return idx, mask, bias
+
+
+def gen_dout(w: Workload, device="cpu") -> torch.Tensor:
+    """Output gradient [T, H] for the backward, ~ N(0, 1) in the activation dtype."""
+    return _act(w, "dout", 0, w.T * w.H, 1.0, device).view(w.T, w.H)
 

@@ -579,6 +579,7 @@ class LayerGrads:
     dsh_gate_up: Optional[np.ndarray]   # [2Is, H]
     dsh_down: Optional[np.ndarray]      # [H, Is]
     dsh_gate: Optional[np.ndarray]      # [H]
+    dweights: Optional[np.ndarray] = None  # [T, K]: d of the routing weights, dout_t . y_k
 
 
 def swiglu_backward(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float,
@@ -676,6 +677,7 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
     dgate = np.zeros_like(gate)
     drb = np.zeros(n_experts) if router_bias is not None else None
     dwgu, dwd, dbgu, dbd = {}, {}, {}, {}
+    dweights_all = np.zeros((t_count, k))
     has_sh = sh_gate_up64 is not None
     if has_sh:
         wsgu = np.asarray(sh_gate_up64, dtype=F64)
@@ -734,6 +736,7 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
                 dz = np.dot(dt, sh) * gam * (1.0 - gam)
                 dx[t] += dz * np.asarray(sh_gate64, dtype=F64)
                 dsg += dz * xt
+        dweights_all[t] = dweights
         # routing weights -> scores -> logits
         ds = np.zeros(n_experts)
         ds[idx[t]] = weights_backward(picked, dweights, norm_topk_prob, route_scale)
@@ -744,4 +747,4 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
         dx[t] += gate.T @ dl
     return LayerGrads(dx, dgate, drb, dwgu, dwd, dbgu, dbd,
                       dsgu if has_sh else None, dsd if has_sh else None,
-                      dsg if has_sh and sh_gate64 is not None else None)
+                      dsg if has_sh and sh_gate64 is not None else None, dweights_all)

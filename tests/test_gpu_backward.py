@@ -1,0 +1,115 @@
+"""GPU parity of moe_ffn_backward against the oracle's ffn_backward.
+
+Every gradient, element by element, within 2e-4 of its RMS (the GPU sums in
+fp32 over up to a few thousand terms from exactly widened bf16 inputs, with
+fp32 scores and weights; the oracle is fp64 throughout), the selection equal
+to the oracle's, and bitwise-equal results on a repeated call.  The router's
+gradients (gate, logit bias) may cancel exactly (top-1 with renormalisation:
+every weight is route_scale), where fp32 leaves rounding noise of f32
+epsilon times the cancelling terms, route_scale * |d weights| per token, in
+each logit gradient; summed over tokens against x, the bound for them has
+the floor 8 * 2^-24 * route_scale * sqrt(sum_t (sum_k |dw_tk|)^2) * max|x|.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_ffn_04_amd import api
+from mixture_experts_ffn_04_amd import workloads as W
+from oracle import moe_oracle as O
+from parity import Case, host, sync
+
+pytestmark = pytest.mark.gpu
+
+Wl = W.Workload
+CASES = [
+    Wl("bwd_top1_t72", T=72, H=256, E=8, I=128, K=1),
+    Wl("bwd_top2_shared_gated_logitbias", T=90, H=192, E=8, I=96, K=2, score_fn="sigmoid",
+       route_scale=2.5, shared_I=64, shared_gated=True, router_bias_std=0.1),
+    Wl("bwd_groups_sqrtsoftplus_clamp", T=70, H=128, E=16, I=64, K=4, score_fn="sqrtsoftplus",
+       n_group=4, topk_group=2, route_scale=1.5, swiglu_limit=0.3, shared_I=96, expert_bias_std=0.05),
+    Wl("bwd_linear_biases", T=65, H=160, E=12, I=96, K=3, expert_linear_bias_std=0.02,
+       norm_topk_prob=False),
+    Wl("bwd_f32", T=64, H=256, E=8, I=128, K=2, act_dtype="f32", w_dtype="f32", shared_I=64),
+    Wl("bwd_many_rows_t300", T=300, H=96, E=6, I=160, K=2, shared_I=32, shared_gated=True),
+    Wl("bwd_t1", T=1, H=64, E=4, I=32, K=2),
+    # the serving-size draft layer at its real shape (8 experts x 1536, top-1, H=4096)
+    W.workload("qwen3_8b_moe_draft", T=72),
+]
+
+
+def _dense(d, E, shape):
+    out = np.zeros((E,) + shape)
+    for e, v in d.items():
+        out[e] = v
+    return out
+
+
+def _check(name, got, want, report, rel=2e-4, floor=0.0):
+    g = got.detach().double().cpu().numpy()
+    w = np.asarray(want, dtype=np.float64)
+    assert g.shape == w.shape, (name, g.shape, w.shape)
+    rms = float(np.sqrt(np.mean(w * w))) if w.size else 0.0
+    err = float(np.max(np.abs(g - w))) if w.size else 0.0
+    report[name] = (err, rms)
+    assert np.all(np.isfinite(g)), name
+    assert err <= rel * rms + floor + 1e-12, (name, err, rms, floor)
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
+def test_backward_matches_oracle(wl):
+    print(f"[backward] {wl.name} T={wl.T} H={wl.H} E={wl.E} I={wl.I} K={wl.K}", flush=True)
+    c = Case(wl)
+    out, r = c.forward()
+    dout = W.gen_dout(wl, "cuda")
+    g = api.ffn_backward(c.cfg, c.x, c.lw, dout, r)
+    sync()
+    g2 = api.ffn_backward(c.cfg, c.x, c.lw, dout, r)
+    sync()
+    for f in ("dx", "dgate", "dw_gate_up", "dw_down"):  # bitwise reproducible
+        assert torch.equal(getattr(g, f), getattr(g2, f)), f
+
+    x64 = c.x64()
+    sh_gu, sh_d, sh_g = c.shared64()
+    og = O.ffn_backward(
+        x64, c.gate64(), c.expert, O.to_f64(host(dout), wl.act_dtype), n_experts=wl.E, k=wl.K,
+        score_fn=wl.score_fn, n_group=wl.n_group, topk_group=wl.topk_group,
+        norm_topk_prob=wl.norm_topk_prob, route_scale=wl.route_scale,
+        expert_bias=c.bias(c.lw.expert_bias), router_bias=c.bias(c.lw.router_bias), limit=wl.swiglu_limit,
+        sh_gate_up64=sh_gu, sh_down64=sh_d, sh_gate64=sh_g)
+    oi = c.oracle_route().indices
+    assert np.array_equal(host(r.indices), oi), "selection differs from the oracle's"
+    rep = {}
+    _check("dx", g.dx, og.dx, rep)
+    dw_tok = np.abs(og.dweights).sum(axis=1)
+    floor = 8 * 2.0 ** -24 * wl.route_scale * float(np.sqrt(np.sum(dw_tok ** 2))) * float(np.abs(x64).max())
+    _check("dgate", g.dgate, og.dgate, rep, floor=floor)
+    _check("dw_gate_up", g.dw_gate_up, _dense(og.dw_gate_up, wl.E, (2 * wl.I, wl.H)), rep)
+    _check("dw_down", g.dw_down, _dense(og.dw_down, wl.E, (wl.H, wl.I)), rep)
+    if og.drouter_bias is not None:
+        _check("drouter_bias", g.drouter_bias, og.drouter_bias, rep, floor=floor)
+    if og.db_gate_up:
+        _check("db_gate_up", g.db_gate_up, _dense(og.db_gate_up, wl.E, (2 * wl.I,)), rep)
+        _check("db_down", g.db_down, _dense(og.db_down, wl.E, (wl.H,)), rep)
+    if og.dsh_gate_up is not None:
+        _check("dsh_gate_up", g.dsh_gate_up, og.dsh_gate_up, rep)
+        _check("dsh_down", g.dsh_down, og.dsh_down, rep)
+    if og.dsh_gate is not None:
+        _check("dsh_gate", g.dsh_gate, og.dsh_gate, rep)
+    print(f"[backward] {wl.name}: " + ", ".join(f"{k} {e / max(r_, 1e-30):.2e}" for k, (e, r_) in rep.items()),
+          flush=True)
+
+
+def test_backward_no_tokens_gives_zeros():
+    wl = Wl("bwd_t0", T=0, H=64, E=4, I=32, K=2, shared_I=32, shared_gated=True, router_bias_std=0.1)
+    c = Case(wl)
+    r = api.empty_routing(c.cfg, "cuda")
+    dout = torch.empty(0, wl.H, dtype=torch.bfloat16, device="cuda")
+    g = api.ffn_backward(c.cfg, c.x, c.lw, dout, r)
+    sync()
+    for f in ("dgate", "dw_gate_up", "dw_down", "drouter_bias", "dsh_gate_up", "dsh_down", "dsh_gate"):
+        assert not getattr(g, f).any(), f
+    assert g.dx.numel() == 0

@@ -72,6 +72,10 @@ int main(void) {
   F(moe_weights, w_gate_up) F(moe_weights, w_down) F(moe_weights, w_gate_up_scale)
   F(moe_weights, w_down_scale) F(moe_weights, b_gate_up) F(moe_weights, b_down)
   F(moe_weights, sh_gate_up) F(moe_weights, sh_down) F(moe_weights, sh_gate)
+  printf("moe_grads %zu\n", sizeof(moe_grads));
+  F(moe_grads, dx) F(moe_grads, dgate) F(moe_grads, drouter_bias) F(moe_grads, dw_gate_up)
+  F(moe_grads, dw_down) F(moe_grads, db_gate_up) F(moe_grads, db_down) F(moe_grads, dsh_gate_up)
+  F(moe_grads, dsh_down) F(moe_grads, dsh_gate)
   printf("enum %d %d %d %d %d %d %d %d %d %d %d\n", MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4,
          MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS, MOE_OK, MOE_ERR_INVALID,
          MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP);
@@ -90,6 +94,9 @@ int main(void) {
         assert int(got[f"moe_config.{name}"]) == getattr(_lib.MoeConfig, name).offset, name
     for name, _ in _lib.MoeWeights._fields_:
         assert int(got[f"moe_weights.{name}"]) == getattr(_lib.MoeWeights, name).offset, name
+    assert int(got["moe_grads"]) == ctypes.sizeof(_lib.MoeGrads)
+    for name, _ in _lib.MoeGrads._fields_:
+        assert int(got[f"moe_grads.{name}"]) == getattr(_lib.MoeGrads, name).offset, name
     enum_line = [l for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines()
                  if l.startswith("enum")][0]
     assert [int(v) for v in enum_line.split()[1:]] == [
@@ -214,3 +221,26 @@ def test_balance_refuses_bad_arguments(L):
     assert "expert_bias" in L.moe_last_error().decode()
     assert L.moe_balance_update(P(FAKE), P(FAKE), 8, f(math.nan), None, None) == -1
     assert L.moe_balance_update(P(FAKE), P(FAKE + 2), 8, f(0.1), None, None) == -1  # bias misaligned
+
+
+def test_backward_refuses_bad_arguments(L):
+    P = ctypes.c_void_p
+    c = cfg()
+    w = _lib.MoeWeights(gate_w=FAKE, w_gate_up=FAKE, w_down=FAKE)
+    g = _lib.MoeGrads(dx=FAKE, dgate=FAKE, dw_gate_up=FAKE, dw_down=FAKE)
+    ws_bytes = ctypes.c_size_t()
+    assert L.moe_backward_workspace_bytes(ctypes.byref(c), ctypes.byref(ws_bytes)) == 0 and ws_bytes.value > 0
+
+    def bw(cc=c, ww=w, gg=g, ws=FAKE + (2 << 30), nbytes=1 << 40):
+        return L.moe_ffn_backward(ctypes.byref(cc), P(FAKE), ctypes.byref(ww), P(FAKE), P(FAKE), P(FAKE),
+                                  ctypes.byref(gg) if gg is not None else None, P(ws), ctypes.c_size_t(nbytes), None)
+    assert bw(gg=None) == -1
+    assert bw(gg=_lib.MoeGrads(dx=FAKE, dgate=FAKE, dw_gate_up=FAKE)) == -1          # dw_down missing
+    assert bw(ww=_lib.MoeWeights(gate_w=FAKE, w_gate_up=FAKE, w_down=FAKE, router_bias=FAKE)) == -1
+    assert "drouter_bias" in L.moe_last_error().decode()
+    assert bw(nbytes=100) == -3
+    assert bw(ws=FAKE + (2 << 30) + 64) == -3
+    assert bw(cc=cfg(H=2880, I=2880, E=32, K=4, w_dtype="mxfp4")) == -2              # MXFP4 experts
+    cs = cfg(shared_I=2048, shared_gated=True)
+    assert bw(cc=cs, ww=_lib.MoeWeights(gate_w=FAKE, w_gate_up=FAKE, w_down=FAKE, sh_gate_up=FAKE,
+                                        sh_down=FAKE, sh_gate=FAKE)) == -1            # dsh_* missing
