@@ -22,17 +22,22 @@
 //   8. router: d weights -> d scores (renormalisation) -> d logits (score
 //      function) -> dgate = dl^T x, drouter_bias = sum_t dl, dx += dl gate
 //   9. dx = sum_k dx_rows (k order) + shared + router + gate terms
-// One generic grouped GEMM (64 x 64 f32 tiles staged in LDS, fixed k order per
-// output) serves every contraction through operand descriptors.
+// One generic grouped GEMM (TM x 64 f32 tiles staged in LDS, fixed k order per
+// output) serves every contraction through operand descriptors.  Expert
+// products with few rows per expert use 16-row tiles of one wave and split
+// the reduction into fixed chunks whose partial results are summed in chunk
+// order by a separate pass, so the result does not depend on scheduling.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kBT = 64;       // output tile (rows and columns)
-constexpr int kBK = 16;       // reduction slice
-constexpr int kGThreads = 256;
+constexpr int kBT = 64;       // output tile columns; rows of the large tile
+constexpr int kBK = 32;       // reduction slice
+constexpr int kSkinnyRows = 16;
 
 // expert ids index memory: keep them in range whatever the caller passed
 __device__ __forceinline__ int clamp_id(int e, int E) { return min(max(e, 0), E - 1); }
@@ -49,7 +54,7 @@ __device__ __forceinline__ float ld_elem(const void *p, int bf16, size_t i) {
 // group's matrix starts at group * gstride.
 struct GOp {
   const void *p;
-  int bf16, kmajor, token_rows;
+  int bf16, kmajor, token_rows, vec;  // vec: 8-element runs may be read as 16-byte vectors
   long ld, gstride;
   const int32_t *gather;
   const float *scale;
@@ -58,8 +63,10 @@ struct GOp {
 // C[m, n] = sum_k A(m, k) B(n, k) for each group.
 //   mode 0: one group of M x N x K.
 //   mode 1: group e has counts[e] rows (M), row base offsets[e]; the row tiles
-//           of all groups are listed by mtile_prefix (64-row tiles); C rows
-//           are the global rows.
+//           of all groups are listed by mtile_prefix (tiles of the kernel's
+//           row height); C rows are the global rows.  With ksplit > 1, chunk
+//           z of kchunk reduction steps writes its partial product to
+//           C + z * split_stride.
 //   mode 2: group e has counts[e] reduction steps (K), row base offsets[e];
 //           C of group e starts at e * cgstride.  Groups with no rows write 0.
 struct GGemm {
@@ -68,24 +75,58 @@ struct GGemm {
   long ldc, cgstride;
   int M, N, K, mode, E;
   const int32_t *counts, *offsets, *mtile_prefix;
+  int ksplit, kchunk;
+  long split_stride;
 };
 
-__device__ __forceinline__ float fetch(const GOp &o, int i, int k, int grp, int r0) {
+// Eight elements of an operand along its contiguous direction: (i, k..k+7)
+// when kmajor = 0, (i..i+7, k) when kmajor = 1.  `ni`, `nk` bound i and k;
+// elements outside are 0.  Whole in-bounds runs of a vectorisable operand
+// are read with 16-byte loads.
+__device__ __forceinline__ void fetch8(const GOp &o, int i, int k, int ni, int nk, int grp, int r0, float (&v)[8]) {
+  const bool rowok = o.kmajor ? k < nk : i < ni;
+  const int run0 = o.kmajor ? i : k, runn = o.kmajor ? ni : nk;
+  if (!rowok || run0 >= runn) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = 0.f;
+    return;
+  }
   const int rix = (o.token_rows ? r0 : 0) + (o.kmajor ? k : i);
-  const int other = o.kmajor ? i : k;
   const long src = o.gather ? o.gather[rix] : rix;
-  float v = ld_elem(o.p, o.bf16, (size_t)grp * o.gstride + (size_t)src * o.ld + other);
-  if (o.scale) v *= o.scale[rix];
-  return v;
+  const size_t base = (size_t)grp * o.gstride + (size_t)src * o.ld + run0;
+  const float sc = o.scale ? o.scale[rix] : 1.f;
+  if (o.vec && run0 + 8 <= runn) {
+    if (o.bf16) {
+      const u32x4_t u = load16(static_cast<const uint16_t *>(o.p) + base);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = bf16_to_f32(u[q] & 0xffffu) * sc;
+        v[2 * q + 1] = bf16_to_f32(u[q] >> 16) * sc;
+      }
+    } else {
+      const float *f = static_cast<const float *>(o.p) + base;
+      const float4 a = *reinterpret_cast<const float4 *>(f), b = *reinterpret_cast<const float4 *>(f + 4);
+      v[0] = a.x * sc; v[1] = a.y * sc; v[2] = a.z * sc; v[3] = a.w * sc;
+      v[4] = b.x * sc; v[5] = b.y * sc; v[6] = b.z * sc; v[7] = b.w * sc;
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = run0 + q < runn ? ld_elem(o.p, o.bf16, base + q) * sc : 0.f;
 }
 
-__global__ __launch_bounds__(kGThreads) void grouped_gemm_f32(GGemm g) {
-  __shared__ float As[kBK][kBT + 4], Bs[kBK][kBT + 4];
+// Tile TM x 64 with TM * 4 threads; each thread owns 4 x 4 outputs.
+template <int TM>
+__global__ __launch_bounds__(TM * 4) void grouped_gemm_f32(GGemm g) {
+  constexpr int NT = TM * 4;
+  constexpr int NB = kBT * kBK / 8 / NT;  // 8-element runs of B per thread and slice
+  static_assert(TM * kBK == NT * 8, "one 8-element run of A per thread and slice");
+  __shared__ float As[kBK][TM + 4], Bs[kBK][kBT + 4];
   const int tid = threadIdx.x;
   const int n0 = blockIdx.x * kBT;
   int grp = 0, m0, M, K, r0 = 0;
   if (g.mode == 0) {
-    m0 = blockIdx.y * kBT;
+    m0 = blockIdx.y * TM;
     M = g.M;
     K = g.K;
   } else if (g.mode == 1) {
@@ -98,33 +139,58 @@ __global__ __launch_bounds__(kGThreads) void grouped_gemm_f32(GGemm g) {
       else hi = mid;
     }
     grp = lo;
-    m0 = (q - g.mtile_prefix[lo]) * kBT;
+    m0 = (q - g.mtile_prefix[lo]) * TM;
     M = g.counts[lo];
     K = g.K;
     r0 = g.offsets[lo];
   } else {
-    const int mtiles = (g.M + kBT - 1) / kBT;
+    const int mtiles = (g.M + TM - 1) / TM;
     grp = blockIdx.y / mtiles;
-    m0 = (blockIdx.y - grp * mtiles) * kBT;
+    m0 = (blockIdx.y - grp * mtiles) * TM;
     M = g.M;
     K = g.counts[grp];
     r0 = g.offsets[grp];
   }
   if (m0 >= M || n0 >= g.N) return;  // whole workgroup leaves together
+  const int kbeg = blockIdx.z * g.kchunk;
+  const int kend = g.ksplit > 1 ? min(K, kbeg + g.kchunk) : K;
 
   const int tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += kBK) {
+  // Each thread reads 8-element runs per slice: (row, 8 k) of a row-major
+  // operand, (8 rows, k) of a k-major one.  The next slice's runs are loaded
+  // while the current one is multiplied.
+  constexpr int AR = TM / 8;  // k-major A: runs per k
+  const int ai = g.A.kmajor ? (tid % AR) * 8 : tid >> 2, ak = g.A.kmajor ? tid / AR : (tid & 3) * 8;
+  float ra[8], rb[NB][8];
+  auto load = [&](int k0) {
+    fetch8(g.A, m0 + ai, k0 + ak, M, kend, grp, r0, ra);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = tid + u * kGThreads;
-      // k-major operands: consecutive threads walk i (contiguous in memory)
-      const int ai = g.A.kmajor ? idx % kBT : idx / kBK, ak = g.A.kmajor ? idx / kBT : idx % kBK;
-      const int bi = g.B.kmajor ? idx % kBT : idx / kBK, bk = g.B.kmajor ? idx / kBT : idx % kBK;
-      As[ak][ai] = (m0 + ai < M && k0 + ak < K) ? fetch(g.A, m0 + ai, k0 + ak, grp, r0) : 0.f;
-      Bs[bk][bi] = (n0 + bi < g.N && k0 + bk < K) ? fetch(g.B, n0 + bi, k0 + bk, grp, r0) : 0.f;
+    for (int u = 0; u < NB; ++u) {
+      const int idx = tid + u * NT;
+      const int bi = g.B.kmajor ? (idx & 7) * 8 : idx >> 2, bk = g.B.kmajor ? idx >> 3 : (idx & 3) * 8;
+      fetch8(g.B, n0 + bi, k0 + bk, g.N, kend, grp, r0, rb[u]);
+    }
+  };
+  if (kbeg < kend) load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kBK) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (g.A.kmajor) As[ak][ai + q] = ra[q];
+      else As[ak + q][ai] = ra[q];
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int idx = tid + u * NT;
+      const int bi = g.B.kmajor ? (idx & 7) * 8 : idx >> 2, bk = g.B.kmajor ? idx >> 3 : (idx & 3) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (g.B.kmajor) Bs[bk][bi + q] = rb[u][q];
+        else Bs[bk + q][bi] = rb[u][q];
+      }
     }
     __syncthreads();
+    if (k0 + kBK < kend) load(k0 + kBK);
 #pragma unroll
     for (int kk = 0; kk < kBK; ++kk) {
       float a[4], b[4];
@@ -139,18 +205,53 @@ __global__ __launch_bounds__(kGThreads) void grouped_gemm_f32(GGemm g) {
     }
     __syncthreads();
   }
-  float *C = g.C + (g.mode == 2 ? (size_t)grp * g.cgstride : 0);
+  float *C = g.C + (g.mode == 2 ? (size_t)grp * g.cgstride : 0) + (size_t)blockIdx.z * g.split_stride;
+  const int nb = n0 + tx * 4;
+  const bool vec = g.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0 && nb + 4 <= g.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
     if (m >= M) continue;
-    const size_t row = g.mode == 1 ? (size_t)(r0 + m) : (size_t)m;
+    float *row = C + (g.mode == 1 ? (size_t)(r0 + m) : (size_t)m) * g.ldc;
+    if (vec) {
+      *reinterpret_cast<float4 *>(row + nb) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      if (n < g.N) C[row * g.ldc + n] = acc[i][j];
+      for (int j = 0; j < 4; ++j)
+        if (nb + j < g.N) row[nb + j] = acc[i][j];
     }
   }
+}
+
+// C[r, :] = sum over z in order of P[z][r, :], for the rows * n outputs
+__global__ void split_sum(const float *P, float *C, size_t n, long stride, int S) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = P[i];
+  for (int z = 1; z < S; ++z) s += P[(size_t)z * stride + i];
+  C[i] = s;
+}
+
+unsigned blocks(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+// Few rows per expert: the expert products are weight streams; 16-row tiles
+// waste less work than 64-row ones.
+bool skinny_rows(int rows, int E) { return rows <= 32 * E; }
+
+// Reduction chunks for a skinny expert product: enough (row tile, column
+// tile, chunk) workgroups to fill the chip (about 2048 waves, assuming the
+// rows spread over min(rows, E) experts), chunks of whole slices and at least
+// 256 steps, at most 16 chunks.
+struct SplitPlan {
+  int S, chunk;
+};
+SplitPlan split_plan(int rows, int E, int N, int K) {
+  const long tiles = (long)((N + kBT - 1) / kBT) * std::max(1, std::min(rows, E)) *
+                     ((std::max(1, rows / std::max(E, 1)) + kSkinnyRows - 1) / kSkinnyRows);
+  int S = (int)std::min<long>(16, std::max<long>(1, (2048 + tiles - 1) / tiles));
+  S = std::max(1, std::min(S, K / 256));
+  const int chunk = ((K + S - 1) / S + kBK - 1) / kBK * kBK;
+  return SplitPlan{chunk > 0 ? (K + chunk - 1) / chunk : 1, chunk};
 }
 
 // ---- 1. stable permutation --------------------------------------------------
@@ -180,7 +281,7 @@ __global__ __launch_bounds__(kPermThreads) void stable_permute(BackwardArgs a) {
       hist[w * a.E + tid] = total;
       total += c;
     }
-    tiles = (total + kBT - 1) / kBT;
+    tiles = (total + a.tile_rows - 1) / a.tile_rows;
   }
   int v0 = total, v1 = tiles;  // inclusive scans of (count, tiles) over experts
 #pragma unroll
@@ -419,19 +520,43 @@ __global__ void dx_combine(BackwardArgs a) {
   a.g.dx[i] = s;
 }
 
-hipError_t gemm(const GGemm &g, int grid_rows, hipStream_t st) {
+// Large tiles: grid_rows row tiles of kBT rows, no split.
+hipError_t gemm(GGemm g, int grid_rows, hipStream_t st) {
   if (grid_rows <= 0 || g.N <= 0) return hipSuccess;
+  g.ksplit = 1; g.kchunk = 0; g.split_stride = 0;
   const dim3 grid((g.N + kBT - 1) / kBT, grid_rows);
-  hipLaunchKernelGGL(grouped_gemm_f32, grid, dim3(kGThreads), 0, st, g);
+  hipLaunchKernelGGL(grouped_gemm_f32<kBT>, grid, dim3(kBT * 4), 0, st, g);
+  return hipGetLastError();
+}
+
+// Expert products (mode 1) over `rows` rows.  Skinny: 16-row tiles, the
+// reduction split as split_plan() says, the chunks' partial products in
+// `part` and summed in chunk order into C.
+hipError_t expert_gemm(GGemm g, int rows, bool skinny, float *part, hipStream_t st) {
+  if (!skinny) return gemm(g, (rows + kBT - 1) / kBT + g.E, st);
+  if (rows <= 0 || g.N <= 0) return hipSuccess;
+  const SplitPlan sp = split_plan(rows, g.E, g.N, g.K);
+  float *C = g.C;
+  g.ksplit = sp.S; g.kchunk = sp.chunk;
+  g.split_stride = (long)rows * g.ldc;
+  if (sp.S > 1) g.C = part;
+  const dim3 grid((g.N + kBT - 1) / kBT, (rows + kSkinnyRows - 1) / kSkinnyRows + g.E, sp.S);
+  hipLaunchKernelGGL(grouped_gemm_f32<kSkinnyRows>, grid, dim3(kSkinnyRows * 4), 0, st, g);
+  if (sp.S > 1) {
+    const size_t n = (size_t)rows * g.ldc;
+    hipLaunchKernelGGL(split_sum, dim3(blocks(n, 256)), dim3(256), 0, st, part, C, n, g.split_stride, sp.S);
+  }
   return hipGetLastError();
 }
 
 GOp op(const void *p, bool bf16, bool kmajor, long ld, long gstride = 0, bool token_rows = false,
        const int32_t *gather = nullptr, const float *scale = nullptr) {
-  return GOp{p, bf16 ? 1 : 0, kmajor ? 1 : 0, token_rows ? 1 : 0, ld, gstride, gather, scale};
+  // 16-byte runs need the base, every row start and every group start on a
+  // 16-byte boundary
+  const long per = bf16 ? 8 : 4;
+  const bool vec = (reinterpret_cast<uintptr_t>(p) & 15) == 0 && ld % per == 0 && gstride % per == 0;
+  return GOp{p, bf16 ? 1 : 0, kmajor ? 1 : 0, token_rows ? 1 : 0, vec ? 1 : 0, ld, gstride, gather, scale};
 }
-
-unsigned blocks(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
 }  // namespace
 
@@ -460,6 +585,15 @@ size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *
   b.dx_rows = reinterpret_cast<float *>(take(rows * H * 4));
   b.dweights = reinterpret_cast<float *>(take(rows * 4));
   b.dl = reinterpret_cast<float *>(take((size_t)T * E * 4));
+  if (skinny_rows((int)rows, E)) {
+    size_t part = 0;
+    const int nk[3][2] = {{2 * I, H}, {I, H}, {H, 2 * I}};  // pre, gd, dx_rows
+    for (const auto &q : nk) {
+      const SplitPlan sp = split_plan((int)rows, E, q[0], q[1]);
+      if (sp.S > 1) part = std::max(part, (size_t)sp.S * rows * q[0] * 4);
+    }
+    b.part = reinterpret_cast<float *>(take(part));
+  }
   b.dx_router = reinterpret_cast<float *>(take((size_t)T * H * 4));
   if (Is > 0) {
     b.pre_s = reinterpret_cast<float *>(take((size_t)T * 2 * Is * 4));
@@ -475,7 +609,7 @@ size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *
     // keep the caller's inputs, outputs and sizes; fill in the scratch
     BackwardArgs c = *a;
     c.row_slot = b.row_slot; c.row_token = b.row_token; c.row_expert = b.row_expert; c.slot_row = b.slot_row;
-    c.counts = b.counts; c.offsets = b.offsets; c.mtile_prefix = b.mtile_prefix;
+    c.counts = b.counts; c.offsets = b.offsets; c.mtile_prefix = b.mtile_prefix; c.part = b.part;
     c.slot_w = b.slot_w; c.row_w = b.row_w; c.pre = b.pre; c.hact = b.hact; c.gd = b.gd; c.dpre = b.dpre;
     c.dx_rows = b.dx_rows; c.dweights = b.dweights; c.dl = b.dl; c.dx_router = b.dx_router;
     c.pre_s = b.pre_s; c.hact_s = b.hact_s; c.gd_s = b.gd_s; c.dpre_s = b.dpre_s; c.dx_sh = b.dx_sh;
@@ -497,13 +631,15 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   const bool ab = a.act_bf16, wb = a.w_bf16;
   const float lim = a.limit;
 
+  const bool skinny = skinny_rows(rows, E);
   // 1-2. permutation and weights
-  hipLaunchKernelGGL(stable_permute, dim3(1), dim3(kPermThreads), (size_t)kPermWaves * E * 4, st, a);
+  BackwardArgs pa = a;
+  pa.tile_rows = skinny ? kSkinnyRows : kBT;
+  hipLaunchKernelGGL(stable_permute, dim3(1), dim3(kPermThreads), (size_t)kPermWaves * E * 4, st, pa);
   BW_TRY(hipGetLastError());
   hipLaunchKernelGGL(slot_weights, dim3(blocks(T, 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(rows_weight, dim3(blocks(rows, 256)), dim3(256), 0, st, a);
   BW_TRY(hipGetLastError());
-  const int mtile_bound = (rows + kBT - 1) / kBT + E;
 
   // 3. pre = x_rows Wgu^T, h = SwiGLU(pre + b)
   GGemm g{};
@@ -511,14 +647,14 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   g.A = op(a.x, ab, false, H, 0, true, a.row_token);
   g.B = op(a.w_gate_up, wb, false, H, (long)2 * I * H);
   g.C = a.pre; g.ldc = 2 * I; g.N = 2 * I; g.K = H;
-  BW_TRY(gemm(g, mtile_bound, st));
+  BW_TRY(expert_gemm(g, rows, skinny, a.part, st));
   hipLaunchKernelGGL(swiglu_fwd, dim3(blocks((size_t)rows * I, 256)), dim3(256), 0, st, a.pre, a.hact, a.row_expert,
                      a.b_gate_up, ab ? 1 : 0, rows, I, lim);
   // 4. gd = dout_rows Wd
   g.A = op(a.dout, ab, false, H, 0, true, a.row_token);
   g.B = op(a.w_down, wb, true, I, (long)H * I);
   g.C = a.gd; g.ldc = I; g.N = I; g.K = H;
-  BW_TRY(gemm(g, mtile_bound, st));
+  BW_TRY(expert_gemm(g, rows, skinny, a.part, st));
   // 5. dweights (slot order) and dpre
   hipLaunchKernelGGL(row_dots, dim3(blocks(rows, 4)), dim3(256), 0, st, a.gd, a.hact, rows, I, a.dout, ab ? 1 : 0,
                      a.row_token, a.row_expert, a.b_down, ab ? 1 : 0, H, a.dweights, a.row_slot);
@@ -529,7 +665,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   g.A = op(a.dpre, false, false, 2 * I, 0, true);
   g.B = op(a.w_gate_up, wb, true, H, (long)2 * I * H);
   g.C = a.dx_rows; g.ldc = H; g.N = H; g.K = 2 * I;
-  BW_TRY(gemm(g, mtile_bound, st));
+  BW_TRY(expert_gemm(g, rows, skinny, a.part, st));
   GGemm w{};
   w.mode = 2; w.E = E; w.counts = a.counts; w.offsets = a.offsets;
   w.A = op(a.dout, ab, true, H, 0, true, a.row_token, a.row_w);

@@ -36,6 +36,9 @@ CASES = [
     Wl("bwd_f32", T=64, H=256, E=8, I=128, K=2, act_dtype="f32", w_dtype="f32", shared_I=64),
     Wl("bwd_many_rows_t300", T=300, H=96, E=6, I=160, K=2, shared_I=32, shared_gated=True),
     Wl("bwd_t1", T=1, H=64, E=4, I=32, K=2),
+    # few rows per expert with a long reduction: split into chunks (a ragged
+    # last chunk and ragged column tiles)
+    Wl("bwd_split_ragged", T=40, H=992, E=4, I=224, K=2, shared_I=96, shared_gated=True),
     # the serving-size draft layer at its real shape (8 experts x 1536, top-1, H=4096)
     W.workload("qwen3_8b_moe_draft", T=72),
 ]
