@@ -36,8 +36,9 @@ namespace moe {
 namespace {
 
 constexpr int kBT = 64;       // output tile columns; rows of the large tile
-constexpr int kBK = 32;       // reduction slice
+constexpr int kBK = 32;       // reduction slice of the large tiles
 constexpr int kSkinnyRows = 16;
+constexpr int kSkinnyK = 32;  // reduction slice of the 16-row tiles
 
 // expert ids index memory: keep them in range whatever the caller passed
 __device__ __forceinline__ int clamp_id(int e, int E) { return min(max(e, 0), E - 1); }
@@ -54,7 +55,7 @@ __device__ __forceinline__ float ld_elem(const void *p, int bf16, size_t i) {
 // group's matrix starts at group * gstride.
 struct GOp {
   const void *p;
-  int bf16, kmajor, token_rows, vec;  // vec: 8-element runs may be read as 16-byte vectors
+  int bf16, kmajor, token_rows, vec;  // vec: the base and every row start are 16-byte aligned
   long ld, gstride;
   const int32_t *gather;
   const float *scale;
@@ -77,54 +78,209 @@ struct GGemm {
   const int32_t *counts, *offsets, *mtile_prefix;
   int ksplit, kchunk;
   long split_stride;
+  int vec;  // both operands read as whole 16-byte runs (vec_runs)
 };
 
-// Eight elements of an operand along its contiguous direction: (i, k..k+7)
-// when kmajor = 0, (i..i+7, k) when kmajor = 1.  `ni`, `nk` bound i and k;
-// elements outside are 0.  Whole in-bounds runs of a vectorisable operand
-// are read with 16-byte loads.
-__device__ __forceinline__ void fetch8(const GOp &o, int i, int k, int ni, int nk, int grp, int r0, float (&v)[8]) {
-  const bool rowok = o.kmajor ? k < nk : i < ni;
-  const int run0 = o.kmajor ? i : k, runn = o.kmajor ? ni : nk;
-  if (!rowok || run0 >= runn) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = 0.f;
-    return;
+// Reads of one operand in runs of eight elements along its contiguous
+// direction: (i, k..k+7) when KM = 0 (row-major), (i..i+7, k) when KM = 1
+// (k-major).  Elements outside [0, ni) x [0, nk) read as 0.  Every access is
+// made at a clamped in-bounds address and masked afterwards, so the code has
+// no branches around loads and the next slice's loads stay in flight while
+// the current one is multiplied.  VEC: every run is whole or empty (the run
+// dimension is a multiple of 8, rows start on 16-byte boundaries), and is
+// read with 16-byte loads.
+template <int KM, int BF, bool VEC>
+struct Runs {
+  // the "row" of a run is i (KM = 0, fixed per thread) or k (KM = 1)
+  size_t base;  // element offset of the row
+  float sc;
+  bool ok;
+  __device__ __forceinline__ void set_row(const GOp &o, int row, int nrow, int grp, int r0) {
+    ok = row < nrow;
+    const int rix = (o.token_rows ? r0 : 0) + (ok ? row : nrow - 1);
+    const long src = o.gather ? o.gather[rix] : rix;
+    base = (size_t)grp * o.gstride + (size_t)src * o.ld;
+    sc = o.scale ? o.scale[rix] : 1.f;
   }
-  const int rix = (o.token_rows ? r0 : 0) + (o.kmajor ? k : i);
-  const long src = o.gather ? o.gather[rix] : rix;
-  const size_t base = (size_t)grp * o.gstride + (size_t)src * o.ld + run0;
-  const float sc = o.scale ? o.scale[rix] : 1.f;
-  if (o.vec && run0 + 8 <= runn) {
-    if (o.bf16) {
-      const u32x4_t u = load16(static_cast<const uint16_t *>(o.p) + base);
+  // issue(): the loads of one run, kept raw; finish(): decode, scale and
+  // mask.  Between the two the loads stay in flight.
+  struct Raw {
+    uint32_t w[8];
+    uint32_t on;  // bit q: element q is in range
+    float sc;
+  };
+  __device__ __forceinline__ void issue(const GOp &o, int run0, int runn, Raw &r) const {
+    r.sc = sc;
+    if constexpr (VEC) {
+      const bool on = ok && run0 < runn;
+      r.on = on ? 0xffu : 0u;
+      const size_t at = base + (on ? run0 : runn - 8);
+      if constexpr (BF) {
+        const u32x4_t u = load16(static_cast<const uint16_t *>(o.p) + at);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = bf16_to_f32(u[q] & 0xffffu) * sc;
-        v[2 * q + 1] = bf16_to_f32(u[q] >> 16) * sc;
+        for (int q = 0; q < 4; ++q) r.w[q] = u[q];
+      } else {
+        const u32x4_t *f = reinterpret_cast<const u32x4_t *>(static_cast<const float *>(o.p) + at);
+        const u32x4_t a = f[0], b = f[1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          r.w[q] = a[q];
+          r.w[4 + q] = b[q];
+        }
       }
     } else {
-      const float *f = static_cast<const float *>(o.p) + base;
-      const float4 a = *reinterpret_cast<const float4 *>(f), b = *reinterpret_cast<const float4 *>(f + 4);
-      v[0] = a.x * sc; v[1] = a.y * sc; v[2] = a.z * sc; v[3] = a.w * sc;
-      v[4] = b.x * sc; v[5] = b.y * sc; v[6] = b.z * sc; v[7] = b.w * sc;
-    }
-    return;
-  }
+      r.on = 0;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) v[q] = run0 + q < runn ? ld_elem(o.p, o.bf16, base + q) * sc : 0.f;
+      for (int q = 0; q < 8; ++q) {
+        const bool on = ok && run0 + q < runn;
+        r.on |= on ? 1u << q : 0u;
+        r.w[q] = __float_as_uint(ld_elem(o.p, BF, base + (on ? run0 + q : 0)));
+      }
+    }
+  }
+  __device__ __forceinline__ static void finish(const Raw &r, float (&v)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float x;
+      if constexpr (VEC && BF) x = bf16_to_f32(q & 1 ? r.w[q >> 1] >> 16 : r.w[q >> 1] & 0xffffu);
+      else x = __uint_as_float(r.w[q]);
+      v[q] = (r.on >> q) & 1 ? x * r.sc : 0.f;
+    }
+  }
+};
+
+// Tile TM x 64 with TM * 4 threads, reduction slices of KB; each thread owns
+// 4 x 4 outputs.  AF and BF give each operand's format: bit 0 kmajor, bit 1
+// bf16.
+template <int TM, int KB, int AF, int BF, bool VEC>
+__device__ __forceinline__ void gemm_tile(const GGemm &g, int grp, int m0, int n0, int M, int K, int r0,
+                                          float (&As)[KB][TM + 4], float (&Bs)[KB][kBT + 4]) {
+  constexpr int AK = AF & 1, BK = BF & 1;
+  constexpr int NT = TM * 4;
+  constexpr int NA = TM * KB / 8 / NT, NB = kBT * KB / 8 / NT;  // 8-element runs per thread and slice
+  static_assert(NA * NT * 8 == TM * KB && NB * NT * 8 == kBT * KB, "whole runs per thread");
+  const int tid = threadIdx.x;
+  const int kbeg = blockIdx.z * g.kchunk;
+  const int kend = g.ksplit > 1 ? min(K, kbeg + g.kchunk) : K;
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  // Run idx (thread tid, then tid + NT, ...) of an operand with `rows` rows
+  // per tile: (row idx / (KB / 8), k (idx % (KB / 8)) * 8) when row-major,
+  // (row (idx % (rows / 8)) * 8, k idx / (rows / 8)) when k-major.
+  auto place = [](int idx, int rows, bool kmajor, int &i, int &k) {
+    i = kmajor ? (idx % (rows / 8)) * 8 : idx / (KB / 8);
+    k = kmajor ? idx / (rows / 8) : (idx % (KB / 8)) * 8;
+  };
+  int ai[NA], ak[NA], bi[NB], bk[NB];
+#pragma unroll
+  for (int u = 0; u < NA; ++u) place(tid + u * NT, TM, AK, ai[u], ak[u]);
+#pragma unroll
+  for (int u = 0; u < NB; ++u) place(tid + u * NT, kBT, BK, bi[u], bk[u]);
+  using RA = Runs<AK, (AF >> 1), VEC>;
+  using RB = Runs<BK, (BF >> 1), VEC>;
+  RA ra_[NA];
+  RB rb_[NB];
+  // rows of row-major operands do not move with k: resolve them once
+  if constexpr (!AK) {
+#pragma unroll
+    for (int u = 0; u < NA; ++u) ra_[u].set_row(g.A, m0 + ai[u], M, grp, r0);
+  }
+  if constexpr (!BK) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) rb_[u].set_row(g.B, n0 + bi[u], g.N, grp, r0);
+  }
+  typename RA::Raw ra[NA];
+  typename RB::Raw rb[NB];
+  auto load = [&](int k0) {
+    if constexpr (AK) {
+#pragma unroll
+      for (int u = 0; u < NA; ++u) ra_[u].set_row(g.A, k0 + ak[u], kend, grp, r0);
+    }
+    if constexpr (BK) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) rb_[u].set_row(g.B, k0 + bk[u], kend, grp, r0);
+    }
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      if constexpr (AK) ra_[u].issue(g.A, m0 + ai[u], M, ra[u]);
+      else ra_[u].issue(g.A, k0 + ak[u], kend, ra[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if constexpr (BK) rb_[u].issue(g.B, n0 + bi[u], g.N, rb[u]);
+      else rb_[u].issue(g.B, k0 + bk[u], kend, rb[u]);
+    }
+  };
+  auto step = [&](int kk) {
+    float a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+  };
+  if (kbeg < kend) load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += KB) {
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      float v[8];
+      RA::finish(ra[u], v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (AK) As[ak[u]][ai[u] + q] = v[q];
+        else As[ak[u] + q][ai[u]] = v[q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      float v[8];
+      RB::finish(rb[u], v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (BK) Bs[bk[u]][bi[u] + q] = v[q];
+        else Bs[bk[u] + q][bi[u]] = v[q];
+      }
+    }
+    __syncthreads();
+    if (k0 + KB < kend) load(k0 + KB);
+    if (k0 + KB <= kend) {
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) step(kk);
+    } else {
+      // the last, partial slice: the steps past the end would add 0 * 0
+      for (int kk = 0; kk < kend - k0; ++kk) step(kk);
+    }
+    __syncthreads();
+  }
+  float *C = g.C + (g.mode == 2 ? (size_t)grp * g.cgstride : 0) + (size_t)blockIdx.z * g.split_stride;
+  const int nb = n0 + tx * 4;
+  const bool vec = g.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0 && nb + 4 <= g.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+    float *row = C + (g.mode == 1 ? (size_t)(r0 + m) : (size_t)m) * g.ldc;
+    if (vec) {
+      const f32x4_t v{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+      // weight gradients are written once and not read back here: stream them
+      if (g.mode == 2) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(row + nb));
+      else *reinterpret_cast<f32x4_t *>(row + nb) = v;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (nb + j < g.N) row[nb + j] = acc[i][j];
+    }
+  }
 }
 
-// Tile TM x 64 with TM * 4 threads; each thread owns 4 x 4 outputs.
-template <int TM>
+template <int TM, int AF, int BF>
 __global__ __launch_bounds__(TM * 4) void grouped_gemm_f32(GGemm g) {
-  constexpr int NT = TM * 4;
-  constexpr int NB = kBT * kBK / 8 / NT;  // 8-element runs of B per thread and slice
-  static_assert(TM * kBK == NT * 8, "one 8-element run of A per thread and slice");
-  __shared__ float As[kBK][TM + 4], Bs[kBK][kBT + 4];
-  const int tid = threadIdx.x;
-  const int n0 = blockIdx.x * kBT;
+  constexpr int KB = TM == kSkinnyRows ? kSkinnyK : kBK;
   int grp = 0, m0, M, K, r0 = 0;
+  const int n0 = blockIdx.x * kBT;
   if (g.mode == 0) {
     m0 = blockIdx.y * TM;
     M = g.M;
@@ -152,75 +308,9 @@ __global__ __launch_bounds__(TM * 4) void grouped_gemm_f32(GGemm g) {
     r0 = g.offsets[grp];
   }
   if (m0 >= M || n0 >= g.N) return;  // whole workgroup leaves together
-  const int kbeg = blockIdx.z * g.kchunk;
-  const int kend = g.ksplit > 1 ? min(K, kbeg + g.kchunk) : K;
-
-  const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][4] = {};
-  // Each thread reads 8-element runs per slice: (row, 8 k) of a row-major
-  // operand, (8 rows, k) of a k-major one.  The next slice's runs are loaded
-  // while the current one is multiplied.
-  constexpr int AR = TM / 8;  // k-major A: runs per k
-  const int ai = g.A.kmajor ? (tid % AR) * 8 : tid >> 2, ak = g.A.kmajor ? tid / AR : (tid & 3) * 8;
-  float ra[8], rb[NB][8];
-  auto load = [&](int k0) {
-    fetch8(g.A, m0 + ai, k0 + ak, M, kend, grp, r0, ra);
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int idx = tid + u * NT;
-      const int bi = g.B.kmajor ? (idx & 7) * 8 : idx >> 2, bk = g.B.kmajor ? idx >> 3 : (idx & 3) * 8;
-      fetch8(g.B, n0 + bi, k0 + bk, g.N, kend, grp, r0, rb[u]);
-    }
-  };
-  if (kbeg < kend) load(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += kBK) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (g.A.kmajor) As[ak][ai + q] = ra[q];
-      else As[ak + q][ai] = ra[q];
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int idx = tid + u * NT;
-      const int bi = g.B.kmajor ? (idx & 7) * 8 : idx >> 2, bk = g.B.kmajor ? idx >> 3 : (idx & 3) * 8;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (g.B.kmajor) Bs[bk][bi + q] = rb[u][q];
-        else Bs[bk + q][bi] = rb[u][q];
-      }
-    }
-    __syncthreads();
-    if (k0 + kBK < kend) load(k0 + kBK);
-#pragma unroll
-    for (int kk = 0; kk < kBK; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-  float *C = g.C + (g.mode == 2 ? (size_t)grp * g.cgstride : 0) + (size_t)blockIdx.z * g.split_stride;
-  const int nb = n0 + tx * 4;
-  const bool vec = g.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0 && nb + 4 <= g.N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
-    if (m >= M) continue;
-    float *row = C + (g.mode == 1 ? (size_t)(r0 + m) : (size_t)m) * g.ldc;
-    if (vec) {
-      *reinterpret_cast<float4 *>(row + nb) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (nb + j < g.N) row[nb + j] = acc[i][j];
-    }
-  }
+  __shared__ float As[KB][TM + 4], Bs[KB][kBT + 4];
+  if (g.vec) gemm_tile<TM, KB, AF, BF, true>(g, grp, m0, n0, M, K, r0, As, Bs);
+  else gemm_tile<TM, KB, AF, BF, false>(g, grp, m0, n0, M, K, r0, As, Bs);
 }
 
 // C[r, :] = sum over z in order of P[z][r, :], for the rows * n outputs
@@ -239,7 +329,7 @@ unsigned blocks(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
 bool skinny_rows(int rows, int E) { return rows <= 32 * E; }
 
 // Reduction chunks for a skinny expert product: enough (row tile, column
-// tile, chunk) workgroups to fill the chip (about 2048 waves, assuming the
+// tile, chunk) workgroups to fill the chip (about 8192 waves, assuming the
 // rows spread over min(rows, E) experts), chunks of whole slices and at least
 // 256 steps, at most 16 chunks.
 struct SplitPlan {
@@ -248,9 +338,10 @@ struct SplitPlan {
 SplitPlan split_plan(int rows, int E, int N, int K) {
   const long tiles = (long)((N + kBT - 1) / kBT) * std::max(1, std::min(rows, E)) *
                      ((std::max(1, rows / std::max(E, 1)) + kSkinnyRows - 1) / kSkinnyRows);
-  int S = (int)std::min<long>(16, std::max<long>(1, (2048 + tiles - 1) / tiles));
+  constexpr long kWaves = 8192;
+  int S = (int)std::min<long>(16, std::max<long>(1, (kWaves + tiles - 1) / tiles));
   S = std::max(1, std::min(S, K / 256));
-  const int chunk = ((K + S - 1) / S + kBK - 1) / kBK * kBK;
+  const int chunk = ((K + S - 1) / S + kSkinnyK - 1) / kSkinnyK * kSkinnyK;
   return SplitPlan{chunk > 0 ? (K + chunk - 1) / chunk : 1, chunk};
 }
 
@@ -520,12 +611,44 @@ __global__ void dx_combine(BackwardArgs a) {
   a.g.dx[i] = s;
 }
 
+template <int TM, int AF>
+void launch_b(const GGemm &g, dim3 grid, hipStream_t st) {
+  switch (g.B.kmajor | g.B.bf16 << 1) {
+    case 0: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 0>), grid, dim3(TM * 4), 0, st, g); break;
+    case 1: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 1>), grid, dim3(TM * 4), 0, st, g); break;
+    case 2: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 2>), grid, dim3(TM * 4), 0, st, g); break;
+    default: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 3>), grid, dim3(TM * 4), 0, st, g); break;
+  }
+}
+template <int TM>
+void launch_gemm(const GGemm &g, dim3 grid, hipStream_t st) {
+  switch (g.A.kmajor | g.A.bf16 << 1) {
+    case 0: launch_b<TM, 0>(g, grid, st); break;
+    case 1: launch_b<TM, 1>(g, grid, st); break;
+    case 2: launch_b<TM, 2>(g, grid, st); break;
+    default: launch_b<TM, 3>(g, grid, st); break;
+  }
+}
+
+// Whole 16-byte runs: both operands aligned, and the dimension each one runs
+// along (k for a row-major operand, its rows for a k-major one) a multiple of
+// 8.  The reduction length of a K-grouped product is only known on the device:
+// there the operands must be k-major.
+bool vec_runs(const GGemm &g) {
+  auto one = [&](const GOp &o, int rows) {
+    const int run = o.kmajor ? rows : (g.mode == 2 ? 1 : g.K);
+    return o.vec && run % 8 == 0;
+  };
+  // rows of A in the row-grouped product vary by group
+  return one(g.A, g.mode == 1 ? 1 : g.M) && one(g.B, g.N) && (g.ksplit <= 1 || g.kchunk % 8 == 0);
+}
+
 // Large tiles: grid_rows row tiles of kBT rows, no split.
 hipError_t gemm(GGemm g, int grid_rows, hipStream_t st) {
   if (grid_rows <= 0 || g.N <= 0) return hipSuccess;
   g.ksplit = 1; g.kchunk = 0; g.split_stride = 0;
-  const dim3 grid((g.N + kBT - 1) / kBT, grid_rows);
-  hipLaunchKernelGGL(grouped_gemm_f32<kBT>, grid, dim3(kBT * 4), 0, st, g);
+  g.vec = vec_runs(g) ? 1 : 0;
+  launch_gemm<kBT>(g, dim3((g.N + kBT - 1) / kBT, grid_rows), st);
   return hipGetLastError();
 }
 
@@ -540,8 +663,9 @@ hipError_t expert_gemm(GGemm g, int rows, bool skinny, float *part, hipStream_t 
   g.ksplit = sp.S; g.kchunk = sp.chunk;
   g.split_stride = (long)rows * g.ldc;
   if (sp.S > 1) g.C = part;
+  g.vec = vec_runs(g) ? 1 : 0;
   const dim3 grid((g.N + kBT - 1) / kBT, (rows + kSkinnyRows - 1) / kSkinnyRows + g.E, sp.S);
-  hipLaunchKernelGGL(grouped_gemm_f32<kSkinnyRows>, grid, dim3(kSkinnyRows * 4), 0, st, g);
+  launch_gemm<kSkinnyRows>(g, grid, st);
   if (sp.S > 1) {
     const size_t n = (size_t)rows * g.ldc;
     hipLaunchKernelGGL(split_sum, dim3(blocks(n, 256)), dim3(256), 0, st, part, C, n, g.split_stride, sp.S);
