@@ -22,11 +22,13 @@
 //   8. router: d weights -> d scores (renormalisation) -> d logits (score
 //      function) -> dgate = dl^T x, drouter_bias = sum_t dl, dx += dl gate
 //   9. dx = sum_k dx_rows (k order) + shared + router + gate terms
-// One generic grouped GEMM (TM x 64 f32 tiles staged in LDS, fixed k order per
-// output) serves every contraction through operand descriptors.  Expert
-// products with few rows per expert use 16-row tiles of one wave and split
-// the reduction into fixed chunks whose partial results are summed in chunk
-// order by a separate pass, so the result does not depend on scheduling.
+// One generic grouped GEMM (64 x 64 f32 tiles staged in LDS, fixed k order
+// per output) serves every contraction through operand descriptors.  The
+// three expert products, when experts hold few rows, run instead on the fp32
+// matrix cores in 16-row tiles of one wave that read their operands straight
+// from memory, with the reduction split into fixed chunks whose partial
+// results a separate pass sums in chunk order, so the result does not depend
+// on scheduling.
 #include <algorithm>
 
 #include "kernels.hpp"
@@ -38,7 +40,6 @@ namespace {
 constexpr int kBT = 64;       // output tile columns; rows of the large tile
 constexpr int kBK = 32;       // reduction slice of the large tiles
 constexpr int kSkinnyRows = 16;
-constexpr int kSkinnyK = 32;  // reduction slice of the 16-row tiles
 
 // expert ids index memory: keep them in range whatever the caller passed
 __device__ __forceinline__ int clamp_id(int e, int E) { return min(max(e, 0), E - 1); }
@@ -278,7 +279,7 @@ __device__ __forceinline__ void gemm_tile(const GGemm &g, int grp, int m0, int n
 
 template <int TM, int AF, int BF>
 __global__ __launch_bounds__(TM * 4) void grouped_gemm_f32(GGemm g) {
-  constexpr int KB = TM == kSkinnyRows ? kSkinnyK : kBK;
+  constexpr int KB = kBK;
   int grp = 0, m0, M, K, r0 = 0;
   const int n0 = blockIdx.x * kBT;
   if (g.mode == 0) {
@@ -313,6 +314,206 @@ __global__ __launch_bounds__(TM * 4) void grouped_gemm_f32(GGemm g) {
   else gemm_tile<TM, KB, AF, BF, false>(g, grp, m0, n0, M, K, r0, As, Bs);
 }
 
+
+// ---- expert products with few rows on the fp32 matrix cores -----------------
+// v_mfma_f32_16x16x4f32 takes fp32 operands and sums fp32 products in fp32,
+// the arithmetic of the multiply-add path.  Lane l supplies A(l % 16, k = l /
+// 16) and B(k = l / 16, col l % 16) and holds C(4 (l / 16) + i, col l % 16).
+// Which reduction index and which output column a lane's operands stand for
+// is ours to choose, as long as A and B agree:
+//   B k-major: each lane loads 8 consecutive columns at one k (16 bytes);
+//   product q of a 4-deep substep gives output column n0 + 8 (l % 16) + q.
+//   A wave computes 16 rows x 128 columns in 32-deep steps (8 substeps).
+//   B row-major: each lane loads 16 consecutive k of one column (a whole
+//   32-byte run, so a 16-lane row group reads whole 128-byte lines); product
+//   r of column block c takes k = k0 + 16 (l / 16) + r and gives column
+//   n0 + 16 c + l % 16.  A wave computes 16 rows x 64 columns in 64-deep steps.
+// The next step's loads are in flight while the current step multiplies.
+// Loads go to clamped in-bounds addresses and are masked at use.
+template <int BKM>
+struct SkinnyShape {
+  static constexpr int cols = BKM ? 128 : 64, step = BKM ? 32 : 64;
+  static constexpr int nacc = 8 * (BKM ? 1 : 0) + 4 * (BKM ? 0 : 1);  // accumulators (16 x 16 each)
+};
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 16-byte load of element offset `at` of a bf16 (BF) or f32 array
+template <int BF>
+__device__ __forceinline__ u32x4_t ld16(const void *p, size_t at) {
+  return BF ? load16(static_cast<const uint16_t *>(p) + at) : load16(static_cast<const float *>(p) + at);
+}
+
+template <int BKM, int ABF, int BBF>
+struct SkinnyStage {
+  // k-major B: 8 substeps x 8 elements; A: 8 single elements (raw words)
+  // row-major B: 4 column blocks x 16 elements; A: 16 elements
+  static constexpr int nb = BKM ? 8 : 4, bw = (BKM ? 8 : 16) / (BBF ? 2 : 1);
+  static constexpr int aw = BKM ? 8 : 16 / (ABF ? 2 : 1);
+  uint32_t b[nb][bw];
+  uint32_t a[aw];
+  uint32_t bon, aon;  // in-range bits
+};
+
+template <int BKM, int ABF, int BBF>
+__global__ __launch_bounds__(64) void skinny_mfma_f32(GGemm g) {
+  using Sh = SkinnyShape<BKM>;
+  const int q = blockIdx.y;
+  if (q >= g.mtile_prefix[g.E]) return;
+  int lo = 0, hi = g.E;  // mtile_prefix[lo] <= q < mtile_prefix[lo + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.mtile_prefix[mid] <= q) lo = mid;
+    else hi = mid;
+  }
+  const int grp = lo, M = g.counts[grp], r0 = g.offsets[grp];
+  const int m0 = (q - g.mtile_prefix[grp]) * kSkinnyRows, n0 = blockIdx.x * Sh::cols;
+  if (m0 >= M || n0 >= g.N) return;
+  const int kbeg = blockIdx.z * g.kchunk;
+  const int kend = g.ksplit > 1 ? min(g.K, kbeg + g.kchunk) : g.K;
+  const int l = threadIdx.x, lr = l & 15, lk = l >> 4;
+  const GOp &A = g.A, &B = g.B;
+  // this lane's A row (token rows of the group, maybe gathered and scaled)
+  const bool aok = m0 + lr < M;
+  const int arix = (A.token_rows ? r0 : 0) + (aok ? m0 + lr : M - 1);
+  const size_t abase = (size_t)(A.gather ? A.gather[arix] : arix) * A.ld;
+  const float asc = A.scale ? A.scale[arix] : 1.f;
+  const size_t bgrp = (size_t)grp * B.gstride;
+  using Stage = SkinnyStage<BKM, ABF, BBF>;
+  auto load = [&](int k0, Stage &st) {
+    st.bon = st.aon = 0;
+    if constexpr (BKM) {
+      const int n = n0 + 8 * lr;
+      const bool nok = n < g.N;  // whole runs: n + 8 <= N
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int k = k0 + 4 * s + lk;
+        const bool on = nok && k < kend;
+        st.bon |= on ? 1u << s : 0u;
+        const size_t at = bgrp + (size_t)(on ? k : kend - 1) * B.ld + (on ? n : g.N - 8);
+        const u32x4_t w0 = ld16<BBF>(B.p, at);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.b[s][j] = w0[j];
+        if constexpr (!BBF) {
+          const u32x4_t w1 = ld16<BBF>(B.p, at + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st.b[s][4 + j] = w1[j];
+        }
+        const bool aon = aok && k < kend;
+        st.aon |= aon ? 1u << s : 0u;
+        const size_t ai = abase + (aon ? k : kend - 1);
+        st.a[s] = ABF ? static_cast<const uint16_t *>(A.p)[ai] : __float_as_uint(static_cast<const float *>(A.p)[ai]);
+      }
+    } else {
+      // two 8-runs per lane: k0 + 16 lk + 8 h, h = 0, 1 (whole runs: each in
+      // range or not)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = k0 + 16 * lk + 8 * h;
+        const bool kok = k < kend;
+        const size_t kc = kok ? k : kend - 8;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int n = n0 + 16 * c + lr;
+          const bool on = kok && n < g.N;
+          st.bon |= on ? 1u << (2 * c + h) : 0u;
+          const size_t at = bgrp + (size_t)(n < g.N ? n : g.N - 1) * B.ld + kc;
+          const u32x4_t w0 = ld16<BBF>(B.p, at);
+          constexpr int hw = BBF ? 4 : 8;  // words per 8-run
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st.b[c][h * hw + j] = w0[j];
+          if constexpr (!BBF) {
+            const u32x4_t w1 = ld16<BBF>(B.p, at + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st.b[c][h * hw + 4 + j] = w1[j];
+          }
+        }
+        const bool aon = aok && kok;
+        st.aon |= aon ? 1u << h : 0u;
+        const u32x4_t w0 = ld16<ABF>(A.p, abase + kc);
+        constexpr int hw = ABF ? 4 : 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.a[h * hw + j] = w0[j];
+        if constexpr (!ABF) {
+          const u32x4_t w1 = ld16<ABF>(A.p, abase + kc + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st.a[h * hw + 4 + j] = w1[j];
+        }
+      }
+    }
+  };
+  // element e of a run of raw words, widened
+  auto elem = [](const uint32_t *w, int e, auto bf) -> float {
+    if constexpr (decltype(bf)::value) return bf16_to_f32(e & 1 ? w[e >> 1] >> 16 : w[e >> 1] & 0xffffu);
+    else return __uint_as_float(w[e]);
+  };
+  using BBf = std::integral_constant<bool, BBF != 0>;
+  using ABf = std::integral_constant<bool, ABF != 0>;
+  f32x4_t acc[Sh::nacc];
+#pragma unroll
+  for (int c = 0; c < Sh::nacc; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Stage &st) {
+    if constexpr (BKM) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float a = (st.aon >> s) & 1 ? (ABF ? bf16_to_f32(st.a[s]) : __uint_as_float(st.a[s])) * asc : 0.f;
+        const bool bon = (st.bon >> s) & 1;
+#pragma unroll
+        for (int qn = 0; qn < 8; ++qn) acc[qn] = mfma_f32(a, bon ? elem(st.b[s], qn, BBf{}) : 0.f, acc[qn]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int h = r >> 3;
+        const float a = (st.aon >> h) & 1 ? elem(st.a, r, ABf{}) * asc : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c] = mfma_f32(a, (st.bon >> (2 * c + h)) & 1 ? elem(st.b[c], r, BBf{}) : 0.f, acc[c]);
+      }
+    }
+  };
+  if (kbeg < kend) {  // the clamped addresses need kend >= 8
+    // the scheduling barriers keep each step's loads ahead of the previous
+    // step's products (the scheduler would otherwise sink them next to their
+    // uses and leave nothing in flight)
+    constexpr int S = Sh::step;
+    Stage st0, st1;
+    load(kbeg, st0);
+    for (int k0 = kbeg; k0 < kend; k0 += 2 * S) {
+      load(k0 + S, st1);  // masked when past the end
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(k0 + 2 * S, st0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float *C = g.C + (size_t)blockIdx.z * g.split_stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 4 * lk + i;
+    if (m >= M) continue;
+    float *row = C + (size_t)(r0 + m) * g.ldc;
+    if constexpr (BKM) {
+      const int n = n0 + 8 * lr;
+      if (n < g.N) {
+        *reinterpret_cast<f32x4_t *>(row + n) = f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+        *reinterpret_cast<f32x4_t *>(row + n + 4) = f32x4_t{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int n = n0 + 16 * c + lr;
+        if (n < g.N) row[n] = acc[c][i];
+      }
+    }
+  }
+}
+
 // C[r, :] = sum over z in order of P[z][r, :], for the rows * n outputs
 __global__ void split_sum(const float *P, float *C, size_t n, long stride, int S) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -328,20 +529,20 @@ unsigned blocks(size_t n, int per) { return (unsigned)((n + per - 1) / per); }
 // waste less work than 64-row ones.
 bool skinny_rows(int rows, int E) { return rows <= 32 * E; }
 
-// Reduction chunks for a skinny expert product: enough (row tile, column
-// tile, chunk) workgroups to fill the chip (about 8192 waves, assuming the
-// rows spread over min(rows, E) experts), chunks of whole slices and at least
-// 256 steps, at most 16 chunks.
+// Reduction chunks for a skinny expert product whose waves cover `cols`
+// columns: enough (row tile, column tile, chunk) waves to keep the weight
+// stream busy (about kWaves, assuming the rows spread over min(rows, E)
+// experts), chunks of whole 64-deep steps and at least 128 deep, at most 32.
 struct SplitPlan {
   int S, chunk;
 };
-SplitPlan split_plan(int rows, int E, int N, int K) {
-  const long tiles = (long)((N + kBT - 1) / kBT) * std::max(1, std::min(rows, E)) *
+SplitPlan split_plan(int rows, int E, int N, int K, int cols) {
+  const long tiles = (long)((N + cols - 1) / cols) * std::max(1, std::min(rows, E)) *
                      ((std::max(1, rows / std::max(E, 1)) + kSkinnyRows - 1) / kSkinnyRows);
-  constexpr long kWaves = 8192;
-  int S = (int)std::min<long>(16, std::max<long>(1, (kWaves + tiles - 1) / tiles));
-  S = std::max(1, std::min(S, K / 256));
-  const int chunk = ((K + S - 1) / S + kSkinnyK - 1) / kSkinnyK * kSkinnyK;
+  constexpr long kWaves = 4096;
+  int S = (int)std::min<long>(32, std::max<long>(1, (kWaves + tiles - 1) / tiles));
+  S = std::max(1, std::min(S, K / 128));
+  const int chunk = ((K + S - 1) / S + 63) / 64 * 64;
   return SplitPlan{chunk > 0 ? (K + chunk - 1) / chunk : 1, chunk};
 }
 
@@ -652,20 +853,42 @@ hipError_t gemm(GGemm g, int grid_rows, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Expert products (mode 1) over `rows` rows.  Skinny: 16-row tiles, the
-// reduction split as split_plan() says, the chunks' partial products in
-// `part` and summed in chunk order into C.
+// The 16-row matrix-core kernel takes whole 16-byte runs, a row-major A, a
+// plain weight operand B (no gather, scale or token rows) and 16-byte aligned
+// output rows (the partial-product buffer is aligned).  Operands that pass
+// the entry point's checks always qualify.
+bool skinny_ok(GGemm g, const float *part) {
+  g.ksplit = 1;
+  return vec_runs(g) && !g.A.kmajor && !g.B.gather && !g.B.scale && !g.B.token_rows && g.ldc % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0;
+}
+
+// Expert products (mode 1) over `rows` rows.  Skinny: 16-row tiles on the
+// matrix cores, the reduction split as split_plan() says, the chunks' partial
+// products in `part` and summed in chunk order into C.  Otherwise 64-row
+// multiply-add tiles.
 hipError_t expert_gemm(GGemm g, int rows, bool skinny, float *part, hipStream_t st) {
   if (!skinny) return gemm(g, (rows + kBT - 1) / kBT + g.E, st);
   if (rows <= 0 || g.N <= 0) return hipSuccess;
-  const SplitPlan sp = split_plan(rows, g.E, g.N, g.K);
+  g.ksplit = 1;
+  g.vec = vec_runs(g) ? 1 : 0;  // 1: skinny_ok() held
+  const int cols = g.B.kmajor ? SkinnyShape<1>::cols : SkinnyShape<0>::cols;
+  const SplitPlan sp = split_plan(rows, g.E, g.N, g.K, cols);
   float *C = g.C;
   g.ksplit = sp.S; g.kchunk = sp.chunk;
   g.split_stride = (long)rows * g.ldc;
   if (sp.S > 1) g.C = part;
-  g.vec = vec_runs(g) ? 1 : 0;
-  const dim3 grid((g.N + kBT - 1) / kBT, (rows + kSkinnyRows - 1) / kSkinnyRows + g.E, sp.S);
-  launch_gemm<kSkinnyRows>(g, grid, st);
+  const dim3 grid((g.N + cols - 1) / cols, (rows + kSkinnyRows - 1) / kSkinnyRows + g.E, sp.S);
+  switch (g.B.kmajor | g.A.bf16 << 1 | g.B.bf16 << 2) {
+    case 0: hipLaunchKernelGGL((skinny_mfma_f32<0, 0, 0>), grid, dim3(64), 0, st, g); break;
+    case 1: hipLaunchKernelGGL((skinny_mfma_f32<1, 0, 0>), grid, dim3(64), 0, st, g); break;
+    case 2: hipLaunchKernelGGL((skinny_mfma_f32<0, 1, 0>), grid, dim3(64), 0, st, g); break;
+    case 3: hipLaunchKernelGGL((skinny_mfma_f32<1, 1, 0>), grid, dim3(64), 0, st, g); break;
+    case 4: hipLaunchKernelGGL((skinny_mfma_f32<0, 0, 1>), grid, dim3(64), 0, st, g); break;
+    case 5: hipLaunchKernelGGL((skinny_mfma_f32<1, 0, 1>), grid, dim3(64), 0, st, g); break;
+    case 6: hipLaunchKernelGGL((skinny_mfma_f32<0, 1, 1>), grid, dim3(64), 0, st, g); break;
+    default: hipLaunchKernelGGL((skinny_mfma_f32<1, 1, 1>), grid, dim3(64), 0, st, g); break;
+  }
   if (sp.S > 1) {
     const size_t n = (size_t)rows * g.ldc;
     hipLaunchKernelGGL(split_sum, dim3(blocks(n, 256)), dim3(256), 0, st, part, C, n, g.split_stride, sp.S);
@@ -712,9 +935,10 @@ size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *
   if (skinny_rows((int)rows, E)) {
     size_t part = 0;
     const int nk[3][2] = {{2 * I, H}, {I, H}, {H, 2 * I}};  // pre, gd, dx_rows
-    for (const auto &q : nk) {
-      const SplitPlan sp = split_plan((int)rows, E, q[0], q[1]);
-      if (sp.S > 1) part = std::max(part, (size_t)sp.S * rows * q[0] * 4);
+    const int cols[3] = {SkinnyShape<0>::cols, SkinnyShape<1>::cols, SkinnyShape<1>::cols};  // B layouts
+    for (int i = 0; i < 3; ++i) {
+      const SplitPlan sp = split_plan((int)rows, E, nk[i][0], nk[i][1], cols[i]);
+      if (sp.S > 1) part = std::max(part, (size_t)sp.S * rows * nk[i][0] * 4);
     }
     b.part = reinterpret_cast<float *>(take(part));
   }
@@ -755,7 +979,22 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   const bool ab = a.act_bf16, wb = a.w_bf16;
   const float lim = a.limit;
 
-  const bool skinny = skinny_rows(rows, E);
+  // the three expert products: pre = x_rows Wgu^T, gd = dout_rows Wd,
+  // dx_rows = dpre Wgu
+  GGemm g1{}, g2{}, g3{};
+  for (GGemm *g : {&g1, &g2, &g3}) {
+    g->mode = 1; g->E = E; g->counts = a.counts; g->offsets = a.offsets; g->mtile_prefix = a.mtile_prefix;
+  }
+  g1.A = op(a.x, ab, false, H, 0, true, a.row_token);
+  g1.B = op(a.w_gate_up, wb, false, H, (long)2 * I * H);
+  g1.C = a.pre; g1.ldc = 2 * I; g1.N = 2 * I; g1.K = H;
+  g2.A = op(a.dout, ab, false, H, 0, true, a.row_token);
+  g2.B = op(a.w_down, wb, true, I, (long)H * I);
+  g2.C = a.gd; g2.ldc = I; g2.N = I; g2.K = H;
+  g3.A = op(a.dpre, false, false, 2 * I, 0, true);
+  g3.B = op(a.w_gate_up, wb, true, H, (long)2 * I * H);
+  g3.C = a.dx_rows; g3.ldc = H; g3.N = H; g3.K = 2 * I;
+  const bool skinny = skinny_rows(rows, E) && skinny_ok(g1, a.part) && skinny_ok(g2, a.part) && skinny_ok(g3, a.part);
   // 1-2. permutation and weights
   BackwardArgs pa = a;
   pa.tile_rows = skinny ? kSkinnyRows : kBT;
@@ -766,19 +1005,11 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   BW_TRY(hipGetLastError());
 
   // 3. pre = x_rows Wgu^T, h = SwiGLU(pre + b)
-  GGemm g{};
-  g.mode = 1; g.E = E; g.counts = a.counts; g.offsets = a.offsets; g.mtile_prefix = a.mtile_prefix;
-  g.A = op(a.x, ab, false, H, 0, true, a.row_token);
-  g.B = op(a.w_gate_up, wb, false, H, (long)2 * I * H);
-  g.C = a.pre; g.ldc = 2 * I; g.N = 2 * I; g.K = H;
-  BW_TRY(expert_gemm(g, rows, skinny, a.part, st));
+  BW_TRY(expert_gemm(g1, rows, skinny, a.part, st));
   hipLaunchKernelGGL(swiglu_fwd, dim3(blocks((size_t)rows * I, 256)), dim3(256), 0, st, a.pre, a.hact, a.row_expert,
                      a.b_gate_up, ab ? 1 : 0, rows, I, lim);
   // 4. gd = dout_rows Wd
-  g.A = op(a.dout, ab, false, H, 0, true, a.row_token);
-  g.B = op(a.w_down, wb, true, I, (long)H * I);
-  g.C = a.gd; g.ldc = I; g.N = I; g.K = H;
-  BW_TRY(expert_gemm(g, rows, skinny, a.part, st));
+  BW_TRY(expert_gemm(g2, rows, skinny, a.part, st));
   // 5. dweights (slot order) and dpre
   hipLaunchKernelGGL(row_dots, dim3(blocks(rows, 4)), dim3(256), 0, st, a.gd, a.hact, rows, I, a.dout, ab ? 1 : 0,
                      a.row_token, a.row_expert, a.b_down, ab ? 1 : 0, H, a.dweights, a.row_slot);
@@ -786,10 +1017,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
                      rows, I, lim);
   BW_TRY(hipGetLastError());
   // 6. dx_rows = dpre Wgu; dWd = sum_r (w dout)^T h; dWgu = sum_r dpre^T x
-  g.A = op(a.dpre, false, false, 2 * I, 0, true);
-  g.B = op(a.w_gate_up, wb, true, H, (long)2 * I * H);
-  g.C = a.dx_rows; g.ldc = H; g.N = H; g.K = 2 * I;
-  BW_TRY(expert_gemm(g, rows, skinny, a.part, st));
+  BW_TRY(expert_gemm(g3, rows, skinny, a.part, st));
   GGemm w{};
   w.mode = 2; w.E = E; w.counts = a.counts; w.offsets = a.offsets;
   w.A = op(a.dout, ab, true, H, 0, true, a.row_token, a.row_w);
