@@ -47,12 +47,6 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t
                                                  c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float swiglu_b(float g, float u, float lim) {
-  g = fminf(g, lim);
-  u = fminf(fmaxf(u, -lim), lim);
-  return g / (1.f + expf(-g)) * u;
-}
-
 // 16-byte unit of (row, chunk) in a tile with CH chunks per row.  Rows
 // that share a 256-byte bank window get different chunk permutations.
 template <int CH>
@@ -149,14 +143,14 @@ __device__ __forceinline__ void big_epilogue(const ExpertGemmArgs &a, const BigC
           if (!cok || row >= c.nrows) continue;
           const float2 g = *reinterpret_cast<const float2 *>(Ew + r * EP + 2 * l32);
           const float2 u = *reinterpret_cast<const float2 *>(Ew + r * EP + 64 + 2 * l32);
-          const float h0 = swiglu_b(g.x + gb0, u.x + ub0, a.limit);
-          const float h1 = swiglu_b(g.y + gb1, u.y + ub1, a.limit);
-          const uint32_t hb0 = f32_to_bf16(h0), hb1 = f32_to_bf16(h1);
+          const float h0 = swiglu_fast(g.x + gb0, u.x + ub0, a.limit);
+          const float h1 = swiglu_fast(g.y + gb1, u.y + ub1, a.limit);
+          const uint32_t hb = pack_bf16x2(h0, h1);
           const size_t off = (size_t)(c.row0 + row) * a.N + col;
-          *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + off) = hb0 | (hb1 << 16);
-          if (a.out_lo)  // h = hi + lo to ~16 bits
+          *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + off) = hb;
+          if (a.out_lo)  // h = hi + lo to ~16 bits (h - hi is exact in f32)
             *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out_lo) + off) =
-                f32_to_bf16(h0 - bf16_to_f32(hb0)) | (f32_to_bf16(h1 - bf16_to_f32(hb1)) << 16);
+                pack_bf16x2(h0 - bf16_lo(hb), h1 - bf16_hi(hb));
         }
       } else {
         // every lane owns output columns 2 lane, 2 lane + 1 of each row
@@ -178,7 +172,7 @@ __device__ __forceinline__ void big_epilogue(const ExpertGemmArgs &a, const BigC
             const int slot = a.perm[c.row0 + row];
             const float wt = a.weights[slot];
             *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.direct_out) + (size_t)slot * a.N + col) =
-                f32_to_bf16(wt * y0) | (f32_to_bf16(wt * y1) << 16);
+                pack_bf16x2(wt * y0, wt * y1);
           } else {
             *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + (size_t)(c.row0 + row) * a.N + col) =
                 make_float2(y0, y1);
@@ -466,7 +460,9 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
   extern __shared__ u32x4_t smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave; saying so keeps every branch
+  // on it a scalar branch
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, lh = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
 
@@ -541,6 +537,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mf][nf][i] = 0.f;
 
+    // 32-row token fragments of this wave that hold rows of the group.  The
+    // main loop is compiled once per count (no guards inside it: a guard per
+    // MFMA group would break the interleaved schedule); a wave with fewer
+    // rows skips the empty fragments' reads and MFMAs but still issues its
+    // share of the tile's loads and meets every barrier.
     const int mf_count = min(MF, max(0, (c.nrows - c.m0 - wm * (TM / 2) + 31) / 32));
     auto wfrag = [&](int nf) {
       if constexpr (GATE_UP) return nf < 2 ? wn * 64 + nf * 32 : BN / 2 + wn * 64 + (nf - 2) * 32;
@@ -550,41 +551,39 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     // step t run while the fragments of step t + 1 are read from LDS.
     constexpr int NB = LO ? 2 * MF : MF;
     u32x4_t af[2][4], bf[2][NB];
-    auto fetch = [&](int set, int slot, int kk, auto full) {
-      constexpr bool FULL = decltype(full)::value;
+    auto fetch = [&](int set, int slot, int kk, auto cnt) {
+      constexpr int C = decltype(cnt)::value;
       const u32x4_t *Wt = smem + slot * SLOT, *Xt = Wt + WUN;
       const int ch = 2 * kk + lh;
+      if constexpr (C > 0) {
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
+        for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
+      }
 #pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        if (FULL || mf < mf_count) {
-          bf[set][mf] = Xt[unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
-          if constexpr (LO) bf[set][MF + mf] = Xt[XUN + unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
-        }
+      for (int mf = 0; mf < C; ++mf) {
+        bf[set][mf] = Xt[unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
+        if constexpr (LO) bf[set][MF + mf] = Xt[XUN + unit<CH>(wm * (TM / 2) + mf * 32 + l32, ch)];
       }
     };
-    auto mma = [&](int set, auto full) {
-      constexpr bool FULL = decltype(full)::value;
+    auto mma = [&](int set, auto cnt) {
+      constexpr int C = decltype(cnt)::value;
 #pragma unroll
-      for (int mf = 0; mf < MF; ++mf) {
-        if (FULL || mf < mf_count) {
+      for (int mf = 0; mf < C; ++mf) {
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[set][nf], bf[set][mf], acc[mf][nf]);
-          if constexpr (LO) {
+        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[set][nf], bf[set][mf], acc[mf][nf]);
+        if constexpr (LO) {
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[set][nf], bf[set][MF + mf], acc[mf][nf]);
-          }
+          for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma_32x32x16(af[set][nf], bf[set][MF + mf], acc[mf][nf]);
         }
       }
     };
     // fetch of the next step and MFMAs of this one in one scheduling region,
-    // the reads spread between the MFMAs (full tiles: no guards, so one region)
-    auto step = [&](int next_set, int next_slot, int next_kk, int set, auto full) {
-      constexpr bool FULL = decltype(full)::value;
-      fetch(next_set, next_slot, next_kk, full);
-      mma(set, full);
-      if constexpr (FULL) interleave_reads<4 + NB, MF * 4 * (LO ? 2 : 1)>();
+    // the reads spread between the MFMAs
+    auto step = [&](int next_set, int next_slot, int next_kk, int set, auto cnt) {
+      constexpr int C = decltype(cnt)::value;
+      fetch(next_set, next_slot, next_kk, cnt);
+      mma(set, cnt);
+      if constexpr (C > 0) interleave_reads<4 + (LO ? 2 * C : C), C * 4 * (LO ? 2 : 1)>();
     };
     // wait until the stage `after` stages before the newest issued one has landed
     auto wait_stage = [&](int after) {
@@ -603,27 +602,33 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     // for stage s + 1, one barrier follows (after it nobody reads slot s any
     // more), stage s + NSTAGE is issued into slot s, and the first fragments
     // of stage s + 1 are read while the second step's MFMAs run.
-    auto run = [&](auto full) {
+    auto run = [&](auto cnt) {
 #pragma unroll
       for (int d = 0; d < NSTAGE; ++d)
         if (d < nst) issue(d);
       wait_stage(min(NSTAGE - 1, nst - 1));
       barrier_lds();
-      fetch(0, 0, 0, full);
+      fetch(0, 0, 0, cnt);
       for (int s = 0; s < nst - 1; ++s) {
         const int slot = s % NSTAGE;
-        step(1, slot, 1, 0, full);
+        step(1, slot, 1, 0, cnt);
         wait_stage(min(NSTAGE - 2, nst - 2 - s));
         barrier_lds();
         if (s + NSTAGE < nst) issue(s + NSTAGE);
-        step(0, (s + 1) % NSTAGE, 0, 1, full);
+        step(0, (s + 1) % NSTAGE, 0, 1, cnt);
       }
-      fetch(1, (nst - 1) % NSTAGE, 1, full);
-      mma(0, full);
-      mma(1, full);
+      fetch(1, (nst - 1) % NSTAGE, 1, cnt);
+      mma(0, cnt);
+      mma(1, cnt);
     };
-    if (c.nrows - c.m0 >= TM) run(std::true_type{});
-    else run(std::false_type{});
+    static_assert(MF == 4 || MF == 2, "fragment counts");
+    if (mf_count == MF) run(std::integral_constant<int, MF>{});  // uniform per wave
+    else if (mf_count == 0) run(std::integral_constant<int, 0>{});
+    else if (mf_count == 1) run(std::integral_constant<int, 1>{});
+    else if constexpr (MF == 4) {
+      if (mf_count == 2) run(std::integral_constant<int, 2>{});
+      else run(std::integral_constant<int, 3>{});
+    }
     barrier_lds();  // every wave is done with the ring
     big_epilogue<GATE_UP, MF>(a, c, col0, acc, reinterpret_cast<float *>(smem));
     barrier_lds();  // the next tile's first loads overwrite the ring

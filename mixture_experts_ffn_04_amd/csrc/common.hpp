@@ -34,6 +34,27 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Two f32 -> one packed bf16 pair (a in the low half), round to nearest
+// even: the single gfx950 conversion instruction v_cvt_pk_bf16_f32; the
+// same bits as f32_to_bf16 on every non-NaN input.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// silu(min(g, L)) * clamp(u, -L, L) with the hardware's exp2 and reciprocal
+// approximations (about 1 ulp each, so a few ulp of f32 on the result: far
+// below the bf16 rounding that follows).  Large |g| behaves as the exact
+// form: exp2 overflows to inf and the reciprocal to 0 (silu -> -0), or
+// underflows to 0 (silu -> g).
+__device__ __forceinline__ float swiglu_fast(float g, float u, float lim) {
+  g = fminf(g, lim);
+  u = fminf(fmaxf(u, -lim), lim);
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.f + e) * u;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA: D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16), one wavefront.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, each with the 8
