@@ -27,6 +27,7 @@
 // codes per byte (low nibble first), one E8M0 scale per 32 inputs.  [MI143]
 // MoE-Infinity PR #143 "feat(dflash): converge DFlash spec-decode stack ->
 // dev (supersedes #140)": output-major MXFP4 blocks, per-expert biases.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -100,86 +101,137 @@ struct BigPlan {
 
 }  // namespace
 
-// Epilogue of a tile through LDS (the stage buffers must be free: at least
-// 4 x 32 x 132 floats).  The wave's sub-tile is MF fragment rows of 32
+// Epilogue of a gate_up tile.  The matching gate and up columns of a lane
+// sit in fragments nf and nf + 2 at the same register index, so SwiGLU runs
+// on the accumulators directly.  The packed bf16 h (hi, and lo when out_lo
+// is set) then passes once through LDS, where each wave turns its pieces of
+// 4 columns x 32 tokens into 16-byte row runs for the global stores.  Staged
+// token rows are 64 bf16 plus 16 bytes, so a half-wave's 8-byte writes (16
+// tokens, one column group) spread over 16 different 16-byte bank groups.
+constexpr int kEpiPitch = 144;  // bytes per staged token row
+template <int MF>
+constexpr size_t epi_gate_up_bytes() {
+  return (size_t)4 * 2 * MF * 32 * kEpiPitch;
+}
+
+template <int MF>
+__device__ __forceinline__ void big_epilogue_gate_up(const ExpertGemmArgs &a, const BigCoord &c, int col0,
+                                                     f32x16_t (&acc)[MF][4], char *lds) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int wcol0 = col0 + wn * 64;  // first h column of the wave
+  char *hi_s = lds + (size_t)wave * 2 * MF * 32 * kEpiPitch;
+  char *lo_s = hi_s + MF * 32 * kEpiPitch;
+  const bool want_lo = a.out_lo != nullptr;
+  const uint16_t *bp = a.bias ? static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride : nullptr;
+  // lane: token l32 of each fragment, columns 32 p + 8 j + 4 lh + q
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cl = 32 * p + 8 * j + 4 * lh;  // column within the wave's 64
+        float gb[4] = {0.f, 0.f, 0.f, 0.f}, ub[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bp && wcol0 + cl < a.N) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gb[q] = bf16_to_f32(bp[wcol0 + cl + q]);
+            ub[q] = bf16_to_f32(bp[a.N + wcol0 + cl + q]);
+          }
+        }
+        float h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          h[q] = swiglu_fast(acc[mf][p][4 * j + q] + gb[q], acc[mf][p + 2][4 * j + q] + ub[q], a.limit);
+        const uint32_t h01 = pack_bf16x2(h[0], h[1]), h23 = pack_bf16x2(h[2], h[3]);
+        const int off = (mf * 32 + l32) * kEpiPitch + cl * 2;
+        *reinterpret_cast<uint2 *>(hi_s + off) = make_uint2(h01, h23);
+        if (want_lo)  // h = hi + lo to ~16 bits (h - hi is exact in f32)
+          *reinterpret_cast<uint2 *>(lo_s + off) =
+              make_uint2(pack_bf16x2(h[0] - bf16_lo(h01), h[1] - bf16_hi(h01)),
+                         pack_bf16x2(h[2] - bf16_lo(h23), h[3] - bf16_hi(h23)));
+      }
+    }
+  }
+  // a wave reads back only what it wrote (LDS operations of a wave complete
+  // in order): 8 lanes per token row, 16 bytes (8 columns) each
+  const int ch = lane & 7;
+  const bool cok = wcol0 + 8 * ch < a.N;  // N is a multiple of 32
+  const int trow0 = c.m0 + wm * (MF * 32);
+#pragma unroll 2
+  for (int i = 0; i < MF * 4; ++i) {
+    const int r = i * 8 + (lane >> 3);
+    const u32x4_t vh = *reinterpret_cast<const u32x4_t *>(hi_s + r * kEpiPitch + ch * 16);
+    u32x4_t vl = {0u, 0u, 0u, 0u};
+    if (want_lo) vl = *reinterpret_cast<const u32x4_t *>(lo_s + r * kEpiPitch + ch * 16);
+    const int row = trow0 + r;
+    if (cok && row < c.nrows) {
+      const size_t off = (size_t)(c.row0 + row) * a.N + wcol0 + 8 * ch;
+      *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.out) + off) = vh;
+      if (want_lo) *reinterpret_cast<u32x4_t *>(static_cast<uint16_t *>(a.out_lo) + off) = vl;
+    }
+  }
+}
+
+// Epilogue of a down tile through LDS (the stage buffers must be free: at
+// least 4 x 32 x 132 floats).  The wave's sub-tile is MF fragment rows of 32
 // tokens x 128 columns.  Each wave writes one fragment row of its sub-tile
-// to its own padded region, then reads it back one token
-// row at a time, so its stores cover contiguous column runs of one row.
-// gate_up: SwiGLU (+ bias) -> h (bf16 hi, and lo when out_lo is set);
-// down: (+ bias) -> y f32, or out[token] = weight * y with direct_out.
-template <bool GATE_UP, int MF = 4>
-__device__ __forceinline__ void big_epilogue(const ExpertGemmArgs &a, const BigCoord &c, int col0,
-                                             f32x16_t (&acc)[MF][4], float *lds) {
+// to its own padded region, then reads it back one token row at a time, so
+// its stores cover contiguous column runs of one row: (+ bias) -> y f32, or
+// out[token] = weight * y with direct_out.
+template <int MF>
+__device__ __forceinline__ void big_epilogue_down(const ExpertGemmArgs &a, const BigCoord &c, int col0,
+                                                  f32x16_t (&acc)[MF][4], float *lds) {
   constexpr int EP = 128 + 4;  // padded row (floats): the 16 rows of a float4 write hit distinct banks
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
   float *Ew = lds + wave * 32 * EP;
-    const int ccol0 = GATE_UP ? col0 + wn * 64 : col0 + wn * 128;  // first output column of the wave
+  const int ccol0 = col0 + wn * 128;  // first output column of the wave
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
+  for (int mf = 0; mf < MF; ++mf) {
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf)
+    for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4 *>(Ew + l32 * EP + nf * 32 + 8 * j + 4 * lh) =
-              make_float4(acc[mf][nf][4 * j], acc[mf][nf][4 * j + 1], acc[mf][nf][4 * j + 2], acc[mf][nf][4 * j + 3]);
-      const int rbase = c.m0 + wm * MF * 32 + mf * 32;  // token row (in the group) of fragment row 0
-      if constexpr (GATE_UP) {
-        // lanes 0..31 take even rows, 32..63 odd rows; lane l32 owns h columns 2 l32, 2 l32 + 1
-        const int col = ccol0 + 2 * l32;
-        const bool cok = col < a.N;
-        float gb0 = 0.f, gb1 = 0.f, ub0 = 0.f, ub1 = 0.f;
-        if (a.bias && cok) {
-          const uint16_t *bp = static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride;
-          gb0 = bf16_to_f32(bp[col]);
-          gb1 = bf16_to_f32(bp[col + 1]);
-          ub0 = bf16_to_f32(bp[a.N + col]);
-          ub1 = bf16_to_f32(bp[a.N + col + 1]);
-        }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(Ew + l32 * EP + nf * 32 + 8 * j + 4 * lh) =
+            make_float4(acc[mf][nf][4 * j], acc[mf][nf][4 * j + 1], acc[mf][nf][4 * j + 2], acc[mf][nf][4 * j + 3]);
+    const int rbase = c.m0 + wm * MF * 32 + mf * 32;  // token row (in the group) of fragment row 0
+    // every lane owns output columns 2 lane, 2 lane + 1 of each row
+    const int col = ccol0 + 2 * lane;
+    const bool cok = col < a.N;
+    float b0 = 0.f, b1 = 0.f;
+    if (a.bias && cok) {
+      const uint16_t *bp = static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride;
+      b0 = bf16_to_f32(bp[col]);
+      b1 = bf16_to_f32(bp[col + 1]);
+    }
 #pragma unroll 4
-        for (int r = lh; r < 32; r += 2) {
-          const int row = rbase + r;
-          if (!cok || row >= c.nrows) continue;
-          const float2 g = *reinterpret_cast<const float2 *>(Ew + r * EP + 2 * l32);
-          const float2 u = *reinterpret_cast<const float2 *>(Ew + r * EP + 64 + 2 * l32);
-          const float h0 = swiglu_fast(g.x + gb0, u.x + ub0, a.limit);
-          const float h1 = swiglu_fast(g.y + gb1, u.y + ub1, a.limit);
-          const uint32_t hb = pack_bf16x2(h0, h1);
-          const size_t off = (size_t)(c.row0 + row) * a.N + col;
-          *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out) + off) = hb;
-          if (a.out_lo)  // h = hi + lo to ~16 bits (h - hi is exact in f32)
-            *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.out_lo) + off) =
-                pack_bf16x2(h0 - bf16_lo(hb), h1 - bf16_hi(hb));
-        }
+    for (int r = 0; r < 32; ++r) {
+      const int row = rbase + r;
+      if (!cok || row >= c.nrows) continue;
+      const float2 v = *reinterpret_cast<const float2 *>(Ew + r * EP + 2 * lane);
+      const float y0 = v.x + b0, y1 = v.y + b1;
+      if (a.direct_out) {  // one expert per token: out = weight * y
+        const int slot = a.perm[c.row0 + row];
+        const float wt = a.weights[slot];
+        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.direct_out) + (size_t)slot * a.N + col) =
+            pack_bf16x2(wt * y0, wt * y1);
       } else {
-        // every lane owns output columns 2 lane, 2 lane + 1 of each row
-        const int col = ccol0 + 2 * lane;
-        const bool cok = col < a.N;
-        float b0 = 0.f, b1 = 0.f;
-        if (a.bias && cok) {
-          const uint16_t *bp = static_cast<const uint16_t *>(a.bias) + (size_t)c.g * a.bias_stride;
-          b0 = bf16_to_f32(bp[col]);
-          b1 = bf16_to_f32(bp[col + 1]);
-        }
-#pragma unroll 4
-        for (int r = 0; r < 32; ++r) {
-          const int row = rbase + r;
-          if (!cok || row >= c.nrows) continue;
-          const float2 v = *reinterpret_cast<const float2 *>(Ew + r * EP + 2 * lane);
-          const float y0 = v.x + b0, y1 = v.y + b1;
-          if (a.direct_out) {  // one expert per token: out = weight * y
-            const int slot = a.perm[c.row0 + row];
-            const float wt = a.weights[slot];
-            *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.direct_out) + (size_t)slot * a.N + col) =
-                pack_bf16x2(wt * y0, wt * y1);
-          } else {
-            *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + (size_t)(c.row0 + row) * a.N + col) =
-                make_float2(y0, y1);
-          }
-        }
+        *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + (size_t)(c.row0 + row) * a.N + col) =
+            make_float2(y0, y1);
       }
     }
+  }
+}
+
+template <bool GATE_UP, int MF = 4>
+__device__ __forceinline__ void big_epilogue(const ExpertGemmArgs &a, const BigCoord &c, int col0,
+                                             f32x16_t (&acc)[MF][4], void *lds) {
+  if constexpr (GATE_UP) big_epilogue_gate_up<MF>(a, c, col0, acc, static_cast<char *>(lds));
+  else big_epilogue_down<MF>(a, c, col0, acc, static_cast<float *>(lds));
 }
 
 template <bool GATE_UP, int WF, bool GATHER, bool LO>
@@ -192,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile(TiledGemmArgs ta) 
   extern __shared__ u32x4_t smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int l32 = lane & 31, lh = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
 
@@ -384,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile(TiledGemmArgs ta) 
     if (c.nrows - c.m0 >= BM) run(std::true_type{});
     else run(std::false_type{});
 
-    big_epilogue<GATE_UP>(a, c, col0, acc, reinterpret_cast<float *>(smem));
+    big_epilogue<GATE_UP>(a, c, col0, acc, smem);
     __syncthreads();  // the next tile's first slice overwrites buffer 0
   }
 }
@@ -456,6 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
   using P = DmaPlan<LO, TM>;
   constexpr int CH = P::CH, WUN = P::WUN, XUN = P::XUN, SLOT = P::SLOT, NSTAGE = P::NSTAGE, OPS = P::OPS;
   constexpr int XI = P::XI, MF = TM / 64;  // wave sub-tile: MF fragments of 32 tokens x 128 columns
+  static_assert(!GATE_UP || P::LDS_BYTES >= epi_gate_up_bytes<MF>(), "gate_up epilogue staging fits the ring");
   const ExpertGemmArgs &a = ta.g;
   extern __shared__ u32x4_t smem[];
 
@@ -630,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
       else run(std::integral_constant<int, 3>{});
     }
     barrier_lds();  // every wave is done with the ring
-    big_epilogue<GATE_UP, MF>(a, c, col0, acc, reinterpret_cast<float *>(smem));
+    big_epilogue<GATE_UP, MF>(a, c, col0, acc, smem);
     barrier_lds();  // the next tile's first loads overwrite the ring
   }
 }
@@ -655,7 +708,8 @@ hipError_t launch_big_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st
     return launch_dma_t<GATE_UP, GATHER, LO>(t, tiles_bound, st);
   } else {  // MXFP4: codes are decoded on their way into LDS (register-staged)
     auto kern = expert_bigtile<GATE_UP, WF, GATHER, LO>;
-    constexpr size_t lds = BigPlan<LO>::LDS_BYTES;
+    constexpr size_t lds = std::max(BigPlan<LO>::LDS_BYTES, GATE_UP ? epi_gate_up_bytes<4>() : (size_t)0);
+    static_assert(lds <= 160 * 1024, "LDS");
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
