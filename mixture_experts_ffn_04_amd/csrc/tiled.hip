@@ -33,12 +33,6 @@ constexpr int TBK = 32;           // reduction slice
 constexpr int TLD = TBK + 8;      // padded LDS row (80 B): conflict-free 16 B fragment reads
 constexpr int TTHREADS = 256;
 
-__device__ __forceinline__ float swiglu_t(float g, float u, float lim) {
-  g = fminf(g, lim);
-  u = fminf(fmaxf(u, -lim), lim);
-  return g / (1.f + expf(-g)) * u;
-}
-
 struct TileCoord {
   int g, nrows, row0;  // group
   int m0, n0;          // first token row (in the group) and first column
@@ -290,19 +284,16 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
               ub[q] = bf16_to_f32(b[a.N + col + q]);
             }
           }
-          uint32_t hb[4], lb[4];
+          float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float hv = swiglu_t(acc[cf][tf][q] + gb[q], acc[cf + 4][tf][q] + ub[q], a.limit);
-            hb[q] = f32_to_bf16(hv);
-            lb[q] = f32_to_bf16(hv - bf16_to_f32(hb[q]));
-          }
+          for (int q = 0; q < 4; ++q) hv[q] = swiglu_fast(acc[cf][tf][q] + gb[q], acc[cf + 4][tf][q] + ub[q], a.limit);
+          const uint32_t h01 = pack_bf16x2(hv[0], hv[1]), h23 = pack_bf16x2(hv[2], hv[3]);
           const size_t off = (size_t)(c.row0 + row) * a.N + col;
-          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) =
-              make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-          if (a.out_lo)
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) = make_uint2(h01, h23);
+          if (a.out_lo)  // h = hi + lo to ~16 bits (h - hi is exact in f32)
             *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out_lo) + off) =
-                make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+                make_uint2(pack_bf16x2(hv[0] - bf16_lo(h01), hv[1] - bf16_hi(h01)),
+                           pack_bf16x2(hv[2] - bf16_lo(h23), hv[3] - bf16_hi(h23)));
         }
       } else {
         int slot = 0;
@@ -325,8 +316,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
           }
           if (a.direct_out) {
             *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.direct_out) + (size_t)slot * a.N + col) =
-                make_uint2(f32_to_bf16(wt * v.x) | (f32_to_bf16(wt * v.y) << 16),
-                           f32_to_bf16(wt * v.z) | (f32_to_bf16(wt * v.w) << 16));
+                make_uint2(pack_bf16x2(wt * v.x, wt * v.y), pack_bf16x2(wt * v.z, wt * v.w));
           } else {
             *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + (size_t)(c.row0 + row) * a.N + col) = v;
           }
