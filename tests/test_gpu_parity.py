@@ -71,6 +71,11 @@ SMALL = [
     Wl("big_top2_t800", T=800, H=256, E=4, I=128, K=2, shared_I=64, shared_gated=True),
     Wl("big_bf16_direct_t1030", T=1030, H=352, E=4, I=288, K=1),
     Wl("big_mxfp4_top2_t1100", T=1100, H=256, E=8, I=160, K=2, w_dtype="mxfp4"),
+    # partial row tiles whose 32-row token fragments cover every count (0 to
+    # 4) in both token halves of the bf16 big-tile kernel (its main loop is
+    # compiled once per count): 305-342 and 393-466 rows per expert
+    Wl("big_bf16_fragments_t1300", T=1300, H=256, E=4, I=128, K=1),
+    Wl("big_bf16_fragments_t1700", T=1700, H=256, E=4, I=128, K=1),
     # tiled router logits (>= 256 tokens, >= 64 columns): partial column and
     # token tiles, a 96-element hidden tail, the shared-gate column
     Wl("router_tiled_t300", T=300, H=352, E=96, I=64, K=6, shared_I=64, shared_gated=True,
