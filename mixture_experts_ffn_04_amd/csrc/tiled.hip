@@ -20,6 +20,8 @@
 // (stacked on #1035)" (clamped SwiGLU; stacked gate_up_proj; FP4 experts two
 // codes per byte, low nibble first, E8M0 scale per 32 inputs) and [MI143]
 // MoE-Infinity PR #143 (output-major MXFP4 blocks, expert biases).
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "tile.hpp"
 
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
   uint16_t *Xl = Ws + 2 * TBN * TLD;           // [2][TBM][TLD] low halves of h (down, LO)
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int lr = lane & 15, lg = lane >> 4;
   const int wm = wave & 1, wn = wave >> 1;
 
@@ -223,46 +225,63 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
       else return wn * 128 + cf * 16;
     };
 
-    auto compute = [&](int buf) {
+    // 16-row token fragments of this wave that hold rows of the group
+    // (uniform); the loop is compiled once per count, so a thin last row
+    // tile skips the empty fragments' reads and MFMAs with no guard inside
+    // the loop.  Loads, LDS stores and barriers are the same for every wave.
+    const int tf_count = min(4, max(0, (c.nrows - c.m0 - wm * 64 + 15) / 16));
+    auto compute = [&](int buf, auto tfc_c) {
+      constexpr int TFC = decltype(tfc_c)::value;
       const uint16_t *xs = Xs + buf * TBM * TLD;
       const uint16_t *ws = Ws + buf * TBN * TLD;
 #pragma unroll
       for (int kk = 0; kk < TBK / 32; ++kk) {
         u32x4_t xf[4], wf[8];
 #pragma unroll
-        for (int tf = 0; tf < 4; ++tf)
+        for (int tf = 0; tf < TFC; ++tf)
           xf[tf] = *reinterpret_cast<const u32x4_t *>(xs + (wm * 64 + tf * 16 + lr) * TLD + kk * 32 + lg * 8);
+        if constexpr (TFC > 0) {
+#pragma unroll
+          for (int cf = 0; cf < 8; ++cf)
+            wf[cf] = *reinterpret_cast<const u32x4_t *>(ws + (wfrag_row(cf) + lr) * TLD + kk * 32 + lg * 8);
+        }
 #pragma unroll
         for (int cf = 0; cf < 8; ++cf)
-          wf[cf] = *reinterpret_cast<const u32x4_t *>(ws + (wfrag_row(cf) + lr) * TLD + kk * 32 + lg * 8);
 #pragma unroll
-        for (int cf = 0; cf < 8; ++cf)
-#pragma unroll
-          for (int tf = 0; tf < 4; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
+          for (int tf = 0; tf < TFC; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
         if constexpr (LO) {  // same weight fragments times the low halves of h
           const uint16_t *xl = Xl + buf * TBM * TLD;
 #pragma unroll
-          for (int tf = 0; tf < 4; ++tf)
+          for (int tf = 0; tf < TFC; ++tf)
             xf[tf] = *reinterpret_cast<const u32x4_t *>(xl + (wm * 64 + tf * 16 + lr) * TLD + kk * 32 + lg * 8);
 #pragma unroll
           for (int cf = 0; cf < 8; ++cf)
 #pragma unroll
-            for (int tf = 0; tf < 4; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
+            for (int tf = 0; tf < TFC; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
         }
       }
     };
 
     // double-buffered LDS: the next slice's global loads are in flight while
     // the current slice is multiplied, then stored to the other buffer
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-      const int buf = ks & 1;
-      if (ks + 1 < nks) gload(ks + 1);
-      compute(buf);
-      if (ks + 1 < nks) lstore(buf ^ 1);
+    auto run = [&](auto tfc_c) {
+      gload(0);
+      lstore(0);
       __syncthreads();
+      for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nks) gload(ks + 1);
+        compute(buf, tfc_c);
+        if (ks + 1 < nks) lstore(buf ^ 1);
+        __syncthreads();
+      }
+    };
+    switch (tf_count) {
+      case 4: run(std::integral_constant<int, 4>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      default: run(std::integral_constant<int, 0>{}); break;
     }
 
     // ---- epilogue ----
