@@ -63,6 +63,10 @@ SMALL = [
        expert_linear_bias_std=0.02),
     Wl("tiled_top1_direct_t640", T=640, H=256, E=4, I=128, K=1),
     Wl("tiled_shared_only_t300", T=300, H=256, E=16, I=64, K=4, shared_I=320, expert_bias_std=0.05),
+    # second row tiles of 87-113 rows: 2, 3 and 4 filled 16-row token
+    # fragments in the second token half of the tiled kernel (its main loop
+    # is compiled once per count)
+    Wl("tiled_fragments_t912", T=912, H=256, E=4, I=128, K=1),
     # large-tile kernels (>= 256 rows per expert on average, shared expert
     # from 256 tokens): ragged 64-deep slices (352), partial column tiles
     Wl("big_routed_t1100", T=1100, H=352, E=4, I=160, K=1, shared_I=96, shared_gated=True),
