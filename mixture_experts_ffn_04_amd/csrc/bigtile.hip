@@ -15,8 +15,9 @@
 // double-buffered: the next slice's global loads are in flight while the
 // current one is multiplied.  Rows of the LDS tiles are 16-byte chunks with
 // an XOR swizzle, so the 16 lanes of an operand read (16 rows, one chunk)
-// and of a store (two rows, eight chunks) touch 64 different banks.  MXFP4
-// codes are decoded to bf16 on their way into LDS.
+// and of a store (two rows, eight chunks) touch 64 different banks.  This
+// register-staged form serves MXFP4 weights when the direct-to-LDS form below
+// does not apply (codes decoded to bf16 on their way into LDS).
 //
 // gate_up tiles hold 128 gate rows and the matching 128 up rows; wavefront
 // column half wn takes gate rows 64 wn .. 64 wn + 63 and the same up rows, so
@@ -442,7 +443,9 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile(TiledGemmArgs ta) 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 weights: the same tile fed by direct-to-LDS loads.  Each load
+// The same tile fed by direct-to-LDS loads (bf16 weights, and the MXFP4
+// gate_up whose scale array starts on 16 bytes and whose reduction is at most
+// 5120 deep).  Each load
 // instruction of a wavefront writes 64 x 16 bytes to consecutive LDS
 // addresses without passing through registers, so the workgroup keeps up to
 // four 32-deep stages in flight beyond the one being multiplied (a ring of
@@ -454,16 +457,27 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile(TiledGemmArgs ta) 
 // ---------------------------------------------------------------------------
 namespace {
 
-template <bool LO, int TM>
+// MXFP4 weights: a stage holds each weight row's 16 code bytes (32 codes) in
+// one unit; the block scales of the tile's 256 weight rows over the whole
+// reduction sit in a table after the ring, loaded once per tile (the gate and
+// up rows' scales are two contiguous runs of 128 * K/32 bytes); fragments are
+// decoded to bf16 when read from LDS.
+template <bool LO, int TM, int WF = W_BF16>
 struct DmaPlan {
+  static constexpr bool MX = WF == W_MXFP4;
   static constexpr int BK = 32, CH = 4;
-  static constexpr int WUN = BN * CH, XUN = TM * CH;        // 16-byte units per operand tile
+  static constexpr int WUN = MX ? BN : BN * CH;             // 16-byte units of the weight part
+  static constexpr int XUN = TM * CH;                       // 16-byte units of one activation tile
   static constexpr int XI = XUN / 256;                      // activation load instructions per wave
   static constexpr int NXS = LO ? 2 : 1;
   static constexpr int SLOT = WUN + NXS * XUN;
   static constexpr int NSTAGE = std::min(6, (160 * 1024) / (SLOT * 16));
-  static constexpr int OPS = 4 + XI * NXS;                  // load instructions per wave and stage
+  static constexpr int OPS = (MX ? 1 : 4) + XI * NXS;       // load instructions per wave and stage
   static constexpr size_t LDS_BYTES = (size_t)NSTAGE * SLOT * 16;
+  // MXFP4 scale table: 256 rows x K/32 bytes = K/2 units, in whole 64-unit
+  // load instructions, after the ring
+  static constexpr int MAX_K = 5120;
+  static __host__ __device__ constexpr int table_units(int K) { return (K / 2 + 63) & ~63; }
   static_assert(NSTAGE >= 3 && LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(NSTAGE * SLOT * 16 >= 4 * 32 * 132 * 4, "epilogue staging fits the ring");
   static_assert((NSTAGE - 1) * OPS < 64, "vmcnt range");
@@ -472,6 +486,8 @@ struct DmaPlan {
 __device__ __forceinline__ void dma16(const char *g, u32x4_t *l) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
 }
+
+
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt and lgkmcnt left at their maxima)
@@ -503,12 +519,13 @@ __device__ __forceinline__ void barrier_lds() {
 
 }  // namespace
 
-template <bool GATE_UP, bool GATHER, bool LO, int TM>
+template <bool GATE_UP, bool GATHER, bool LO, int TM, int WF>
 __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs ta) {
-  using P = DmaPlan<LO, TM>;
+  using P = DmaPlan<LO, TM, WF>;
+  constexpr bool MX = P::MX;
   constexpr int CH = P::CH, WUN = P::WUN, XUN = P::XUN, SLOT = P::SLOT, NSTAGE = P::NSTAGE, OPS = P::OPS;
   constexpr int XI = P::XI, MF = TM / 64;  // wave sub-tile: MF fragments of 32 tokens x 128 columns
-  static_assert(!GATE_UP || P::LDS_BYTES >= epi_gate_up_bytes<MF>(), "gate_up epilogue staging fits the ring");
+  static_assert(!MX || (GATE_UP && !LO), "MXFP4 weights: gate_up only");
   const ExpertGemmArgs &a = ta.g;
   extern __shared__ u32x4_t smem[];
 
@@ -540,12 +557,8 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     // row = (wave*4 + i)*16 + lane/4; the unit holds logical chunk cs ^ f(row)
     const char *xbase = static_cast<const char *>(a.A);
     const char *xlbase = static_cast<const char *>(a.A_lo);
-    const char *wbase = static_cast<const char *>(a.W) + (size_t)c.g * a.w_stride * 2;
-    uint32_t wof[4], xof[XI], xlof[LO ? XI : 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (wave * 4 + i) * 16 + (lane >> 2);
-      const int ch = (lane & 3) ^ ((row >> 2) & 3);
+    // weight tile row -> weight row of the expert (clamped into the matrix)
+    auto wrow = [&](int row) {
       int wr, lim;
       if constexpr (GATE_UP) {
         wr = row < BN / 2 ? col0 + row : a.N + col0 + (row - BN / 2);
@@ -554,7 +567,20 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
         wr = col0 + row;
         lim = a.N - 1;
       }
-      wof[i] = ((uint32_t)min(wr, lim) * (uint32_t)a.Kdim + ch * 8) * 2u;
+      return (uint32_t)min(wr, lim);
+    };
+    const char *wbase = static_cast<const char *>(a.W) + (size_t)c.g * a.w_stride * (MX ? 1 : 2);
+    constexpr int NW = MX ? 1 : 4;  // weight load instructions per wave and stage
+    uint32_t wof[NW], xof[XI], xlof[LO ? XI : 1];
+    if constexpr (MX) {  // lane -> weight row wave * 64 + lane: its 16 code bytes
+      wof[0] = wrow(wave * 64 + lane) * (uint32_t)(a.Kdim / 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (wave * 4 + i) * 16 + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 2) & 3);
+        wof[i] = (wrow(row) * (uint32_t)a.Kdim + ch * 8) * 2u;
+      }
     }
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
@@ -572,8 +598,12 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     auto issue = [&](int st) {  // stage st into ring slot st % NSTAGE
       u32x4_t *sl = smem + (st % NSTAGE) * SLOT;
       const uint32_t kb = (uint32_t)st * (P::BK * 2);
+      if constexpr (MX) {
+        dma16(wbase + wof[0] + (uint32_t)st * (P::BK / 2), sl + wave * 64);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(wbase + wof[i] + kb, sl + (wave * 4 + i) * 64);
+        for (int i = 0; i < 4; ++i) dma16(wbase + wof[i] + kb, sl + (wave * 4 + i) * 64);
+      }
 #pragma unroll
       for (int i = 0; i < XI; ++i) dma16(xbase + xof[i] + kb, sl + WUN + (wave * XI + i) * 64);
       if constexpr (LO) {
@@ -604,13 +634,32 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     // step t run while the fragments of step t + 1 are read from LDS.
     constexpr int NB = LO ? 2 * MF : MF;
     u32x4_t af[2][4], bf[2][NB];
-    auto fetch = [&](int set, int slot, int kk, auto cnt) {
+    // MXFP4: byte of the scale table where the scales of fragment nf's row
+    // start; the scales of the stage being read (both of its 16-deep steps)
+    const uint8_t *stab = reinterpret_cast<const uint8_t *>(smem + NSTAGE * SLOT);
+    int srow[MX ? 4 : 1];
+    float scl[MX ? 4 : 1];
+    if constexpr (MX) {
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) srow[nf] = (wfrag(nf) + l32) * (a.Kdim / 32);
+    }
+    auto fetch = [&](int set, int stg, int kk, auto cnt) {
       constexpr int C = decltype(cnt)::value;
-      const u32x4_t *Wt = smem + slot * SLOT, *Xt = Wt + WUN;
+      const u32x4_t *Wt = smem + (stg % NSTAGE) * SLOT, *Xt = Wt + WUN;
       const int ch = 2 * kk + lh;
       if constexpr (C > 0) {
+        if constexpr (MX) {  // codes 16 kk + 8 lh .. + 7 of the row: dword 2 kk + lh of its unit
+          const uint32_t *Wd = reinterpret_cast<const uint32_t *>(Wt);
+          if (kk == 0) {  // a new stage: its scale bytes
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
+            for (int nf = 0; nf < 4; ++nf) scl[nf] = e8m0_to_f32(stab[srow[nf] + stg]);
+          }
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf) af[set][nf] = decode_e2m1x8(Wd[(wfrag(nf) + l32) * 4 + ch], scl[nf]);
+        } else {
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf) af[set][nf] = Wt[unit<CH>(wfrag(nf) + l32, ch)];
+        }
       }
 #pragma unroll
       for (int mf = 0; mf < C; ++mf) {
@@ -632,11 +681,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     };
     // fetch of the next step and MFMAs of this one in one scheduling region,
     // the reads spread between the MFMAs
-    auto step = [&](int next_set, int next_slot, int next_kk, int set, auto cnt) {
+    auto step = [&](int next_set, int next_stg, int next_kk, int set, auto cnt) {
       constexpr int C = decltype(cnt)::value;
-      fetch(next_set, next_slot, next_kk, cnt);
+      fetch(next_set, next_stg, next_kk, cnt);
       mma(set, cnt);
-      if constexpr (C > 0) interleave_reads<4 + (LO ? 2 * C : C), C * 4 * (LO ? 2 : 1)>();
+      if constexpr (C > 0) interleave_reads<(MX ? 8 : 4) + (LO ? 2 * C : C), C * 4 * (LO ? 2 : 1)>();
     };
     // wait until the stage `after` stages before the newest issued one has landed
     auto wait_stage = [&](int after) {
@@ -656,6 +705,25 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
     // more), stage s + NSTAGE is issued into slot s, and the first fragments
     // of stage s + 1 are read while the second step's MFMAs run.
     auto run = [&](auto cnt) {
+      if constexpr (MX) {
+        // the tile's scale table: LDS unit p holds bytes 16 q .. 16 q + 15 of
+        // the gate rows' run (p < K/4, q = p) or of the up rows' run (q = p -
+        // K/4); units past a run's valid rows (a partial last column tile) and
+        // the padding read the run's start instead and are never used.  These
+        // loads precede stage 0's, so stage 0's wait covers them.
+        const int hu = a.Kdim / 4;  // units per run of 128 rows
+        const int nv = min(BN / 2, a.N - col0) * (a.Kdim / 32) / 16;  // units of the valid rows
+        const char *gs = reinterpret_cast<const char *>(a.Wscale) + (size_t)c.g * a.s_stride;
+        const char *g0 = gs + (size_t)col0 * (a.Kdim / 32), *u0 = gs + (size_t)(a.N + col0) * (a.Kdim / 32);
+        u32x4_t *tab = smem + NSTAGE * SLOT;
+        const int n_inst = P::table_units(a.Kdim) / 64;
+        for (int j = wave; j < n_inst; j += 4) {
+          const int p = j * 64 + lane;
+          const int q = p < hu ? p : p - hu;
+          const char *src = (p < hu ? g0 : u0) + (p < 2 * hu && q < nv ? q * 16 : 0);
+          dma16(src, tab + j * 64);
+        }
+      }
 #pragma unroll
       for (int d = 0; d < NSTAGE; ++d)
         if (d < nst) issue(d);
@@ -663,14 +731,13 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
       barrier_lds();
       fetch(0, 0, 0, cnt);
       for (int s = 0; s < nst - 1; ++s) {
-        const int slot = s % NSTAGE;
-        step(1, slot, 1, 0, cnt);
+        step(1, s, 1, 0, cnt);
         wait_stage(min(NSTAGE - 2, nst - 2 - s));
         barrier_lds();
         if (s + NSTAGE < nst) issue(s + NSTAGE);
-        step(0, (s + 1) % NSTAGE, 0, 1, cnt);
+        step(0, s + 1, 0, 1, cnt);
       }
-      fetch(1, (nst - 1) % NSTAGE, 1, cnt);
+      fetch(1, nst - 1, 1, cnt);
       mma(0, cnt);
       mma(1, cnt);
     };
@@ -690,12 +757,18 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
 
 namespace {
 
-template <bool GATE_UP, bool GATHER, bool LO, int TM = BM>
+template <bool GATE_UP, bool GATHER, bool LO, int TM = BM, int WF = W_BF16>
 hipError_t launch_dma_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
-  auto kern = expert_bigtile_dma<GATE_UP, GATHER, LO, TM>;
-  constexpr size_t lds = DmaPlan<LO, TM>::LDS_BYTES;
+  using P = DmaPlan<LO, TM, WF>;
+  auto kern = expert_bigtile_dma<GATE_UP, GATHER, LO, TM, WF>;
+  // the ring (+ the MXFP4 scale table), or the gate_up epilogue's staging if
+  // that is larger
+  constexpr size_t lds_max = 160 * 1024;
+  const size_t ring = P::LDS_BYTES + (P::MX ? (size_t)P::table_units(t.g.Kdim) * 16 : 0);
+  const size_t lds = std::max(ring, GATE_UP ? epi_gate_up_bytes<TM / 64>() : (size_t)0);
+  if (lds > lds_max) return hipErrorInvalidValue;
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
   if (attr != hipSuccess) return attr;
   const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));  // one per CU
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, t);
@@ -706,7 +779,15 @@ template <bool GATE_UP, int WF, bool GATHER, bool LO>
 hipError_t launch_big_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
   if constexpr (WF == W_BF16) {
     return launch_dma_t<GATE_UP, GATHER, LO>(t, tiles_bound, st);
-  } else {  // MXFP4: codes are decoded on their way into LDS (register-staged)
+  } else {
+    if constexpr (GATE_UP && !LO) {
+      // MXFP4 gate_up: codes and the tile's scale table fed by direct-to-LDS
+      // loads (16-byte loads: the scale array starts on 16 bytes; the table
+      // fits beside the ring up to a reduction of MAX_K)
+      if ((reinterpret_cast<uintptr_t>(t.g.Wscale) & 15) == 0 && t.g.Kdim <= DmaPlan<LO, BM, W_MXFP4>::MAX_K)
+        return launch_dma_t<GATE_UP, GATHER, LO, BM, W_MXFP4>(t, tiles_bound, st);
+    }
+    // otherwise codes are decoded on their way into LDS (register-staged)
     auto kern = expert_bigtile<GATE_UP, WF, GATHER, LO>;
     constexpr size_t lds = std::max(BigPlan<LO>::LDS_BYTES, GATE_UP ? epi_gate_up_bytes<4>() : (size_t)0);
     static_assert(lds <= 160 * 1024, "LDS");

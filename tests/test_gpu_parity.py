@@ -92,10 +92,7 @@ def _report(name, rep):
     print(f"\n[parity] {name}: " + json.dumps(rep, sort_keys=True))
 
 
-@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
-def test_small_full_parity(wl):
-    print(f"[case] {wl.name}", flush=True)
-    case = Case(wl)
+def _check_whole_layer(case, name, floor_allowance=0.0):
     out, r = case.forward()
     o, ref = case.oracle_forward()
     rep = {}
@@ -103,10 +100,32 @@ def test_small_full_parity(wl):
     gi = r.indices.cpu().numpy()
     for t in np.nonzero(mism)[0]:      # near-tie tokens: the oracle on the GPU's pick
         ref[t] = case.oracle_token(t, gi[t], ow[t])
+    check_output(case, out, ref, rep, floor_allowance=floor_allowance)
+    _report(name, rep)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_full_parity(wl):
+    print(f"[case] {wl.name}", flush=True)
     # scales over 2^-40..2^20 make the output so heavy-tailed that its own bf16
     # rounding exceeds 2e-2 of its RMS; allow two of those roundings there
-    check_output(case, out, ref, rep, floor_allowance=2.0 if wl.name == "mxfp4_wide_scales" else 0.0)
-    _report(wl.name, rep)
+    _check_whole_layer(Case(wl), wl.name, floor_allowance=2.0 if wl.name == "mxfp4_wide_scales" else 0.0)
+
+
+def test_big_mxfp4_unaligned_gate_up_scales():
+    """A gate_up scale array that does not start on a 16-byte boundary: the
+    big tile then decodes through registers (its direct-to-LDS form loads
+    the scale table in 16-byte pieces); the same parity bar."""
+    wl = next(w for w in SMALL if w.name == "big_mxfp4_top2_t1100")
+    print(f"[case] {wl.name} with gate_up scales at a 1-byte offset", flush=True)
+    case = Case(wl)
+    s = case.lw.w_gate_up_scale
+    buf = torch.empty(s.numel() + 16, dtype=torch.uint8, device=s.device)
+    shifted = buf[1:1 + s.numel()].view(s.shape)
+    shifted.copy_(s)
+    assert shifted.is_contiguous() and shifted.data_ptr() % 16 == 1
+    case.lw.w_gate_up_scale = shifted
+    _check_whole_layer(case, wl.name + "_unaligned_scales")
 
 
 def test_route_entry_point_matches_forward():
