@@ -145,7 +145,8 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
     // block (16 code bytes + 1 scale)
     constexpr int WCH = (WF == W_MXFP4) ? TBN / TTHREADS : TBN * (TBK / 8) / TTHREADS;
     u32x4_t xbuf[XCH], xlbuf[XCH], wbuf[WCH];
-    uint32_t sbuf[WCH];
+    uint32_t sbuf[WCH] = {};
+    static_assert(TBK == 32, "one MXFP4 scale block per slice: slice ks reads block ks");
     int wr_l[WCH], wkc[WCH];
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
@@ -159,6 +160,11 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
       }
     }
     const size_t wbase_rows = (size_t)c.g;
+    // MXFP4 scales: with an even number of blocks per row (and the array on 2
+    // bytes), one 16-bit load brings a row's scales of two consecutive
+    // slices (a slice is one block deep), halving the scale loads, each of
+    // which touches a cache line per lane
+    const bool spair = WF == W_MXFP4 && (a.Kdim / 32) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.Wscale) & 1) == 0;
 
     auto gload = [&](int ks) {
       const int k0 = ks * TBK;
@@ -176,7 +182,10 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
             const uint8_t *cp = static_cast<const uint8_t *>(a.W) + wbase_rows * a.w_stride +
                                 (size_t)grow * (a.Kdim / 2) + k0 / 2;
             wbuf[i] = load_stream16(cp);
-            sbuf[i] = a.Wscale[wbase_rows * a.s_stride + (size_t)grow * (a.Kdim / 32) + k0 / 32];
+            const uint8_t *sp = a.Wscale + wbase_rows * a.s_stride + (size_t)grow * (a.Kdim / 32) + ks;
+            if (!spair) sbuf[i] = *sp;
+            else if ((ks & 1) == 0)  // the last slice of an odd count reads its byte alone
+              sbuf[i] = ks + 1 < nks ? (uint32_t)*reinterpret_cast<const uint16_t *>(sp) : (uint32_t)*sp;
           } else {
             wbuf[i] = u32x4_t{0u, 0u, 0u, 0u};
             sbuf[i] = 127u;
@@ -201,7 +210,8 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
 #pragma unroll
       for (int i = 0; i < WCH; ++i) {
         if constexpr (WF == W_MXFP4) {
-          const float sc = e8m0_to_f32(sbuf[i]);
+          // the buffer index is the slice's parity
+          const float sc = e8m0_to_f32(spair ? (sbuf[i] >> (8 * buf)) & 255u : sbuf[i]);
           uint16_t *dst = ws + wr_l[i] * TLD;
           *reinterpret_cast<u32x4_t *>(dst + 0) = decode_e2m1x8(wbuf[i].x, sc);
           *reinterpret_cast<u32x4_t *>(dst + 8) = decode_e2m1x8(wbuf[i].y, sc);

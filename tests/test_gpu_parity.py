@@ -61,6 +61,10 @@ SMALL = [
     Wl("tiled_routed_t600", T=600, H=384, E=8, I=160, K=2, shared_I=96, shared_gated=True),
     Wl("tiled_mxfp4_t520", T=520, H=352, E=8, I=288, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
        expert_linear_bias_std=0.02),
+    # even numbers of scale blocks per row (10 for gate_up, 6 for down): the
+    # tiled kernel reads a row's scales of two slices with one 16-bit load
+    Wl("tiled_mxfp4_paired_scales_t600", T=600, H=320, E=8, I=192, K=2, w_dtype="mxfp4",
+       swiglu_limit=7.0, expert_linear_bias_std=0.02),
     Wl("tiled_top1_direct_t640", T=640, H=256, E=4, I=128, K=1),
     Wl("tiled_shared_only_t300", T=300, H=256, E=16, I=64, K=4, shared_I=320, expert_bias_std=0.05),
     # second row tiles of 87-113 rows: 2, 3 and 4 filled 16-row token
