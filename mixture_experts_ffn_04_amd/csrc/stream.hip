@@ -155,7 +155,12 @@ struct Plan {
   static_assert(G::S_BYTES % kThreads == 0, "whole scale loads per thread");
 };
 
-template <int MT, int WF, int NS, bool GATHER, bool GATE_UP, bool LO>
+// TAB (MXFP4 gate_up, reduction <= 4096, scale array on 16 bytes): the
+// item's block scales (its gate rows' and up rows' runs of HC * K/32 bytes)
+// are loaded once per item into an LDS table with coalesced 16-byte loads,
+// instead of one byte per lane and stage (one such load instruction touches
+// about seven cache lines for 64 bytes).
+template <int MT, int WF, int NS, bool GATHER, bool GATE_UP, bool LO, bool TAB>
 __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void expert_lds_stream(ExpertGemmArgs a) {
   using P = Plan<MT, WF, NS, LO>;
   using G = typename P::G;
@@ -171,6 +176,8 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
   u32x4_t *Wl = lds;                                // [2][W_UNITS]
   u32x4_t *Xl = lds + 2 * G::W_UNITS;               // [2][NXS][X_UNITS]
   float *Sl = reinterpret_cast<float *>(lds + MAIN_UNITS);      // [2][S_BYTES] block scales as f32
+  uint8_t *tab = reinterpret_cast<uint8_t *>(lds + MAIN_UNITS);  // TAB: [2 HC][K/32] E8M0 scales
+  static_assert(!TAB || (WF == W_MXFP4 && GATE_UP), "scale table: MXFP4 gate_up");
   f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -218,9 +225,27 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
       for (int j = 0; j < G::W_LOADS; ++j)
         cp[j] = static_cast<const uint8_t *>(a.W) + (size_t)C.g * a.w_stride +
                 (size_t)wrow(j * 32 + (tid >> 3)) * (a.Kdim / 2) + wch * 16;
+      if constexpr (!TAB) {
 #pragma unroll
-      for (int j = 0; j < G::S_LOADS; ++j)
-        sp[j] = a.Wscale + (size_t)C.g * a.s_stride + (size_t)wrow(j * 32 + (tid >> 3)) * (a.Kdim / 32) + sb;
+        for (int j = 0; j < G::S_LOADS; ++j)
+          sp[j] = a.Wscale + (size_t)C.g * a.s_stride + (size_t)wrow(j * 32 + (tid >> 3)) * (a.Kdim / 32) + sb;
+      }
+    }
+    // TAB: this thread's 16-byte units of the item's scale table (unit u of
+    // the gate run, then of the up run; lanes past the table load its last
+    // unit again and store nothing)
+    constexpr int TL = 2;  // units per thread: 2 HC * K/32 / 16 <= 512 for K <= 4096
+    u32x4_t tv[TL];
+    const int t_units = TAB ? 2 * HC * (a.Kdim / 32) / 16 : 0;
+    if constexpr (TAB) {
+      const int run = t_units / 2;
+      const char *gs = reinterpret_cast<const char *>(a.Wscale) + (size_t)C.g * a.s_stride;
+      const char *g0 = gs + (size_t)(ct * HC) * (a.Kdim / 32), *u0 = gs + (size_t)(a.N + ct * HC) * (a.Kdim / 32);
+#pragma unroll
+      for (int j = 0; j < TL; ++j) {
+        const int u = min(j * kThreads + tid, t_units - 1);
+        tv[j] = load16(u < run ? g0 + u * 16 : u0 + (u - run) * 16);
+      }
     }
     // activation rows of the thread's loads.  Lanes of rows past the chunk
     // read the chunk's last row (the same addresses as that row's lanes, so
@@ -265,9 +290,11 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
         const int kc = wch * 32 < kv ? k0 / 2 : -wch * 16;
 #pragma unroll
         for (int j = 0; j < G::W_LOADS; ++j) wv[d][j] = load16(cp[j] + kc);
-        const int ks = sb * 32 < kv ? k0 / 32 : -sb;
+        if constexpr (!TAB) {
+          const int ks = sb * 32 < kv ? k0 / 32 : -sb;
 #pragma unroll
-        for (int j = 0; j < G::S_LOADS; ++j) sv[d][j] = sp[j][ks];
+          for (int j = 0; j < G::S_LOADS; ++j) sv[d][j] = sp[j][ks];
+        }
       }
       const int kx = xch * 8 < kv ? k0 : -xch * 8;
 #pragma unroll
@@ -283,8 +310,10 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
       } else {
 #pragma unroll
         for (int j = 0; j < G::W_LOADS; ++j) Wl[buf * G::W_UNITS + unit8(j * 32 + (tid >> 3), wch)] = wv[d][j];
+        if constexpr (!TAB) {
 #pragma unroll
-        for (int j = 0; j < G::S_LOADS; ++j) Sl[buf * G::S_BYTES + j * kThreads + tid] = e8m0_to_f32(sv[d][j] & 0xffu);
+          for (int j = 0; j < G::S_LOADS; ++j) Sl[buf * G::S_BYTES + j * kThreads + tid] = e8m0_to_f32(sv[d][j] & 0xffu);
+        }
       }
 #pragma unroll
       for (int j = 0; j < X_LOADS; ++j) {
@@ -319,7 +348,10 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
               wa[sx] = Wl[buf * G::W_UNITS + unit16(row, 4 * q + lg)];
             } else {
               const uint32_t *u = reinterpret_cast<const uint32_t *>(&Wl[buf * G::W_UNITS + unit8(row, q)]);
-              wa[sx] = decode_e2m1x8(u[lg], Sl[buf * G::S_BYTES + row * 8 + q]);
+              if constexpr (TAB)  // block s * 8 + q of tile row `row`
+                wa[sx] = decode_e2m1x8(u[lg], e8m0_to_f32(tab[row * (a.Kdim / 32) + s * 8 + q]));
+              else
+                wa[sx] = decode_e2m1x8(u[lg], Sl[buf * G::S_BYTES + row * 8 + q]);
             }
           }
 #pragma unroll
@@ -345,6 +377,11 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
     // last 2*kDepth - 1 stages or fewer issue only what is left.
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) issue(d, min(d, nst - 1));
+    if constexpr (TAB) {  // the previous item's last barrier is behind every wave
+#pragma unroll
+      for (int j = 0; j < TL; ++j)
+        if (j * kThreads + tid < t_units) reinterpret_cast<u32x4_t *>(tab)[j * kThreads + tid] = tv[j];
+    }
     const int nfull = nst >= 2 * kDepth ? (nst - kDepth) / kDepth : 0;
     for (int g = 0; g < nfull; ++g) {
 #pragma unroll
@@ -452,13 +489,15 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
 
 constexpr int kGridCap = 256 * 8;
 
-template <int MT, int WF, int NS, bool GATHER, bool GATE_UP, bool LO>
+template <int MT, int WF, int NS, bool GATHER, bool GATE_UP, bool LO, bool TAB>
 void launch_one(ExpertGemmArgs a, long max_chunks, hipStream_t st) {
-  constexpr size_t lds = Plan<MT, WF, NS, LO>::LDS_BYTES;
-  auto *k = expert_lds_stream<MT, WF, NS, GATHER, GATE_UP, LO>;
-  if constexpr (lds > 64 * 1024) {
+  using P = Plan<MT, WF, NS, LO>;
+  // TAB: the scale table (2 HC rows x K/32 bytes) replaces the f32 stage scales
+  const size_t lds = TAB ? (size_t)P::MAIN_UNITS * 16 + (size_t)2 * 8 * NS * (a.Kdim / 32) : P::LDS_BYTES;
+  auto *k = expert_lds_stream<MT, WF, NS, GATHER, GATE_UP, LO, TAB>;
+  if (lds > 64 * 1024) {
     static const hipError_t attr =
-        hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)attr;
   }
   a.n_tiles = a.N / (GATE_UP ? 8 * NS : 16 * NS);
@@ -467,14 +506,15 @@ void launch_one(ExpertGemmArgs a, long max_chunks, hipStream_t st) {
   hipLaunchKernelGGL(k, g, b, lds, st, a);
 }
 
-template <int MT, int WF, int NS, bool GATE_UP>
+template <int MT, int WF, int NS, bool GATE_UP, bool TAB = false>
 void launch_ns(const ExpertGemmArgs &a, bool gather, bool lo, long max_chunks, hipStream_t st) {
   if constexpr (GATE_UP) {
-    if (gather) launch_one<MT, WF, NS, true, true, false>(a, max_chunks, st);
-    else launch_one<MT, WF, NS, false, true, false>(a, max_chunks, st);
+    if (gather) launch_one<MT, WF, NS, true, true, false, TAB>(a, max_chunks, st);
+    else launch_one<MT, WF, NS, false, true, false, TAB>(a, max_chunks, st);
   } else {  // the down projection reads h rows in expert order: no gather
-    if (lo) launch_one<MT, WF, NS, false, false, true>(a, max_chunks, st);
-    else launch_one<MT, WF, NS, false, false, false>(a, max_chunks, st);
+    static_assert(!TAB, "scale table: gate_up only");
+    if (lo) launch_one<MT, WF, NS, false, false, true, false>(a, max_chunks, st);
+    else launch_one<MT, WF, NS, false, false, false, false>(a, max_chunks, st);
   }
 }
 
@@ -483,7 +523,10 @@ void launch_mt(const ExpertGemmArgs &a, WFormat wf, bool gather, bool lo, long m
   // MXFP4 items span 64 weight rows when the output columns allow it; so do
   // bf16 down items of 16-row chunks (half as many items, each streaming
   // twice the weight rows: measured 8-13% faster on down, slower on gate_up)
-  if (wf == W_MXFP4 && a.N % (GATE_UP ? 32 : 64) == 0)
+  const bool table = GATE_UP && a.Kdim <= 4096 && (reinterpret_cast<uintptr_t>(a.Wscale) & 15) == 0;
+  if (wf == W_MXFP4 && a.N % (GATE_UP ? 32 : 64) == 0 && table) {
+    if constexpr (GATE_UP) launch_ns<MT, W_MXFP4, 4, GATE_UP, true>(a, gather, lo, max_chunks, st);
+  } else if (wf == W_MXFP4 && a.N % (GATE_UP ? 32 : 64) == 0)
     launch_ns<MT, W_MXFP4, 4, GATE_UP>(a, gather, lo, max_chunks, st);
   else if (wf == W_MXFP4)
     launch_ns<MT, W_MXFP4, 2, GATE_UP>(a, gather, lo, max_chunks, st);

@@ -116,11 +116,13 @@ def test_small_full_parity(wl):
     _check_whole_layer(Case(wl), wl.name, floor_allowance=2.0 if wl.name == "mxfp4_wide_scales" else 0.0)
 
 
-def test_big_mxfp4_unaligned_gate_up_scales():
+@pytest.mark.parametrize("name", ["big_mxfp4_top2_t1100", "gpt_oss_like_mxfp4"])
+def test_mxfp4_unaligned_gate_up_scales(name):
     """A gate_up scale array that does not start on a 16-byte boundary: the
-    big tile then decodes through registers (its direct-to-LDS form loads
-    the scale table in 16-byte pieces); the same parity bar."""
-    wl = next(w for w in SMALL if w.name == "big_mxfp4_top2_t1100")
+    big tile then decodes through registers and the streaming kernel reads
+    the scales stage by stage (their usual forms load per-tile or per-item
+    scale tables in 16-byte pieces); the same parity bar."""
+    wl = next(w for w in SMALL if w.name == name)
     print(f"[case] {wl.name} with gate_up scales at a 1-byte offset", flush=True)
     case = Case(wl)
     s = case.lw.w_gate_up_scale
