@@ -394,7 +394,7 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path)", file=sys.stderr)
         return 2
 

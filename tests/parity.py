@@ -164,7 +164,7 @@ def check_routing(case: Case, o: O.RouteResult, g: api.Routing, report: dict):
 
 
 def valid_near_tie(choice_row, picked, tau, wl):
-    """The GPU's pick, judged by the oracle's selection values, is a top-K
+    """The GPU's pick, measured by the oracle's selection values, is a top-K
     (and a top-topk_group group choice) up to tau, and is ordered up to tau."""
     c = np.asarray(choice_row, dtype=np.float64)
     picked = np.asarray(picked)
