@@ -512,6 +512,23 @@ __device__ __forceinline__ void interleave_reads() {
   }
 }
 
+// The same with VALU work between the later MFMAs (the MXFP4 decode of the
+// next step's weight fragments): after the reads, each MFMA is followed by
+// an even share of NVALU vector instructions.
+template <int NREAD, int NMFMA, int NVALU, int I = 0>
+__device__ __forceinline__ void interleave_reads_valu() {
+  if constexpr (I < NREAD) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, NREAD - I >= 2 ? 2 : 1, 0);  // up to two LDS reads
+    interleave_reads_valu<NREAD, NMFMA - 1, NVALU, I + 2>();
+  } else if constexpr (NMFMA > 0) {
+    constexpr int V = (NVALU + NMFMA - 1) / NMFMA;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);                       // its share of VALU work
+    interleave_reads_valu<NREAD, NMFMA - 1, NVALU - V, I>();
+  }
+}
+
 // workgroup barrier that the compiler does not move memory operations across
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -685,7 +702,12 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
       constexpr int C = decltype(cnt)::value;
       fetch(next_set, next_stg, next_kk, cnt);
       mma(set, cnt);
-      if constexpr (C > 0) interleave_reads<(MX ? 8 : 4) + (LO ? 2 * C : C), C * 4 * (LO ? 2 : 1)>();
+      if constexpr (C > 0) {
+        if constexpr (MX)  // 4 code reads + C token reads; 4 decodes of 4 converts and their scale work
+          interleave_reads_valu<4 + C, C * 4, 20>();
+        else
+          interleave_reads<4 + (LO ? 2 * C : C), C * 4 * (LO ? 2 : 1)>();
+      }
     };
     // wait until the stage `after` stages before the newest issued one has landed
     auto wait_stage = [&](int after) {
