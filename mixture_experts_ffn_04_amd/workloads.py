@@ -210,12 +210,15 @@ def _c2(T=72):
 
 
 def _c3(T=72, selection_bias=False):
-    # router (logit) bias ~ N(0, 0.1).  The selection-only variant scales its
-    # bias to the spread of softmax scores over 512 experts (about 1/E): a
-    # bias far above the scores would pick the same experts for every token.
+    # The drafter's "router bias ~ N(0, 0.1)" in its two readings: a logit
+    # bias added to the fp32 router logits (moves selection and weights), or
+    # the selection-only expert bias (moves the picks only).  At std 0.1 the
+    # selection-only bias dominates softmax scores of about 1/E = 0.002, so
+    # that reading routes most tokens to the same few experts (collapsed
+    # routing: a few dozen active experts, the largest holding every token).
     if selection_bias:
         return Workload("qwen3_5_moe_drafter_e512_top10_selbias", T=T, H=5120, E=512,
-                        I=512, K=10, shared_I=2048, shared_gated=True, expert_bias_std=0.002)
+                        I=512, K=10, shared_I=2048, shared_gated=True, expert_bias_std=0.1)
     return Workload("qwen3_5_moe_drafter_e512_top10", T=T, H=5120, E=512, I=512, K=10,
                     shared_I=2048, shared_gated=True, router_bias_std=0.1)
 

@@ -7,13 +7,14 @@ rounded in a different order than the oracle's exact-then-rounded logits:
     to the GPU's own scores must reproduce the GPU's indices exactly and its
     weights within 1e-6 (this pins the selection logic bit for bit);
  2. scores: GPU scores are within a small relative distance of the oracle's;
- 3. end to end: on every token whose oracle selection margin exceeds
-    tau = 8 x the largest selection-value difference, the indices are equal.
-    A token inside that distance of a tie has more than one correct top-k at
-    the precision both sides decide in (f32); if the GPU picks differently
-    there, its pick must be a top-k of the oracle's own selection values up
-    to tau, and its weights and output are checked against the oracle
-    evaluated on that pick.  Counts equal the oracle's when no token differs.
+ 3. end to end: the GPU's indices equal the oracle's on every token, in
+    order, and the per-expert counts equal the oracle's counts.  A token
+    within tau = 8 x the largest selection-value difference of a tie has more
+    than one correct top-k at the precision both sides decide in (f32); such
+    a token may differ only if it is listed in NEAR_TIES with both candidate
+    selections (recorded from a run, with its margin), and its pick must then
+    still be a top-k of the oracle's own selection values up to tau.  Every
+    case reports its smallest margin, tau and the number of tokens within tau.
 Outputs: max |gpu - oracle| <= 2e-2 * rms(oracle) for bf16 outputs (the
 bound the pages' measured drift supports), 1e-5 * rms + 1e-6 for f32.
 """
@@ -30,8 +31,14 @@ from mixture_experts_ffn_04_amd import workloads as W
 from oracle import moe_oracle as O
 
 BF16_TOL = 2e-2        # max-abs error / rms(oracle output)
+
 F32_TOL = 1e-5
 WEIGHT_TOL = 1e-6
+
+# Recorded near-ties: (workload name, T) -> {token: (oracle indices, GPU
+# indices)}.  A token listed here sits within tau of a tie (its margin is
+# recorded beside it); every other token of every case must match exactly.
+NEAR_TIES: dict = {}
 
 
 def host(t):
@@ -148,10 +155,17 @@ def check_routing(case: Case, o: O.RouteResult, g: api.Routing, report: dict):
                   near_ties=int((~unique).sum()), index_mismatches=int(mism.sum()),
                   indices_equal_frac=float(1.0 - mism.mean()) if mism.size else 1.0)
     assert not np.any(mism & unique), "indices differ on a token with a clear margin"
+    allowed = NEAR_TIES.get((wl.name, wl.T), {})
+    expect = o.indices.copy()
     for t in np.nonzero(mism)[0]:
+        assert int(t) in allowed, (f"token {t}: GPU picked {gi[t].tolist()}, oracle {o.indices[t].tolist()} "
+                                   f"(margin {margins[t]:.3g}, tau {tau:.3g}); not a listed near-tie")
+        want_oracle, want_gpu = allowed[int(t)]
+        assert o.indices[t].tolist() == list(want_oracle) and gi[t].tolist() == list(want_gpu)
         assert valid_near_tie(o.choice[t], gi[t], tau, wl), f"token {t}: GPU pick is not a near-tie"
-    if not mism.any():
-        assert np.array_equal(gc, O.expert_counts(o.indices, wl.E)), "per-expert counts differ"
+        expect[t] = gi[t]
+    assert report["index_mismatches"] == len([t for t in allowed if t < len(mism)]), report
+    assert np.array_equal(gc, O.expert_counts(expect, wl.E)), "per-expert counts differ from the oracle's"
     assert np.array_equal(gc, O.expert_counts(gi, wl.E)), "counts inconsistent with the GPU indices"
     # weights: the oracle's weights for the GPU's own selection
     ow = o.weights.copy()

@@ -553,6 +553,137 @@ def test_selection_margins():
     assert abs(m[0] - (0.5 - 0.4)) < 1e-7
 
 
+def test_selection_margins_group_worked_examples():
+    # Two groups of four experts, keep one group, K = 2.  Dyadic values, so
+    # every fp32 sum and difference below is exact.
+    # (a) the group gap binds: group scores 0.875 + 0.25 = 1.125 and
+    #     0.625 + 0.4375 = 1.0625 (gap 0.0625); inside the kept group the picks
+    #     are experts 0, 1 and the best admissible value left is 0.125 (gap 0.125)
+    a = np.array([[0.875, 0.25, 0.125, 0.0, 0.625, 0.4375, 0.25, 0.0625]], dtype=F32)
+    ia = O.select(a, 2, n_group=2, topk_group=1)
+    assert ia.tolist() == [[0, 1]]
+    assert O.selection_margins(a, ia, 2, 1)[0] == 0.0625
+    # (b) the within-group gap binds, and the dropped group's 0.5 (larger than
+    #     every unpicked kept value) must not count: group scores 1.125 and
+    #     0.875 (gap 0.25); picks 0, 1; best admissible left 0.1875 -> 0.0625
+    b = np.array([[0.875, 0.25, 0.1875, 0.0, 0.5, 0.375, 0.25, 0.0625]], dtype=F32)
+    ib = O.select(b, 2, n_group=2, topk_group=1)
+    assert ib.tolist() == [[0, 1]]
+    assert O.selection_margins(b, ib, 2, 1)[0] == 0.0625
+    # (c) exact ties give a zero margin: equal group scores (1.125 both) ...
+    c = np.array([[0.875, 0.25, 0.0, 0.0, 0.625, 0.5, 0.0, 0.0]], dtype=F32)
+    assert O.selection_margins(c, O.select(c, 2, 2, 1), 2, 1)[0] == 0.0
+    # ... and a kept-group value equal to the last pick
+    d = np.array([[0.875, 0.25, 0.25, 0.0, 0.5, 0.375, 0.0, 0.0]], dtype=F32)
+    assert O.selection_margins(d, O.select(d, 2, 2, 1), 2, 1)[0] == 0.0
+    # (d) K covers every expert of the kept groups: only the group gap is left
+    e = np.array([[0.875, 0.25, 0.625, 0.4375, 0.125, 0.0]], dtype=F32)
+    ie = O.select(e, 4, n_group=3, topk_group=2)
+    assert sorted(ie[0].tolist()) == [0, 1, 2, 3]
+    assert O.selection_margins(e, ie, 3, 2)[0] == (0.625 + 0.4375) - (0.125 + 0.0)
+
+
+def _margin_by_pairs(row, picked, n_group, topk_group):
+    """Independent coding of the selection margin by enumeration: the smallest
+    difference between a kept and a dropped group score (all pairs), and
+    between a picked value and an admissible unpicked one (all pairs).  The
+    kept groups are the topk_group-subset of largest score sum, ties broken
+    by the lexicographically smallest group ids; group scores are re-derived
+    by a scalar top-2 scan."""
+    e = len(row)
+    size = e // n_group
+    gs = []
+    for g in range(n_group):
+        best, second = -math.inf, -math.inf
+        for v in row[g * size:(g + 1) * size]:
+            v = float(v)
+            if v > best:
+                best, second = v, best
+            elif v > second:
+                second = v
+        gs.append(float(F32(F32(best) + F32(second))))
+    m = math.inf
+    admissible = set(range(e))
+    if n_group > 1:
+        subsets = list(itertools.combinations(range(n_group), topk_group))
+        kept = max(subsets, key=lambda s: (sum(sorted((gs[g] for g in s))), [-g for g in s]))
+        # the kept set must be the top groups individually as well
+        dropped = [g for g in range(n_group) if g not in kept]
+        for a in kept:
+            for b in dropped:
+                m = min(m, gs[a] - gs[b])
+        admissible = {j for g in kept for j in range(g * size, (g + 1) * size)}
+    picked = [int(p) for p in picked]
+    for i in picked:
+        for j in admissible:
+            if j not in picked:
+                m = min(m, float(row[i]) - float(row[j]))
+    return m
+
+
+def test_selection_margins_match_pairwise_enumeration():
+    rng = np.random.default_rng(61)
+    cases = [(8, 2, 1, 2), (8, 2, 1, 3), (12, 3, 2, 3), (12, 4, 2, 4), (12, 4, 3, 5),
+             (12, 3, 1, 1), (9, 3, 2, 6), (12, 1, 1, 3)]
+    for e, g, tg, k in cases:
+        for trial in range(40):
+            # coarse values make exact ties (within groups, between groups) common
+            row = (rng.integers(0, 9, size=e) / 8.0).astype(F32) if trial % 2 else \
+                rng.random(e).astype(F32)
+            c = row[None, :]
+            idx = O.select(c, k, g, tg)
+            got = O.selection_margins(c, idx, g, tg)[0]
+            want = _margin_by_pairs(row, idx[0], g, tg)
+            assert got == want, (e, g, tg, k, row.tolist(), idx.tolist(), got, want)
+
+
+def test_selection_margins_bound_the_stable_region():
+    """Soundness: moving every selection value by less than margin/4 leaves the
+    group-limited selection unchanged (group scores, sums of two values, move
+    by less than margin/2).  Tightness: raising the best excluded candidate by
+    slightly more than the margin changes it."""
+    rng = np.random.default_rng(62)
+    for e, g, tg, k in [(16, 4, 2, 3), (32, 8, 4, 8), (12, 3, 1, 2), (16, 1, 1, 4)]:
+        for _ in range(60):
+            row = rng.random(e).astype(np.float64)
+            c = row.astype(F32)[None, :]
+            idx = O.select(c, k, g, tg)
+            m = O.selection_margins(c, idx, g, tg)[0]
+            assert m > 0
+            for _ in range(5):
+                d = rng.uniform(-0.24 * m, 0.24 * m, size=e)
+                c2 = (c.astype(np.float64) + d).astype(F32)
+                if np.max(np.abs(c2.astype(np.float64) - c.astype(np.float64))) >= 0.25 * m:
+                    continue     # fp32 rounding of the perturbed value
+                # the selected set (the order of near-equal picks may change)
+                assert np.array_equal(np.sort(O.select(c2, k, g, tg)), np.sort(idx))
+            # tightness: push the candidate that defines the margin past it
+            c3 = c.astype(np.float64).copy()[0]
+            size = e // g
+            gsc = O.group_scores(c[0], g).astype(np.float64) if g > 1 else None
+            kept = [0]
+            if g > 1:
+                order = np.argsort(-gsc, kind="stable")
+                kept = [int(x) for x in order[:tg]]
+                group_gap = gsc[order[tg - 1]] - gsc[order[tg]] if tg < g else math.inf
+            else:
+                group_gap = math.inf
+            adm = np.zeros(e, dtype=bool)
+            for kg in kept:
+                adm[kg * size:(kg + 1) * size] = True
+            rest = adm.copy()
+            rest[idx[0]] = False
+            within_gap = c3[idx[0]].min() - c3[rest].max() if rest.any() else math.inf
+            if within_gap <= group_gap:
+                j = int(np.flatnonzero(rest)[np.argmax(c3[rest])])
+                c3[j] += within_gap * 1.01 + 1e-6
+            else:
+                b = int(order[tg])                 # best dropped group: raise its top value
+                top = b * size + int(np.argmax(c3[b * size:(b + 1) * size]))
+                c3[top] += group_gap * 1.01 + 1e-6
+            assert not np.array_equal(np.sort(O.select(c3.astype(F32)[None, :], k, g, tg)), np.sort(idx))
+
+
 # ----------------------------------------------------------------------------
 # Load-balancing state ([SF1073] commit notes on tokens_per_expert,
 # moe/step_balance and update_expert_bias)
