@@ -342,10 +342,14 @@ enum moe_stage {
 /*
  * Arms (stage >= 0) or disarms (stage < 0) event recording on the calling
  * thread: the i-th subsequent moe_ffn_forward call on this thread records
- * start_events[i % n_events] on its stream just before the stage's kernels
- * and stop_events[i % n_events] just after them.  The events are hipEvent_t
- * handles (passed as void*) created and owned by the caller; the arrays must
- * stay valid while armed.  Arming resets the call counter.
+ * start_events[i % n_events] and stop_events[i % n_events] around the stage.
+ * Stages whose work is one kernel (MOE_STAGE_PERMUTE .. MOE_STAGE_COMBINE)
+ * hand the pair to that kernel's launch (hipExtLaunchKernelGGL), so the GPU
+ * records them at the kernel's own start and end; a stage that launches no
+ * kernel in a call records the pair back to back.  The router stages record
+ * them on the stream just before and after their kernels.  The events are
+ * hipEvent_t handles (passed as void*) created and owned by the caller; the
+ * arrays must stay valid while armed.  Arming resets the call counter.
  */
 MOE_API int moe_profile_stage(int stage, void *const *start_events, void *const *stop_events,
                               int n_events);

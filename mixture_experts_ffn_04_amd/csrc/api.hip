@@ -26,12 +26,32 @@ struct ProfileHook {
 };
 thread_local ProfileHook g_profile;
 
-// Records the hook's start (begin = true) or stop event around `stage`.
+thread_local LaunchEvents g_launch_events;
+
+// Stages whose work is a single kernel: their events ride on that kernel's
+// launch (recorded by the GPU at the kernel's own start and end).  The router
+// stages (no kernel, one or two) are bracketed by event records instead.
+bool single_kernel_stage(int stage) {
+  return stage >= MOE_STAGE_PERMUTE && stage <= MOE_STAGE_COMBINE;
+}
+
+// Arms (begin = true) or closes the hook's events around `stage`.
 hipError_t profile_mark(int stage, bool begin, hipStream_t st) {
   if (g_profile.stage != stage || g_profile.n <= 0) return hipSuccess;
   const int i = (int)(g_profile.calls % g_profile.n);
-  hipEvent_t ev = static_cast<hipEvent_t>(begin ? g_profile.start[i] : g_profile.stop[i]);
-  return hipEventRecord(ev, st);
+  hipEvent_t start = static_cast<hipEvent_t>(g_profile.start[i]);
+  hipEvent_t stop = static_cast<hipEvent_t>(g_profile.stop[i]);
+  if (single_kernel_stage(stage)) {
+    if (begin) {
+      g_launch_events = LaunchEvents{start, stop};
+      return hipSuccess;
+    }
+    if (!g_launch_events.start) return hipSuccess;  // the kernel took them
+    g_launch_events = LaunchEvents{};               // no kernel ran: an empty interval
+    hipError_t e = hipEventRecord(start, st);
+    return e != hipSuccess ? e : hipEventRecord(stop, st);
+  }
+  return hipEventRecord(begin ? start : stop, st);
 }
 
 int fail(int code, const char *fmt, ...) {
@@ -265,6 +285,10 @@ int enqueue_route(const moe_config &c, const void *x, const void *gate_w, const 
 
 }  // namespace
 
+namespace moe {
+LaunchEvents &pending_launch_events() { return g_launch_events; }
+}  // namespace moe
+
 extern "C" {
 
 MOE_API int moe_abi_version(void) { return MOE_FFN_ABI_VERSION; }
@@ -382,13 +406,15 @@ MOE_API int moe_route(const moe_config *cfg, const void *x, const void *gate_w,
                        static_cast<char *>(workspace), L, false, st);
 }
 
-MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weights *wt, void *out,
-                            float *scores, int32_t *indices, float *weights, int32_t *counts,
-                            void *workspace, size_t workspace_bytes, void *stream) {
-  const int v = moe_validate(cfg);
-  if (v != MOE_OK) return v;
-  const moe_config &c = *cfg;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// The layer forward of moe_ffn_forward after validation of cfg, on the given
+// workspace (checked here against the layout's size and alignment).
+int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void *out, float *scores,
+                 int32_t *indices, float *weights, int32_t *counts, void *workspace, size_t workspace_bytes,
+                 hipStream_t st) {
   OPTIONAL_PTR(counts, "counts");
   if (c.T == 0) {
     if (counts) HIP_TRY(launch_fill_i32(counts, 0, c.E, st), "fill launch");
@@ -599,6 +625,19 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
   HIP_TRY(profile_mark(MOE_STAGE_COMBINE, false, st), "profile event");
   ++g_profile.calls;
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weights *wt, void *out,
+                            float *scores, int32_t *indices, float *weights, int32_t *counts,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  const int v = moe_validate(cfg);
+  if (v != MOE_OK) return v;
+  return forward_impl(*cfg, x, wt, out, scores, indices, weights, counts, workspace, workspace_bytes,
+                      reinterpret_cast<hipStream_t>(stream));
 }
 
 MOE_API int moe_backward_workspace_bytes(const moe_config *cfg, size_t *bytes) {

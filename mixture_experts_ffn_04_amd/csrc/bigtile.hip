@@ -793,7 +793,7 @@ hipError_t launch_dma_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
   if (attr != hipSuccess) return attr;
   const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));  // one per CU
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, t);
+  enqueue_kernel(kern, dim3(grid), dim3(kThreads), lds, st, t);
   return hipGetLastError();
 }
 
@@ -817,7 +817,7 @@ hipError_t launch_big_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st
         hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));  // one per CU
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, t);
+    enqueue_kernel(kern, dim3(grid), dim3(kThreads), lds, st, t);
     return hipGetLastError();
   }
 }

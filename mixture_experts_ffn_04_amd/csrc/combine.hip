@@ -49,9 +49,9 @@ hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const dim3 grid((a.H + 1023) / 1024, a.T);
   if (bf16_out)
-    hipLaunchKernelGGL(combine_rows<true>, grid, dim3(256), 0, st, a);
+    enqueue_kernel(combine_rows<true>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(combine_rows<false>, grid, dim3(256), 0, st, a);
+    enqueue_kernel(combine_rows<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // pass to the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -89,6 +90,32 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
   return v;
+}
+
+// ---------------------------------------------------------------------------
+// Launch with optional timing events.  The measurement hook of the C ABI
+// (moe_profile_stage) arms a start/stop pair just before a stage whose work is
+// one kernel; that kernel's launch takes the pair, and the GPU records them
+// at the kernel's own start and end (hipExtLaunchKernelGGL), with no extra
+// packets between the kernel and its neighbours.  Thread-local, defined with
+// the hook.
+// ---------------------------------------------------------------------------
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents &pending_launch_events();
+
+// Enqueues only; the caller reads the launch status (hipGetLastError).
+template <typename K, typename... Args>
+inline void enqueue_kernel(K kern, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+  LaunchEvents &ev = pending_launch_events();
+  if (ev.start || ev.stop) {
+    const LaunchEvents e = ev;
+    ev = LaunchEvents{};
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, st, e.start, e.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kern, grid, block, lds, st, args...);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -103,15 +103,17 @@ __global__ __launch_bounds__(256) void down_f32(ExpertGemmArgs a) {
 hipError_t launch_gate_up_f32(const ExpertGemmArgs &a, int max_groups, hipStream_t st) {
   if (max_groups <= 0) return hipSuccess;
   const dim3 grid((a.N + 63) / 64, max_groups);
-  if (a.perm) hipLaunchKernelGGL(gate_up_f32<true>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(gate_up_f32<false>, grid, dim3(256), 0, st, a);
+  if (a.perm)
+    enqueue_kernel(gate_up_f32<true>, grid, dim3(256), 0, st, a);
+  else
+    enqueue_kernel(gate_up_f32<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_f32(const ExpertGemmArgs &a, int max_groups, hipStream_t st) {
   if (max_groups <= 0) return hipSuccess;
   const dim3 grid((a.N + 63) / 64, max_groups);
-  hipLaunchKernelGGL(down_f32, grid, dim3(256), 0, st, a);
+  enqueue_kernel(down_f32, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

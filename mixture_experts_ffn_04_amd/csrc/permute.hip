@@ -144,9 +144,9 @@ __global__ void fill_i32(int32_t *p, int32_t v, size_t n) {
 
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t st) {
   if (a.n_slots <= kPermuteHeld * 64 && a.E <= 64)
-    hipLaunchKernelGGL(permute_slots<64>, dim3(1), dim3(64), 0, st, a);
+    enqueue_kernel(permute_slots<64>, dim3(1), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL(permute_slots<kPermuteThreads>, dim3(1), dim3(kPermuteThreads), 0, st, a);
+    enqueue_kernel(permute_slots<kPermuteThreads>, dim3(1), dim3(kPermuteThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -503,7 +503,7 @@ void launch_one(ExpertGemmArgs a, long max_chunks, hipStream_t st) {
   a.n_tiles = a.N / (GATE_UP ? 8 * NS : 16 * NS);
   const long items = max_chunks * a.n_tiles;
   const dim3 g((unsigned)std::max(1L, std::min(items, (long)kGridCap))), b(kThreads);
-  hipLaunchKernelGGL(k, g, b, lds, st, a);
+  enqueue_kernel(k, g, b, lds, st, a);
 }
 
 template <int MT, int WF, int NS, bool GATE_UP, bool TAB = false>

@@ -370,7 +370,7 @@ static hipError_t launch_tiled_t(const TiledGemmArgs &t, long tiles_bound, hipSt
     attr_set = true;
   }
   const int grid = (int)std::max(1L, std::min(tiles_bound, 512L));  // two per CU
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(TTHREADS), tiled_lds_bytes(LO), st, t);
+  enqueue_kernel(kern, dim3(grid), dim3(TTHREADS), tiled_lds_bytes(LO), st, t);
   return hipGetLastError();
 }
 
