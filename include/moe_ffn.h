@@ -239,6 +239,31 @@ MOE_API int moe_ffn_forward(const moe_config *cfg, const void *x, const moe_weig
                     void *stream);
 
 /*
+ * Forward without allocation, for callers that cannot allocate device memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same layer as moe_ffn_forward, with
+ * the same arguments except the workspace: its scratch memory is a fixed
+ * array of MOE_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
+ * one per GPU it runs on, until the process ends.
+ *   - Returns MOE_ERR_WORKSPACE (with moe_last_error() text) when cfg needs
+ *     more scratch than that (moe_workspace_bytes(cfg) > the maximum; at
+ *     T = 72 every workload of this layer family fits; larger batches use
+ *     moe_ffn_forward).
+ *   - Calls no allocating routine (no hipMalloc / hipFree); the first call on
+ *     a device looks up that device's copy of the array.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (different streams, threads or processes sharing a
+ *     context) race and give undefined results; order them on one stream.
+ *     Nothing in the array needs to start at zero, so the contents left by
+ *     an earlier call do not matter.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+MOE_API int moe_ffn_forward_noalloc(const moe_config *cfg, const void *x, const moe_weights *w,
+                                    void *out, float *scores, int32_t *indices, float *weights,
+                                    int32_t *counts, void *stream);
+
+/*
  * Load-balancing state ([SF1073] commit notes on tokens_per_expert, on
  * MoEBalancing and on update_expert_bias).
  *

@@ -16,11 +16,14 @@ ABI_VERSION = 1
 
 MOE_DTYPE = {"f32": 0, "bf16": 1, "mxfp4": 2}
 MOE_SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
+# MOE_NOALLOC_SCRATCH_BYTES: the scratch array of moe_ffn_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route", "moe_ffn_forward",
             "moe_status_string", "moe_last_error", "moe_abi_version", "moe_profile_stage",
-            "moe_balance_count", "moe_balance_update", "moe_backward_workspace_bytes", "moe_ffn_backward")
+            "moe_balance_count", "moe_balance_update", "moe_backward_workspace_bytes", "moe_ffn_backward",
+            "moe_ffn_forward_noalloc")
 
 STAGES = ("router_logits", "router_select", "permute", "gate_up", "shared_gate_up", "down",
           "shared_down", "combine")
@@ -102,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.moe_ffn_backward.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, P, P, ctypes.POINTER(MoeGrads), P,
                                    ctypes.c_size_t, P]
     L.moe_ffn_backward.restype = ctypes.c_int
+    L.moe_ffn_forward_noalloc.argtypes = [cfgp, P, ctypes.POINTER(MoeWeights), P, P, P, P, P, P]
+    L.moe_ffn_forward_noalloc.restype = ctypes.c_int
     L.moe_abi_version.argtypes = []
     L.moe_abi_version.restype = ctypes.c_int
     if L.moe_abi_version() != ABI_VERSION:

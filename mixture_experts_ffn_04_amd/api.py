@@ -182,6 +182,28 @@ def ffn_forward(cfg: MoeConfig, x: torch.Tensor, weights: LayerWeights, *, out=N
     return out
 
 
+def ffn_forward_noalloc(cfg: MoeConfig, x: torch.Tensor, weights: LayerWeights, *, out: torch.Tensor,
+                        routing: Optional[Routing] = None, stream=None):
+    """moe_ffn_forward_noalloc: the layer forward on the library's own scratch
+    array (no workspace).  `out` (and `routing`, when given) are the caller's;
+    this wrapper allocates nothing."""
+    dev = x.device
+    T, H, E, K = cfg.T, cfg.H, cfg.E, cfg.K
+    ad = _act_dtype(cfg)
+    w = weights.check(cfg, dev)
+    r = routing
+    rargs = [
+        _ptr(r.scores if r else None, "scores", dtype=torch.float32, shape=(T, E), device=dev),
+        _ptr(r.indices if r else None, "indices", dtype=torch.int32, shape=(T, K), device=dev),
+        _ptr(r.weights if r else None, "weights", dtype=torch.float32, shape=(T, K), device=dev),
+        _ptr(r.counts if r else None, "counts", dtype=torch.int32, shape=(E,), device=dev),
+    ]
+    check(lib().moe_ffn_forward_noalloc(
+        ctypes.byref(cfg), _ptr(x, "x", dtype=ad, shape=(T, H), device=dev), ctypes.byref(w),
+        _ptr(out, "out", dtype=ad, shape=(T, H), device=dev), *rargs, _stream(stream)))
+    return out
+
+
 def balance_count(indices: torch.Tensor, tokens_per_expert: torch.Tensor, token_mask=None, *,
                   stream=None) -> torch.Tensor:
     """moe_balance_count: tokens_per_expert [E] int64 += the kept slots of

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_ffn.h"
@@ -770,6 +771,67 @@ MOE_API int moe_balance_update(int64_t *tokens_per_expert, float *expert_bias, i
   BalanceUpdateArgs a{tokens_per_expert, expert_bias, step_balance, bias_update_rate, E};
   HIP_TRY(launch_balance_update(a, reinterpret_cast<hipStream_t>(stream)), "balance update launch");
   return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward without allocation: moe_ffn_forward on a scratch array that the
+// library holds in device memory, one per GPU, for callers that cannot
+// allocate a workspace.
+// ---------------------------------------------------------------------------
+
+// In host code `scratch` names a host-side stand-in, not device memory: host
+// code uses only the device address that hipGetSymbolAddress returns for it
+// (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept.
+int scratch_ptr(void **out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255) != 0)
+      return fail(MOE_ERR_HIP, "scratch array has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOE_API int moe_ffn_forward_noalloc(const moe_config *cfg, const void *x, const moe_weights *wt, void *out,
+                                    float *scores, int32_t *indices, float *weights, int32_t *counts,
+                                    void *stream) {
+  const int v = moe_validate(cfg);
+  if (v != MOE_OK) return v;
+  const size_t need = make_layout(*cfg).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this configuration needs %zu bytes of scratch; the no-allocation forward holds %zu "
+                "(use moe_ffn_forward with a workspace)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (cfg->T > 0) {
+    const int r = scratch_ptr(&ws);
+    if (r != MOE_OK) return r;
+  }
+  return forward_impl(*cfg, x, wt, out, scores, indices, weights, counts, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                      reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
