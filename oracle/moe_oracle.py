@@ -328,7 +328,18 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float) -> np.ndarray:
+# READING of gpt-oss's "swigluoai" ([SGL48763] DraftMLP commit note names it
+# as an activation; no page defines it): the form gpt-oss publishes with its
+# model, h = g * sigmoid(alpha * g) * (u + 1) with alpha = 1.702, on the same
+# clamped pre-activations as the SwiGLU clamp below (g capped above at +limit,
+# u clipped to [-limit, +limit]; gpt-oss uses limit 7).  Parity unpinned by
+# the pages: its pins check this reading, not the pages.
+SWIGLU_OAI_ALPHA = 1.702
+ACTIVATIONS = ("swiglu", "swiglu_oai")
+
+
+def swiglu(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float,
+           activation: str = "swiglu") -> np.ndarray:
     """SwiGLU activation with the optional clamp.
 
     [SGL48763] Modifications / DraftMLP commit note: gate-up and down linears
@@ -337,14 +348,25 @@ def swiglu(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float) -> np.ndarray
     (the pages do not spell it out): the gate pre-activation is capped above at
     +limit, the up pre-activation is clipped to [-limit, +limit];
     limit = +inf means no clamp.
+
+    activation "swiglu":     silu(g) * u
+    activation "swiglu_oai": g * sigmoid(SWIGLU_OAI_ALPHA * g) * (u + 1)
+    (g, u the clamped gate and up pre-activations).
     """
     if math.isinf(limit):
-        return silu(gate_pre) * up_pre
-    return silu(np.minimum(gate_pre, limit)) * np.clip(up_pre, -limit, limit)
+        g, u = gate_pre, up_pre
+    else:
+        g, u = np.minimum(gate_pre, limit), np.clip(up_pre, -limit, limit)
+    if activation == "swiglu":
+        return silu(g) * u
+    if activation == "swiglu_oai":
+        return g / (1.0 + np.exp(-SWIGLU_OAI_ALPHA * g)) * (u + 1.0)
+    raise ValueError(activation)
 
 
 def expert_mlp(rows64: np.ndarray, w_gate_up64: np.ndarray, w_down64: np.ndarray,
-               limit: float, b_gate_up64=None, b_down64=None) -> np.ndarray:
+               limit: float, b_gate_up64=None, b_down64=None,
+               activation: str = "swiglu") -> np.ndarray:
     """One expert (or the dense/shared MLP) on rows [n, H] -> [n, H], fp64.
 
     w_gate_up is the stacked [2I, H] matrix ([SF1073] converter commit note:
@@ -358,7 +380,7 @@ def expert_mlp(rows64: np.ndarray, w_gate_up64: np.ndarray, w_down64: np.ndarray
     pre = rows64 @ w_gate_up64.T
     if b_gate_up64 is not None:
         pre = pre + b_gate_up64
-    h = swiglu(pre[:, :inter], pre[:, inter:], limit)
+    h = swiglu(pre[:, :inter], pre[:, inter:], limit, activation)
     y = h @ w_down64.T
     if b_down64 is not None:
         y = y + b_down64
@@ -395,7 +417,7 @@ def permutation(indices: np.ndarray, n_experts: int):
 
 def routed_grouped(x64: np.ndarray, indices: np.ndarray, weights32: np.ndarray,
                    get_expert: Callable[[int], ExpertWeights], n_experts: int,
-                   limit: float) -> np.ndarray:
+                   limit: float, activation: str = "swiglu") -> np.ndarray:
     """Weighted routed output [T, H] (fp64), expert-grouped coding.
 
     Slots are grouped by expert (permutation), each expert runs once on its
@@ -412,7 +434,7 @@ def routed_grouped(x64: np.ndarray, indices: np.ndarray, weights32: np.ndarray,
             continue
         w = get_expert(e)
         y_slot[sl] = expert_mlp(x64[sl // k], w.w_gate_up, w.w_down, limit,
-                                w.b_gate_up, w.b_down)
+                                w.b_gate_up, w.b_down, activation)
     out = np.zeros_like(x64)
     w64 = weights32.astype(F64)
     for kk in range(k):
@@ -421,7 +443,8 @@ def routed_grouped(x64: np.ndarray, indices: np.ndarray, weights32: np.ndarray,
 
 
 def routed_loop(x64: np.ndarray, indices: np.ndarray, weights32: np.ndarray,
-                get_expert: Callable[[int], ExpertWeights], limit: float) -> np.ndarray:
+                get_expert: Callable[[int], ExpertWeights], limit: float,
+                activation: str = "swiglu") -> np.ndarray:
     """The same routed output, token by token (a second, independent coding)."""
     t_count, k = indices.shape
     out = np.zeros_like(x64)
@@ -430,14 +453,15 @@ def routed_loop(x64: np.ndarray, indices: np.ndarray, weights32: np.ndarray,
         for kk in range(k):
             w = get_expert(int(indices[t, kk]))
             y = expert_mlp(x64[t:t + 1], w.w_gate_up, w.w_down, limit,
-                           w.b_gate_up, w.b_down)[0]
+                           w.b_gate_up, w.b_down, activation)[0]
             acc = acc + F64(weights32[t, kk]) * y
         out[t] = acc
     return out
 
 
 def shared_expert(x64: np.ndarray, sh_gate_up64: np.ndarray, sh_down64: np.ndarray,
-                  limit: float, sh_gate64: Optional[np.ndarray]) -> np.ndarray:
+                  limit: float, sh_gate64: Optional[np.ndarray],
+                  activation: str = "swiglu") -> np.ndarray:
     """gamma_t * SwiGLU-MLP(x_t) [T, H], fp64.
 
     [SGL48763] DraftMoE commit notes: the shared expert is a DraftMLP with an
@@ -445,9 +469,10 @@ def shared_expert(x64: np.ndarray, sh_gate_up64: np.ndarray, sh_down64: np.ndarr
     Qwen-style block's sigmoid-gated shared expert; [SF1073] DeepSeek-V4
     family: one ungated shared expert with the same clamp.  READING: the gate
     is a bias-free H -> 1 linear, gamma = sigmoid(x . sh_gate); ungated means
-    gamma = 1; route_scale does not touch the shared expert.
+    gamma = 1; route_scale does not touch the shared expert.  The layer's
+    activation (and clamp) applies to the shared expert as to the routed ones.
     """
-    sh = expert_mlp(x64, sh_gate_up64, sh_down64, limit)
+    sh = expert_mlp(x64, sh_gate_up64, sh_down64, limit, activation=activation)
     if sh_gate64 is None:
         return sh
     gamma = 1.0 / (1.0 + np.exp(-(x64 @ sh_gate64)))
@@ -458,7 +483,7 @@ def ffn_forward(x64, gate64, get_expert, *, n_experts, k, score_fn="softmax",
                 n_group=1, topk_group=1, norm_topk_prob=True, route_scale=1.0,
                 expert_bias=None, router_bias=None, limit=math.inf,
                 sh_gate_up64=None, sh_down64=None, sh_gate64=None,
-                coding="grouped"):
+                coding="grouped", activation="swiglu"):
     """Whole layer forward: (RouteResult, out [T, H] fp64).
 
     out[t] = sum_k w[t,k] * expert_{idx[t,k]}(x_t) + gamma_t * shared(x_t).
@@ -468,18 +493,19 @@ def ffn_forward(x64, gate64, get_expert, *, n_experts, k, score_fn="softmax",
               route_scale=route_scale, expert_bias=expert_bias,
               router_bias=router_bias)
     if coding == "grouped":
-        out = routed_grouped(x64, r.indices, r.weights, get_expert, n_experts, limit)
+        out = routed_grouped(x64, r.indices, r.weights, get_expert, n_experts, limit, activation)
     elif coding == "loop":
-        out = routed_loop(x64, r.indices, r.weights, get_expert, limit)
+        out = routed_loop(x64, r.indices, r.weights, get_expert, limit, activation)
     else:
         raise ValueError(coding)
     if sh_gate_up64 is not None:
-        out = out + shared_expert(x64, sh_gate_up64, sh_down64, limit, sh_gate64)
+        out = out + shared_expert(x64, sh_gate_up64, sh_down64, limit, sh_gate64, activation)
     return r, out
 
 
 def token_output(x_row64, indices_row, weights_row32, get_expert, limit,
-                 sh_gate_up64=None, sh_down64=None, sh_gate64=None) -> np.ndarray:
+                 sh_gate_up64=None, sh_down64=None, sh_gate64=None,
+                 activation="swiglu") -> np.ndarray:
     """One token's output row [H] (fp64) given its routing; for sampled checks
     at sizes where the whole layer is too large to evaluate on the CPU."""
     x1 = np.asarray(x_row64, dtype=F64)[None, :]
@@ -487,9 +513,9 @@ def token_output(x_row64, indices_row, weights_row32, get_expert, limit,
     for kk in range(len(indices_row)):
         w = get_expert(int(indices_row[kk]))
         acc = acc + F64(weights_row32[kk]) * expert_mlp(
-            x1, w.w_gate_up, w.w_down, limit, w.b_gate_up, w.b_down)[0]
+            x1, w.w_gate_up, w.w_down, limit, w.b_gate_up, w.b_down, activation)[0]
     if sh_gate_up64 is not None:
-        acc = acc + shared_expert(x1, sh_gate_up64, sh_down64, limit, sh_gate64)[0]
+        acc = acc + shared_expert(x1, sh_gate_up64, sh_down64, limit, sh_gate64, activation)[0]
     return acc
 
 
@@ -583,10 +609,12 @@ class LayerGrads:
 
 
 def swiglu_backward(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float,
-                    dh: np.ndarray):
-    """(d gate_pre, d up_pre) of h = silu(min(g, L)) * clip(u, -L, L).
+                    dh: np.ndarray, activation: str = "swiglu"):
+    """(d gate_pre, d up_pre) of h = act(min(g, L), clip(u, -L, L)).
 
-    silu'(z) = sigma(z) * (1 + z * (1 - sigma(z))).  READING: where the clamp
+    "swiglu": act = silu(g) u, silu'(z) = sigma(z) * (1 + z * (1 - sigma(z)));
+    "swiglu_oai": act = g sigma(a g) (u + 1), d/dg = sigma(a g) (1 + a g
+    (1 - sigma(a g))) (u + 1), d/du = g sigma(a g).  READING: where the clamp
     binds the gradient is cut; on the boundary itself (g = L, u = +-L) it
     passes, as for a clamp whose gradient mask is inclusive.
     """
@@ -600,11 +628,15 @@ def swiglu_backward(gate_pre: np.ndarray, up_pre: np.ndarray, limit: float,
         gc, uc = np.minimum(g, limit), np.clip(u, -limit, limit)
         g_pass = g <= limit
         u_pass = (u >= -limit) & (u <= limit)
-    sig = 1.0 / (1.0 + np.exp(-gc))
-    silu_g = gc * sig
-    dsilu = sig * (1.0 + gc * (1.0 - sig))
-    dg = np.where(g_pass, dh * uc * dsilu, 0.0)
-    du = np.where(u_pass, dh * silu_g, 0.0)
+    a = 1.0 if activation == "swiglu" else SWIGLU_OAI_ALPHA
+    if activation not in ACTIVATIONS:
+        raise ValueError(activation)
+    sig = 1.0 / (1.0 + np.exp(-a * gc))
+    glu = gc * sig
+    dglu = sig * (1.0 + a * gc * (1.0 - sig))
+    lin = uc if activation == "swiglu" else uc + 1.0
+    dg = np.where(g_pass, dh * lin * dglu, 0.0)
+    du = np.where(u_pass, dh * glu, 0.0)
     return dg, du
 
 
@@ -643,7 +675,8 @@ def weights_backward(picked64: np.ndarray, dweights: np.ndarray, norm_topk_prob:
 def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="softmax",
                  n_group=1, topk_group=1, norm_topk_prob=True, route_scale=1.0,
                  expert_bias=None, router_bias=None, limit=math.inf,
-                 sh_gate_up64=None, sh_down64=None, sh_gate64=None) -> LayerGrads:
+                 sh_gate_up64=None, sh_down64=None, sh_gate64=None,
+                 activation="swiglu") -> LayerGrads:
     """Gradients of the layer at (x, weights) for the output gradient dout.
 
     The selection (indices) is the forward's (route(), fp32 decisions) and is
@@ -700,7 +733,7 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
             pre = wgu @ xt
             if ew.b_gate_up is not None:
                 pre = pre + ew.b_gate_up
-            h = swiglu(pre[:inter], pre[inter:], limit)
+            h = swiglu(pre[:inter], pre[inter:], limit, activation)
             y = wd @ h
             if ew.b_down is not None:
                 y = y + ew.b_down
@@ -713,7 +746,7 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
             if ew.b_down is not None:
                 dbd[e] = dbd.get(e, 0.0) + dy
             # SwiGLU and gate_up: pre = Wgu x (+ b)
-            dg, du = swiglu_backward(pre[:inter], pre[inter:], limit, dh)
+            dg, du = swiglu_backward(pre[:inter], pre[inter:], limit, dh, activation)
             dpre = np.concatenate([dg, du])
             dwgu[e] = dwgu.get(e, 0.0) + np.outer(dpre, xt)
             if ew.b_gate_up is not None:
@@ -722,13 +755,13 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
         if has_sh:
             inter_s = wsgu.shape[0] // 2
             pre_s = wsgu @ xt
-            h_s = swiglu(pre_s[:inter_s], pre_s[inter_s:], limit)
+            h_s = swiglu(pre_s[:inter_s], pre_s[inter_s:], limit, activation)
             sh = wsd @ h_s
             gam = 1.0 / (1.0 + np.exp(-np.dot(xt, sh_gate64))) if sh_gate64 is not None else 1.0
             dsh = gam * dt
             dh_s = wsd.T @ dsh
             dsd += np.outer(dsh, h_s)
-            dg_s, du_s = swiglu_backward(pre_s[:inter_s], pre_s[inter_s:], limit, dh_s)
+            dg_s, du_s = swiglu_backward(pre_s[:inter_s], pre_s[inter_s:], limit, dh_s, activation)
             dpre_s = np.concatenate([dg_s, du_s])
             dsgu += np.outer(dpre_s, xt)
             dx[t] += wsgu.T @ dpre_s

@@ -59,7 +59,7 @@ def oracle_indices(c, **kw):
 
 
 def torch_forward(c, idx, t, score_fn="softmax", norm_topk_prob=True, route_scale=1.0,
-                  limit=math.inf, **_):
+                  limit=math.inf, activation="swiglu", **_):
     """The layer in torch ops, selection `idx` fixed.  `t`: dict of leaf tensors."""
     logits = t["x"] @ t["gate"].T
     if "rb" in t:
@@ -85,7 +85,10 @@ def torch_forward(c, idx, t, score_fn="softmax", norm_topk_prob=True, route_scal
         if not math.isinf(limit):
             g = torch.clamp(g, max=limit)
             u = torch.clamp(u, -limit, limit)
-        y = (F.silu(g) * u) @ wd.T
+        if activation == "swiglu_oai":
+            y = (g * torch.sigmoid(1.702 * g) * (u + 1.0)) @ wd.T
+        else:
+            y = (F.silu(g) * u) @ wd.T
         return y + bd if bd is not None else y
 
     rows = []
@@ -130,6 +133,8 @@ KW_CASES = [
     dict(score_fn="softmax", norm_topk_prob=False),
     dict(score_fn="sigmoid", n_group=3, topk_group=2, route_scale=2.5),
     dict(score_fn="softmax", limit=0.7),
+    dict(score_fn="softmax", limit=0.7, activation="swiglu_oai"),
+    dict(score_fn="sigmoid", n_group=3, topk_group=2, route_scale=2.5, activation="swiglu_oai"),
 ]
 
 
@@ -242,7 +247,8 @@ def test_score_backward_matches_autograd(fn):
     np.testing.assert_allclose(got, lt.grad.numpy(), rtol=1e-12, atol=1e-14)
 
 
-def test_swiglu_backward_matches_autograd_with_clamp_on_both_sides():
+@pytest.mark.parametrize("activation", ["swiglu", "swiglu_oai"])
+def test_swiglu_backward_matches_autograd_with_clamp_on_both_sides(activation):
     rng = np.random.default_rng(9)
     g = rng.standard_normal(200) * 4
     u = rng.standard_normal(200) * 4
@@ -252,8 +258,12 @@ def test_swiglu_backward_matches_autograd_with_clamp_on_both_sides():
         ut = torch.tensor(u, requires_grad=True)
         gc = gt if math.isinf(lim) else torch.clamp(gt, max=lim)
         uc = ut if math.isinf(lim) else torch.clamp(ut, -lim, lim)
-        (F.silu(gc) * uc * torch.tensor(dh)).sum().backward()
-        dg, du = O.swiglu_backward(g, u, lim, dh)
+        if activation == "swiglu":
+            h = F.silu(gc) * uc
+        else:
+            h = gc * torch.sigmoid(1.702 * gc) * (uc + 1.0)
+        (h * torch.tensor(dh)).sum().backward()
+        dg, du = O.swiglu_backward(g, u, lim, dh, activation)
         np.testing.assert_allclose(dg, gt.grad.numpy(), rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(du, ut.grad.numpy(), rtol=1e-12, atol=1e-14)
         if not math.isinf(lim):

@@ -400,7 +400,18 @@ def _rand_experts(rng, e, h, i, with_bias=False):
     return ws
 
 
-def _pure_python_forward(x, idx, w, experts, limit, shared=None):
+def _act_scalar(g, u, limit, activation):
+    """One SwiGLU element by scalar math.  swiglu_oai takes the logistic
+    function in its tanh form, sigma(z) = (1 + tanh(z / 2)) / 2, a route
+    independent of the oracle's 1 / (1 + exp(-z))."""
+    if limit != math.inf:
+        g = min(g, limit); u = max(-limit, min(limit, u))
+    if activation == "swiglu_oai":
+        return g * 0.5 * (1.0 + math.tanh(0.851 * g)) * (u + 1.0)     # 0.851 = 1.702 / 2
+    return g / (1.0 + math.exp(-g)) * u
+
+
+def _pure_python_forward(x, idx, w, experts, limit, shared=None, activation="swiglu"):
     """Brute force with scalar loops only (tiny sizes)."""
     t_count, h = x.shape
     out = [[0.0] * h for _ in range(t_count)]
@@ -414,9 +425,7 @@ def _pure_python_forward(x, idx, w, experts, limit, shared=None):
                 u = sum(x[t, c] * ex.w_gate_up[inter + j, c] for c in range(h))
                 if ex.b_gate_up is not None:
                     g += ex.b_gate_up[j]; u += ex.b_gate_up[inter + j]
-                if limit != math.inf:
-                    g = min(g, limit); u = max(-limit, min(limit, u))
-                hv.append(g / (1.0 + math.exp(-g)) * u)
+                hv.append(_act_scalar(g, u, limit, activation))
             for n in range(h):
                 y = sum(hv[j] * ex.w_down[n, j] for j in range(inter))
                 if ex.b_down is not None:
@@ -429,19 +438,18 @@ def _pure_python_forward(x, idx, w, experts, limit, shared=None):
             for j in range(inter):
                 g = sum(x[t, c] * gu[j, c] for c in range(h))
                 u = sum(x[t, c] * gu[inter + j, c] for c in range(h))
-                if limit != math.inf:
-                    g = min(g, limit); u = max(-limit, min(limit, u))
-                hv.append(g / (1.0 + math.exp(-g)) * u)
+                hv.append(_act_scalar(g, u, limit, activation))
             gamma = 1.0 if gv is None else 1.0 / (1.0 + math.exp(-sum(x[t, c] * gv[c] for c in range(h))))
             for n in range(h):
                 out[t][n] += gamma * sum(hv[j] * dn[n, j] for j in range(inter))
     return np.array(out)
 
 
-@pytest.mark.parametrize("limit,bias,shared,gated", [
-    (math.inf, False, False, False), (0.7, False, True, True),
-    (0.7, True, False, False), (math.inf, False, True, False)])
-def test_forward_matches_pure_python(limit, bias, shared, gated):
+@pytest.mark.parametrize("limit,bias,shared,gated,activation", [
+    (math.inf, False, False, False, "swiglu"), (0.7, False, True, True, "swiglu"),
+    (0.7, True, False, False, "swiglu"), (math.inf, False, True, False, "swiglu"),
+    (0.7, True, True, True, "swiglu_oai"), (math.inf, False, True, False, "swiglu_oai")])
+def test_forward_matches_pure_python(limit, bias, shared, gated, activation):
     rng = np.random.default_rng(51)
     t_count, h, i, e, k = 5, 6, 3, 4, 2
     x = rng.standard_normal((t_count, h))
@@ -454,8 +462,8 @@ def test_forward_matches_pure_python(limit, bias, shared, gated):
               0.3 * rng.standard_normal(h) if gated else None)
         kw = dict(sh_gate_up64=sh[0], sh_down64=sh[1], sh_gate64=sh[2])
     r, out = O.ffn_forward(x, gate, lambda j: experts[j], n_experts=e, k=k,
-                           limit=limit, **kw)
-    ref = _pure_python_forward(x, r.indices, r.weights, experts, limit, sh)
+                           limit=limit, activation=activation, **kw)
+    ref = _pure_python_forward(x, r.indices, r.weights, experts, limit, sh, activation)
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
@@ -502,6 +510,36 @@ def test_clamp_definition_and_special_limits():
     assert np.allclose(O.swiglu(gg.numpy(), uu.numpy(), math.inf), (F.silu(gg) * uu).numpy(),
                        rtol=1e-14, atol=1e-300)
     assert np.all(O.swiglu(gg.numpy(), uu.numpy(), 0.0) == 0)
+
+
+def test_swiglu_oai_closed_forms_and_identities():
+    """gpt-oss's activation as read here: h = g sigma(1.702 g) (u + 1) on the
+    clamped pre-activations (a reading, not the pages' definition: parity of
+    this activation is unpinned by the pages)."""
+    rng = np.random.default_rng(57)
+    g = rng.uniform(-6.5, 6.5, 2000); u = rng.uniform(-9, 9, 2000)
+    L = 7.0
+    # zeros: the gate at 0, the linear factor at u = -1
+    assert np.all(O.swiglu(np.zeros(5), rng.uniform(-5, 5, 5), L, "swiglu_oai") == 0)
+    assert np.all(O.swiglu(rng.uniform(-5, 5, 5), np.full(5, -1.0), L, "swiglu_oai") == 0)
+    # one value worked by hand: g = 1, u = 0 gives sigma(1.702) = 1 / (1 + 0.182319...) = 0.845796...
+    assert abs(O.swiglu(np.array([1.0]), np.array([0.0]), L, "swiglu_oai")[0] - 0.8457957659) < 1e-9
+    # odd part: sigma(z) + sigma(-z) = 1, so h(g, u) - h(-g, u) = g (u + 1) for |g| <= L
+    uc = np.clip(u, -L, L)
+    d = O.swiglu(g, u, L, "swiglu_oai") - O.swiglu(-g, u, L, "swiglu_oai")
+    assert np.allclose(d, g * (uc + 1.0), rtol=1e-13, atol=1e-13)
+    # the clamp: g above L acts as L, u outside [-L, L] as the bound
+    assert np.array_equal(O.swiglu(g + 20.0, u, L, "swiglu_oai"), O.swiglu(np.full_like(g, L), u, L, "swiglu_oai"))
+    assert np.array_equal(O.swiglu(g, np.where(u > 0, 30.0, -30.0), L, "swiglu_oai"),
+                          O.swiglu(g, np.where(u > 0, L, -L), L, "swiglu_oai"))
+    # tails without a clamp: g sigma(a g) -> g for large g, -> 0 for very negative g
+    big = np.array([60.0, -60.0])
+    h = O.swiglu(big, np.array([1.0, 1.0]), math.inf, "swiglu_oai")
+    assert h[0] == 120.0 and abs(h[1]) < 1e-40
+    # against torch's sigmoid (fp64), a library route to the logistic function
+    gt, ut = torch.from_numpy(np.minimum(g, L)), torch.from_numpy(uc)
+    ref = (gt * torch.sigmoid(1.702 * gt) * (ut + 1.0)).numpy()
+    assert np.allclose(O.swiglu(g, u, L, "swiglu_oai"), ref, rtol=1e-14, atol=1e-14)
 
 
 def test_zero_limit_leaves_only_shared_expert():
