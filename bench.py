@@ -490,7 +490,7 @@ def cpu_baseline(wl, host, budget_s):
             O.to_f64(x_h[t0:t1], ad), O.to_f64(gate_h, ad), get_expert, n_experts=wl.E, k=wl.K,
             score_fn=wl.score_fn, n_group=wl.n_group, topk_group=wl.topk_group,
             norm_topk_prob=wl.norm_topk_prob, route_scale=wl.route_scale,
-            expert_bias=eb, router_bias=rb, limit=wl.swiglu_limit,
+            expert_bias=eb, router_bias=rb, limit=wl.swiglu_limit, activation=wl.activation,
             sh_gate_up64=O.to_f64(sh[0], ad) if sh else None,
             sh_down64=O.to_f64(sh[1], ad) if sh else None,
             sh_gate64=O.to_f64(shg, ad) if shg is not None else None)

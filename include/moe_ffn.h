@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 1
+#define MOE_FFN_ABI_VERSION 2
 
 /* Symbols of the shared library are exported explicitly. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -91,6 +91,19 @@ enum moe_score_fn {
   MOE_SCORE_SIGMOID = 1,      /* 1 / (1 + exp(-logit))                         */
   MOE_SCORE_SQRTSOFTPLUS = 2  /* sqrt(log(1 + exp(logit)))                      */
 };
+
+/* SwiGLU activation of the experts (routed and shared), on the clamped
+ * pre-activations g' = min(g, L), u' = min(max(u, -L), L) (L = swiglu_limit):
+ *   MOE_ACT_SWIGLU      h = silu(g') * u'                  ([SGL48763] DraftMLP
+ *                       commit note; [SF1073] DeepSeek-V4 family: clamped SwiGLU)
+ *   MOE_ACT_SWIGLU_OAI  h = g' * sigmoid(1.702 g') * (u' + 1): gpt-oss's
+ *                       "swigluoai", named in [SGL48763]'s DraftMLP commit note
+ *                       but defined on no page; the form gpt-oss publishes. */
+enum moe_activation {
+  MOE_ACT_SWIGLU = 0,
+  MOE_ACT_SWIGLU_OAI = 1
+};
+#define MOE_SWIGLU_OAI_ALPHA 1.702f
 
 /* Status codes. */
 enum moe_status {
@@ -129,6 +142,10 @@ enum moe_status {
  *   shared_I   intermediate size of the shared expert; 0 = none.
  *   shared_gated  1: the shared expert is scaled by sigmoid(x . sh_gate)
  *              ([SGL48763], [SF941]); 0: ungated ([SF1073]).
+ *   activation enum moe_activation, for routed and shared experts alike.
+ *              Both kinds take w_gate_up's gate rows first, then its up rows
+ *              (a checkpoint that interleaves them is de-interleaved once when
+ *              the weights are laid out).
  */
 typedef struct moe_config {
   int32_t T, H, E, I, K;
@@ -142,6 +159,7 @@ typedef struct moe_config {
   float swiglu_limit;
   int32_t shared_I;
   int32_t shared_gated;
+  int32_t activation;
 } moe_config;
 
 /*
@@ -190,7 +208,8 @@ typedef struct moe_weights {
  * MOE_ERR_INVALID (T < 0; H, E, I or K <= 0; K > E; n_group < 1; E not a
  * multiple of n_group; topk_group outside [1, n_group]; group size < 2 with
  * n_group > 1; K > topk_group * E / n_group; unknown dtype or score_fn;
- * route_scale not finite; swiglu_limit NaN or negative; shared_I < 0) or
+ * route_scale not finite; swiglu_limit NaN or negative; shared_I < 0;
+ * unknown activation) or
  * MOE_ERR_UNSUPPORTED (E > MOE_MAX_EXPERTS, K > MOE_MAX_TOPK,
  * n_group > MOE_MAX_GROUPS, H, I or shared_I not a multiple of 32, a dtype
  * pairing other than f32/f32, bf16/bf16, bf16/mxfp4).

@@ -349,6 +349,8 @@ MOE_API int moe_validate(const moe_config *cfg) {
     return fail(MOE_ERR_INVALID, "swiglu_limit must be >= 0 or +inf");
   if (c.shared_I < 0) return fail(MOE_ERR_INVALID, "shared_I = %d < 0", c.shared_I);
   if (c.shared_gated != 0 && c.shared_gated != 1) return fail(MOE_ERR_INVALID, "shared_gated must be 0 or 1");
+  if (c.activation != MOE_ACT_SWIGLU && c.activation != MOE_ACT_SWIGLU_OAI)
+    return fail(MOE_ERR_INVALID, "activation %d is unknown", c.activation);
 
   if (c.E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", c.E, MOE_MAX_EXPERTS);
   if (c.K > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "K = %d > %d", c.K, MOE_MAX_TOPK);
@@ -506,6 +508,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
   g1.out = ws + L.h;
   if (hilo) g1.out_lo = h_lo;
   g1.limit = c.swiglu_limit;
+  g1.act = c.activation;
   HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, true, st), "profile event");
   if (wf == W_F32) {
     HIP_TRY(launch_gate_up_f32(g1, max_groups, st), "routed gate_up launch");
@@ -530,6 +533,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
     s1.out = ws + L.sh_h;
     if (hilo) s1.out_lo = sh_h_lo;
     s1.limit = c.swiglu_limit;
+    s1.act = c.activation;
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, true, st), "profile event");
     if (af == W_F32) {
       HIP_TRY(launch_gate_up_f32(s1, 1, st), "shared gate_up launch");
@@ -720,6 +724,7 @@ MOE_API int moe_ffn_backward(const moe_config *cfg, const void *x, const moe_wei
   a.norm = c.norm_topk_prob;
   a.score_fn = c.score_fn;
   a.limit = c.swiglu_limit;
+  a.act = c.activation;
   a.route_scale = c.route_scale;
   a.x = x; a.dout = dout; a.gate_w = wt->gate_w; a.w_gate_up = wt->w_gate_up; a.w_down = wt->w_down;
   a.b_gate_up = wt->b_gate_up; a.b_down = wt->b_down;

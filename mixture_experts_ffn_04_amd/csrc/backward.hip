@@ -646,7 +646,7 @@ __global__ void rows_weight(BackwardArgs a) {
 // pre [rows, 2I] gets the per-group bias added in place; h [rows, I].
 // group = row_expert[r] (routed) or 0 (shared: one group, no bias).
 __global__ void swiglu_fwd(float *pre, float *h, const int32_t *row_group, const void *bias, int bias_bf16,
-                           int rows, int I, float limit) {
+                           int rows, int I, float limit, int act) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)rows * I) return;
   const size_t r = i / I, j = i - r * I;
@@ -658,25 +658,27 @@ __global__ void swiglu_fwd(float *pre, float *h, const int32_t *row_group, const
     pre[r * 2 * I + j] = g;
     pre[r * 2 * I + I + j] = u;
   }
-  const float gc = fminf(g, limit), uc = fminf(fmaxf(u, -limit), limit);
-  h[i] = gc / (1.f + expf(-gc)) * uc;
+  h[i] = swiglu_exact(g, u, limit, act);
 }
 
 // ---- 5. dpre = SwiGLU'(pre, w * gd) -------------------------------------------
-// silu'(z) = sigma(z) (1 + z (1 - sigma(z))); the clamp cuts the gradient
-// where it binds (it passes on the boundary itself).
+// With s = sigma(a g') (a = 1, or 1.702 for swigluoai): d/dg' (g' s) =
+// s (1 + a g' (1 - s)), times u' (or u' + 1); d/du' = g' s.  The clamp cuts
+// the gradient where it binds (it passes on the boundary itself).
 __global__ void swiglu_bwd(const float *pre, const float *gd, const float *row_scale, float *dpre, int rows, int I,
-                           float limit) {
+                           float limit, int act) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)rows * I) return;
   const size_t r = i / I, j = i - r * I;
   const float g = pre[r * 2 * I + j], u = pre[r * 2 * I + I + j];
   const float dh = (row_scale ? row_scale[r] : 1.f) * gd[i];
   const float gc = fminf(g, limit), uc = fminf(fmaxf(u, -limit), limit);
-  const float sg = 1.f / (1.f + expf(-gc));
-  const float silu = gc * sg, dsilu = sg * (1.f + gc * (1.f - sg));
-  dpre[r * 2 * I + j] = g <= limit ? dh * uc * dsilu : 0.f;
-  dpre[r * 2 * I + I + j] = (u >= -limit && u <= limit) ? dh * silu : 0.f;
+  const float al = act ? kOaiAlpha : 1.f;
+  const float sg = 1.f / (1.f + expf(-al * gc));
+  const float glu = gc * sg, dglu = sg * (1.f + al * gc * (1.f - sg));
+  const float lin = act ? uc + 1.f : uc;
+  dpre[r * 2 * I + j] = g <= limit ? dh * lin * dglu : 0.f;
+  dpre[r * 2 * I + I + j] = (u >= -limit && u <= limit) ? dh * glu : 0.f;
 }
 
 // Row dot products, one wavefront per row, lanes strided then a fixed
@@ -1007,14 +1009,14 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   // 3. pre = x_rows Wgu^T, h = SwiGLU(pre + b)
   BW_TRY(expert_gemm(g1, rows, skinny, a.part, st));
   hipLaunchKernelGGL(swiglu_fwd, dim3(blocks((size_t)rows * I, 256)), dim3(256), 0, st, a.pre, a.hact, a.row_expert,
-                     a.b_gate_up, ab ? 1 : 0, rows, I, lim);
+                     a.b_gate_up, ab ? 1 : 0, rows, I, lim, a.act);
   // 4. gd = dout_rows Wd
   BW_TRY(expert_gemm(g2, rows, skinny, a.part, st));
   // 5. dweights (slot order) and dpre
   hipLaunchKernelGGL(row_dots, dim3(blocks(rows, 4)), dim3(256), 0, st, a.gd, a.hact, rows, I, a.dout, ab ? 1 : 0,
                      a.row_token, a.row_expert, a.b_down, ab ? 1 : 0, H, a.dweights, a.row_slot);
   hipLaunchKernelGGL(swiglu_bwd, dim3(blocks((size_t)rows * I, 256)), dim3(256), 0, st, a.pre, a.gd, a.row_w, a.dpre,
-                     rows, I, lim);
+                     rows, I, lim, a.act);
   BW_TRY(hipGetLastError());
   // 6. dx_rows = dpre Wgu; dWd = sum_r (w dout)^T h; dWgu = sum_r dpre^T x
   BW_TRY(expert_gemm(g3, rows, skinny, a.part, st));
@@ -1042,7 +1044,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     s.C = a.pre_s; s.ldc = 2 * Is; s.N = 2 * Is; s.K = H;
     BW_TRY(gemm(s, (T + kBT - 1) / kBT, st));
     hipLaunchKernelGGL(swiglu_fwd, dim3(blocks((size_t)T * Is, 256)), dim3(256), 0, st, a.pre_s, a.hact_s,
-                       (const int32_t *)nullptr, (const void *)nullptr, 0, T, Is, lim);
+                       (const int32_t *)nullptr, (const void *)nullptr, 0, T, Is, lim, a.act);
     s.A = op(a.dout, ab, false, H);
     s.B = op(a.sh_down, ab, true, Is);
     s.C = a.gd_s; s.ldc = Is; s.N = Is; s.K = H;
@@ -1058,7 +1060,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
       gam = a.gamma;
     }
     hipLaunchKernelGGL(swiglu_bwd, dim3(blocks((size_t)T * Is, 256)), dim3(256), 0, st, a.pre_s, a.gd_s, gam, a.dpre_s,
-                       T, Is, lim);
+                       T, Is, lim, a.act);
     s.A = op(a.dpre_s, false, false, 2 * Is);
     s.B = op(a.sh_gate_up, ab, true, H);
     s.C = a.dx_sh; s.ldc = H; s.N = H; s.K = 2 * Is;

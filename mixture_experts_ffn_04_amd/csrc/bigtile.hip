@@ -145,7 +145,7 @@ __device__ __forceinline__ void big_epilogue_gate_up(const ExpertGemmArgs &a, co
         float h[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          h[q] = swiglu_fast(acc[mf][p][4 * j + q] + gb[q], acc[mf][p + 2][4 * j + q] + ub[q], a.limit);
+          h[q] = swiglu_fast(acc[mf][p][4 * j + q] + gb[q], acc[mf][p + 2][4 * j + q] + ub[q], a.limit, a.act);
         const uint32_t h01 = pack_bf16x2(h[0], h[1]), h23 = pack_bf16x2(h[2], h[3]);
         const int off = (mf * 32 + l32) * kEpiPitch + cl * 2;
         *reinterpret_cast<uint2 *>(hi_s + off) = make_uint2(h01, h23);

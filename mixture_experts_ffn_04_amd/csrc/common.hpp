@@ -44,16 +44,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// silu(min(g, L)) * clamp(u, -L, L) with the hardware's exp2 and reciprocal
-// approximations (about 1 ulp each, so a few ulp of f32 on the result: far
-// below the bf16 rounding that follows).  Large |g| behaves as the exact
-// form: exp2 overflows to inf and the reciprocal to 0 (silu -> -0), or
-// underflows to 0 (silu -> g).
-__device__ __forceinline__ float swiglu_fast(float g, float u, float lim) {
+// The experts' SwiGLU on the clamped pre-activations g' = min(g, L),
+// u' = clamp(u, -L, L):
+//   act 0 (clamped SwiGLU): silu(g') * u'
+//   act 1 (gpt-oss's swigluoai, as published with gpt-oss): g' sigmoid(1.702 g') (u' + 1)
+// [SGL48763] DraftMLP commit note (silu, the clamped SwiGLU, swigluoai);
+// [SF1073] DeepSeek-V4 family commit note (the clamp).
+constexpr float kOaiAlpha = 1.702f;
+
+// With the hardware's exp2 and reciprocal approximations (about 1 ulp each,
+// so a few ulp of f32 on the result: far below the bf16 rounding that
+// follows).  Large |g| behaves as the exact form: exp2 overflows to inf and
+// the reciprocal to 0 (-> -0), or underflows to 0 (-> g).  For act 0 the
+// scale factor is exactly -log2(e).
+__device__ __forceinline__ float swiglu_fast(float g, float u, float lim, int act) {
   g = fminf(g, lim);
   u = fminf(fmaxf(u, -lim), lim);
-  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-  return g * __builtin_amdgcn_rcpf(1.f + e) * u;
+  const float k = act ? kOaiAlpha * -1.4426950408889634f : -1.4426950408889634f;
+  const float e = __builtin_amdgcn_exp2f(g * k);
+  return g * __builtin_amdgcn_rcpf(1.f + e) * (act ? u + 1.f : u);
+}
+
+// The same with the library expf and an IEEE division.
+__device__ __forceinline__ float swiglu_exact(float g, float u, float lim, int act) {
+  g = fminf(g, lim);
+  u = fminf(fmaxf(u, -lim), lim);
+  return g / (1.f + expf(act ? -kOaiAlpha * g : -g)) * (act ? u + 1.f : u);
 }
 
 // ---------------------------------------------------------------------------
@@ -215,6 +231,7 @@ struct ExpertGemmArgs {
   void *out;                // gate_up: h [rows, N] act dtype; down: y [rows, N] f32
   void *out_lo;             // gate_up with bf16 h: bf16(h - hi) [rows, N]; or null
   float limit;              // SwiGLU clamp (+inf = none)
+  int act;                  // SwiGLU kind (moe_activation): 0 silu(g) u, 1 g sigmoid(1.702 g) (u + 1)
   // down only: write out[token] = weight * y (bf16) instead of y; valid when
   // every token has one expert and there is no shared expert
   void *direct_out;
@@ -258,6 +275,7 @@ struct GradPtrs {
 struct BackwardArgs {
   int T, K, E, H, I, Is;
   int act_bf16, w_bf16, norm, score_fn;
+  int act;  // SwiGLU kind (moe_activation)
   float limit, route_scale;
   const void *x, *dout, *gate_w, *w_gate_up, *w_down, *b_gate_up, *b_down, *sh_gate_up, *sh_down, *sh_gate;
   const float *scores;

@@ -23,12 +23,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ float swiglu_clamped(float g, float u, float lim) {
-  g = fminf(g, lim);
-  u = fminf(fmaxf(u, -lim), lim);
-  return g / (1.f + expf(-g)) * u;
-}
-
 struct GroupInfo {
   int g, nrows, row0;
 };
@@ -75,7 +69,7 @@ __global__ __launch_bounds__(256) void gate_up_f32(ExpertGemmArgs a) {
       g = fmaf(x[k], wg[k], g);
       u = fmaf(x[k], wu[k], u);
     }
-    static_cast<float *>(a.out)[(size_t)(G.row0 + r) * a.N + j] = swiglu_clamped(g + gb, u + ub, a.limit);
+    static_cast<float *>(a.out)[(size_t)(G.row0 + r) * a.N + j] = swiglu_exact(g + gb, u + ub, a.limit, a.act);
   }
 }
 

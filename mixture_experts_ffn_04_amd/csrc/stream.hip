@@ -77,12 +77,6 @@ __device__ __forceinline__ int unit16(int row, int ch) { return row * 16 + (ch ^
 __device__ __forceinline__ int unit32(int row, int ch) { return row * 32 + (ch ^ (row & 15)); }  // 32 chunks/row
 __device__ __forceinline__ int unit8(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }  // 8 chunks/row
 
-__device__ __forceinline__ float swiglu_clamped(float g, float u, float lim) {
-  g = fminf(g, lim);
-  u = fminf(fmaxf(u, -lim), lim);
-  return g / (1.f + expf(-g)) * u;
-}
-
 struct Chunk {
   int g, row0, nrows;  // expert (group), first row in expert-sorted order, rows
   int first, count;    // the expert's chunks: index of the first, how many
@@ -442,7 +436,7 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
               uint32_t hb[4], lb[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const float hv = swiglu_clamped(v[c2][q] + gb[q], v[NS / 2 + c2][q] + ub[q], a.limit);
+                const float hv = swiglu_exact(v[c2][q] + gb[q], v[NS / 2 + c2][q] + ub[q], a.limit, a.act);
                 hb[q] = f32_to_bf16(hv);
                 lb[q] = f32_to_bf16(hv - bf16_to_f32(hb[q]));  // h = hi + lo to ~16 bits
               }

@@ -315,7 +315,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
           }
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = swiglu_fast(acc[cf][tf][q] + gb[q], acc[cf + 4][tf][q] + ub[q], a.limit);
+          for (int q = 0; q < 4; ++q) hv[q] = swiglu_fast(acc[cf][tf][q] + gb[q], acc[cf + 4][tf][q] + ub[q], a.limit, a.act);
           const uint32_t h01 = pack_bf16x2(hv[0], hv[1]), h23 = pack_bf16x2(hv[2], hv[3]);
           const size_t off = (size_t)(c.row0 + row) * a.N + col;
           *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) = make_uint2(h01, h23);

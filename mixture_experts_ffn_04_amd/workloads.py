@@ -181,6 +181,7 @@ class Workload:
     norm_topk_prob: bool = True
     route_scale: float = 1.0
     swiglu_limit: float = math.inf
+    activation: str = "swiglu"         # "swiglu" | "swiglu_oai" (gpt-oss's swigluoai)
     shared_I: int = 0
     shared_gated: bool = False
     x_std: float = 1.0
@@ -230,9 +231,11 @@ def _c4(T=72, score_fn="sigmoid"):
                     expert_bias_std=0.05)
 
 
-def _c5(T=72):
-    return Workload("gpt_oss_style_mxfp4_e32_top4", T=T, H=2880, E=32, I=2880, K=4,
-                    w_dtype="mxfp4", swiglu_limit=7.0, expert_linear_bias_std=0.02)
+def _c5(T=72, activation="swiglu"):
+    # activation "swiglu_oai": the same experts with gpt-oss's own activation
+    name = "gpt_oss_style_mxfp4_e32_top4" + ("_oai" if activation == "swiglu_oai" else "")
+    return Workload(name, T=T, H=2880, E=32, I=2880, K=4, w_dtype="mxfp4", swiglu_limit=7.0,
+                    activation=activation, expert_linear_bias_std=0.02)
 
 
 WORKLOADS = {
@@ -255,6 +258,8 @@ FULL_CASES = [
     ("deepseek_v4_style", {"T": 72, "score_fn": "sqrtsoftplus"}),
     ("deepseek_v4_style", {"T": 4096, "score_fn": "sqrtsoftplus"}),
     ("gpt_oss_style_mxfp4", {"T": 72}), ("gpt_oss_style_mxfp4", {"T": 2048}),
+    ("gpt_oss_style_mxfp4", {"T": 72, "activation": "swiglu_oai"}),
+    ("gpt_oss_style_mxfp4", {"T": 2048, "activation": "swiglu_oai"}),
 ]
 
 

@@ -112,12 +112,12 @@ class Case:
                              norm_topk_prob=wl.norm_topk_prob, route_scale=wl.route_scale,
                              expert_bias=self.bias(self.lw.expert_bias),
                              router_bias=self.bias(self.lw.router_bias), limit=wl.swiglu_limit,
-                             sh_gate_up64=shg, sh_down64=shd, sh_gate64=shgate)
+                             sh_gate_up64=shg, sh_down64=shd, sh_gate64=shgate, activation=wl.activation)
 
     def oracle_token(self, t, indices_row, weights_row):
         shg, shd, shgate = self.shared64()
         return O.token_output(self.x64()[t], indices_row, weights_row, self.expert,
-                              self.wl.swiglu_limit, shg, shd, shgate)
+                              self.wl.swiglu_limit, shg, shd, shgate, activation=self.wl.activation)
 
 
 def check_routing(case: Case, o: O.RouteResult, g: api.Routing, report: dict):

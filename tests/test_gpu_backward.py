@@ -36,6 +36,9 @@ CASES = [
     Wl("bwd_f32", T=64, H=256, E=8, I=128, K=2, act_dtype="f32", w_dtype="f32", shared_I=64),
     Wl("bwd_many_rows_t300", T=300, H=96, E=6, I=160, K=2, shared_I=32, shared_gated=True),
     Wl("bwd_t1", T=1, H=64, E=4, I=32, K=2),
+    # gpt-oss's swigluoai with an active clamp, routed and shared
+    Wl("bwd_swiglu_oai", T=70, H=128, E=16, I=64, K=4, activation="swiglu_oai", swiglu_limit=0.4,
+       shared_I=96, shared_gated=True, expert_linear_bias_std=0.02, w_std=0.1),
     # few rows per expert with a long reduction: split into chunks (a ragged
     # last chunk and ragged column tiles)
     Wl("bwd_split_ragged", T=40, H=992, E=4, I=224, K=2, shared_I=96, shared_gated=True),
@@ -81,7 +84,7 @@ def test_backward_matches_oracle(wl):
         x64, c.gate64(), c.expert, O.to_f64(host(dout), wl.act_dtype), n_experts=wl.E, k=wl.K,
         score_fn=wl.score_fn, n_group=wl.n_group, topk_group=wl.topk_group,
         norm_topk_prob=wl.norm_topk_prob, route_scale=wl.route_scale,
-        expert_bias=c.bias(c.lw.expert_bias), router_bias=c.bias(c.lw.router_bias), limit=wl.swiglu_limit,
+        expert_bias=c.bias(c.lw.expert_bias), router_bias=c.bias(c.lw.router_bias), limit=wl.swiglu_limit, activation=wl.activation,
         sh_gate_up64=sh_gu, sh_down64=sh_d, sh_gate64=sh_g)
     oi = c.oracle_route().indices
     assert np.array_equal(host(r.indices), oi), "selection differs from the oracle's"

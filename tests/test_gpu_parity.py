@@ -85,6 +85,22 @@ SMALL = [
     # keeps the output's own bf16 rounding near 1.4% of RMS, clear of the bar
     Wl("big_bf16_fragments_t1300", T=1300, H=256, E=4, I=256, K=1),
     Wl("big_bf16_fragments_t1700", T=1700, H=256, E=4, I=256, K=1),
+    # gpt-oss's swigluoai on every GEMM path (streaming bf16 and MXFP4 with
+    # the shared expert, tiled, big tile, f32) with an active clamp
+    Wl("oai_stream_shared", T=72, H=384, E=32, I=160, K=4, swiglu_limit=7.0, activation="swiglu_oai",
+       shared_I=128, shared_gated=True, expert_linear_bias_std=0.02, w_std=0.15),
+    Wl("oai_stream_mxfp4", T=72, H=352, E=32, I=288, K=4, w_dtype="mxfp4", swiglu_limit=7.0,
+       activation="swiglu_oai", expert_linear_bias_std=0.02),
+    Wl("oai_tiled_t600", T=600, H=384, E=8, I=160, K=2, shared_I=96, activation="swiglu_oai",
+       swiglu_limit=7.0, w_std=0.1),
+    Wl("oai_tiled_mxfp4_t520", T=520, H=352, E=8, I=288, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
+       activation="swiglu_oai", expert_linear_bias_std=0.02),
+    Wl("oai_big_t1100", T=1100, H=352, E=4, I=160, K=1, shared_I=96, shared_gated=True,
+       activation="swiglu_oai", swiglu_limit=7.0),
+    Wl("oai_big_mxfp4_t1030", T=1030, H=352, E=4, I=288, K=1, w_dtype="mxfp4", swiglu_limit=7.0,
+       activation="swiglu_oai", expert_linear_bias_std=0.02),
+    Wl("oai_f32", T=64, H=256, E=8, I=128, K=2, act_dtype="f32", w_dtype="f32", activation="swiglu_oai",
+       swiglu_limit=7.0, w_std=0.3, shared_I=64),
     # tiled router logits (>= 256 tokens, >= 64 columns): partial column and
     # token tiles, a 96-element hidden tail, the shared-gate column
     Wl("router_tiled_t300", T=300, H=352, E=96, I=64, K=6, shared_I=64, shared_gated=True,

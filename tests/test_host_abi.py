@@ -67,7 +67,7 @@ int main(void) {
   F(moe_config, act_dtype) F(moe_config, w_dtype) F(moe_config, score_fn)
   F(moe_config, n_group) F(moe_config, topk_group) F(moe_config, norm_topk_prob)
   F(moe_config, route_scale) F(moe_config, swiglu_limit) F(moe_config, shared_I)
-  F(moe_config, shared_gated)
+  F(moe_config, shared_gated) F(moe_config, activation)
   F(moe_weights, gate_w) F(moe_weights, router_bias) F(moe_weights, expert_bias)
   F(moe_weights, w_gate_up) F(moe_weights, w_down) F(moe_weights, w_gate_up_scale)
   F(moe_weights, w_down_scale) F(moe_weights, b_gate_up) F(moe_weights, b_down)
@@ -76,9 +76,9 @@ int main(void) {
   F(moe_grads, dx) F(moe_grads, dgate) F(moe_grads, drouter_bias) F(moe_grads, dw_gate_up)
   F(moe_grads, dw_down) F(moe_grads, db_gate_up) F(moe_grads, db_down) F(moe_grads, dsh_gate_up)
   F(moe_grads, dsh_down) F(moe_grads, dsh_gate)
-  printf("enum %d %d %d %d %d %d %d %d %d %d %d\n", MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4,
+  printf("enum %d %d %d %d %d %d %d %d %d %d %d %d %d\n", MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4,
          MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID, MOE_SCORE_SQRTSOFTPLUS, MOE_OK, MOE_ERR_INVALID,
-         MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP);
+         MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ACT_SWIGLU, MOE_ACT_SWIGLU_OAI);
   return 0;
 }
 ''')
@@ -101,7 +101,7 @@ int main(void) {
                  if l.startswith("enum")][0]
     assert [int(v) for v in enum_line.split()[1:]] == [
         0, 1, 2, 0, 1, 2, _lib.MOE_OK, _lib.MOE_ERR_INVALID, _lib.MOE_ERR_UNSUPPORTED,
-        _lib.MOE_ERR_WORKSPACE, _lib.MOE_ERR_HIP]
+        _lib.MOE_ERR_WORKSPACE, _lib.MOE_ERR_HIP, _lib.MOE_ACT["swiglu"], _lib.MOE_ACT["swiglu_oai"]]
 
 
 def cfg(**kw):
@@ -147,7 +147,7 @@ def test_validate_refusals(L, kw, code):
 
 def test_bad_enum_values(L):
     for field, val in (("act_dtype", 7), ("w_dtype", 9), ("score_fn", 3), ("norm_topk_prob", 2),
-                       ("shared_gated", 5)):
+                       ("shared_gated", 5), ("activation", 2), ("activation", -1)):
         c = cfg()
         setattr(c, field, val)
         assert status(L, c) == -1, field
