@@ -9,7 +9,7 @@
 // the weights; clamped SwiGLU; the V4.1 port's output and every gradient are
 // compared.  [SGL48763] = sglang PR #48763: sigmoid-gated shared expert.
 //
-// Plan (the forward in reverse; every step fp32, bf16 inputs widened exactly):
+// Plan (the forward in reverse; fp32 arithmetic, bf16 inputs widened exactly):
 //   1. stable permutation: rows of each expert in slot order (so every sum
 //      over an expert's rows has a fixed order), row -> token, row -> weight
 //   2. routing weights per slot from the forward's scores (as the forward)
@@ -22,14 +22,17 @@
 //   8. router: d weights -> d scores (renormalisation) -> d logits (score
 //      function) -> dgate = dl^T x, drouter_bias = sum_t dl, dx += dl gate
 //   9. dx = sum_k dx_rows (k order) + shared + router + gate terms
-// One generic grouped GEMM (64 x 64 f32 tiles staged in LDS, fixed k order
-// per output) serves every contraction through operand descriptors.  The
-// three expert products, when experts hold few rows, run instead on the fp32
+// One generic grouped GEMM on the bf16 matrix cores (128 x 128 tiles staged
+// in LDS, fixed k order per output) serves every contraction through operand
+// descriptors; fp32 operands enter as exact pairs of bf16 numbers (hi + lo),
+// so the products carry at most a few 2^-18 of relative error.  The three
+// expert products, when experts hold few rows, run instead on the fp32
 // matrix cores in 16-row tiles of one wave that read their operands straight
 // from memory, with the reduction split into fixed chunks whose partial
 // results a separate pass sums in chunk order, so the result does not depend
 // on scheduling.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -37,8 +40,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kBT = 64;       // output tile columns; rows of the large tile
-constexpr int kBK = 32;       // reduction slice of the large tiles
 constexpr int kSkinnyRows = 16;
 
 // expert ids index memory: keep them in range whatever the caller passed
@@ -150,140 +151,50 @@ struct Runs {
   }
 };
 
-// Tile TM x 64 with TM * 4 threads, reduction slices of KB; each thread owns
-// 4 x 4 outputs.  AF and BF give each operand's format: bit 0 kmajor, bit 1
-// bf16.
-template <int TM, int KB, int AF, int BF, bool VEC>
-__device__ __forceinline__ void gemm_tile(const GGemm &g, int grp, int m0, int n0, int M, int K, int r0,
-                                          float (&As)[KB][TM + 4], float (&Bs)[KB][kBT + 4]) {
-  constexpr int AK = AF & 1, BK = BF & 1;
-  constexpr int NT = TM * 4;
-  constexpr int NA = TM * KB / 8 / NT, NB = kBT * KB / 8 / NT;  // 8-element runs per thread and slice
-  static_assert(NA * NT * 8 == TM * KB && NB * NT * 8 == kBT * KB, "whole runs per thread");
-  const int tid = threadIdx.x;
-  const int kbeg = blockIdx.z * g.kchunk;
-  const int kend = g.ksplit > 1 ? min(K, kbeg + g.kchunk) : K;
-  const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][4] = {};
-  // Run idx (thread tid, then tid + NT, ...) of an operand with `rows` rows
-  // per tile: (row idx / (KB / 8), k (idx % (KB / 8)) * 8) when row-major,
-  // (row (idx % (rows / 8)) * 8, k idx / (rows / 8)) when k-major.
-  auto place = [](int idx, int rows, bool kmajor, int &i, int &k) {
-    i = kmajor ? (idx % (rows / 8)) * 8 : idx / (KB / 8);
-    k = kmajor ? idx / (rows / 8) : (idx % (KB / 8)) * 8;
-  };
-  int ai[NA], ak[NA], bi[NB], bk[NB];
-#pragma unroll
-  for (int u = 0; u < NA; ++u) place(tid + u * NT, TM, AK, ai[u], ak[u]);
-#pragma unroll
-  for (int u = 0; u < NB; ++u) place(tid + u * NT, kBT, BK, bi[u], bk[u]);
-  using RA = Runs<AK, (AF >> 1), VEC>;
-  using RB = Runs<BK, (BF >> 1), VEC>;
-  RA ra_[NA];
-  RB rb_[NB];
-  // rows of row-major operands do not move with k: resolve them once
-  if constexpr (!AK) {
-#pragma unroll
-    for (int u = 0; u < NA; ++u) ra_[u].set_row(g.A, m0 + ai[u], M, grp, r0);
-  }
-  if constexpr (!BK) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) rb_[u].set_row(g.B, n0 + bi[u], g.N, grp, r0);
-  }
-  typename RA::Raw ra[NA];
-  typename RB::Raw rb[NB];
-  auto load = [&](int k0) {
-    if constexpr (AK) {
-#pragma unroll
-      for (int u = 0; u < NA; ++u) ra_[u].set_row(g.A, k0 + ak[u], kend, grp, r0);
-    }
-    if constexpr (BK) {
-#pragma unroll
-      for (int u = 0; u < NB; ++u) rb_[u].set_row(g.B, k0 + bk[u], kend, grp, r0);
-    }
-#pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      if constexpr (AK) ra_[u].issue(g.A, m0 + ai[u], M, ra[u]);
-      else ra_[u].issue(g.A, k0 + ak[u], kend, ra[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      if constexpr (BK) rb_[u].issue(g.B, n0 + bi[u], g.N, rb[u]);
-      else rb_[u].issue(g.B, k0 + bk[u], kend, rb[u]);
-    }
-  };
-  auto step = [&](int kk) {
-    float a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-  };
-  if (kbeg < kend) load(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += KB) {
-#pragma unroll
-    for (int u = 0; u < NA; ++u) {
-      float v[8];
-      RA::finish(ra[u], v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (AK) As[ak[u]][ai[u] + q] = v[q];
-        else As[ak[u] + q][ai[u]] = v[q];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      float v[8];
-      RB::finish(rb[u], v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (BK) Bs[bk[u]][bi[u] + q] = v[q];
-        else Bs[bk[u] + q][bi[u]] = v[q];
-      }
-    }
-    __syncthreads();
-    if (k0 + KB < kend) load(k0 + KB);
-    if (k0 + KB <= kend) {
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) step(kk);
-    } else {
-      // the last, partial slice: the steps past the end would add 0 * 0
-      for (int kk = 0; kk < kend - k0; ++kk) step(kk);
-    }
-    __syncthreads();
-  }
-  float *C = g.C + (g.mode == 2 ? (size_t)grp * g.cgstride : 0) + (size_t)blockIdx.z * g.split_stride;
-  const int nb = n0 + tx * 4;
-  const bool vec = g.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0 && nb + 4 <= g.N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
-    if (m >= M) continue;
-    float *row = C + (g.mode == 1 ? (size_t)(r0 + m) : (size_t)m) * g.ldc;
-    if (vec) {
-      const f32x4_t v{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-      // weight gradients are written once and not read back here: stream them
-      if (g.mode == 2) __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(row + nb));
-      else *reinterpret_cast<f32x4_t *>(row + nb) = v;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (nb + j < g.N) row[nb + j] = acc[i][j];
-    }
-  }
+// ---- contractions on the bf16 matrix cores ----------------------------------
+// C[m, n] = sum_k A(m, k) B(n, k) with v_mfma_f32_32x32x16_bf16: bf16 operand
+// products are exact in fp32 and summed in fp32.  An operand that is bf16 in
+// memory (and not scaled) enters as it is; an fp32 (or scaled) operand v is
+// split into two bf16 numbers hi = rne(v), lo = rne(v - hi), which hold v to
+// 2^-18 of its size, and the product takes the passes hi.hi, lo.hi (A split),
+// hi.lo (B split); the lo.lo term (2^-18 of the product) is dropped.  So each
+// product carries a relative error of a few 2^-18 at most, far below the
+// rounding of the fp32 sums over the reduction.
+//
+// Tile 128 x 128 with 256 threads; four waves of 64 x 64 (2 x 2 fragments of
+// 32 x 32); 32-deep reduction slices staged in LDS as bf16 planes (hi, and lo
+// for a split operand) of [row][k] with an XOR swizzle of the 16-byte chunks
+// (row r, chunk c at r * 4 + (c ^ (r / 4) % 4)), so the 32 rows of a fragment
+// read and the 16 rows of a row-major store hit distinct banks.  The next
+// slice's global loads are in flight while the current slice is multiplied.
+constexpr int kMT = 128;  // output tile rows and columns of the matrix-core kernel
+constexpr int kMK = 32;   // reduction slice
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16v mfma32(u32x4_t a, u32x4_t b, f32x16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b), c,
+                                                 0, 0, 0);
 }
 
-template <int TM, int AF, int BF>
-__global__ __launch_bounds__(TM * 4) void grouped_gemm_f32(GGemm g) {
-  constexpr int KB = kBK;
+__device__ __forceinline__ int munit(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
+
+template <int AF, int BF, bool VEC>
+__global__ __launch_bounds__(256) void grouped_gemm_mfma(GGemm g) {
+  constexpr int AK = AF & 1, BK = BF & 1;
+  constexpr int NT = 256;
+  constexpr int NR = kMT * kMK / 8 / NT;  // 8-element runs per thread, operand and slice (2)
+  constexpr int PU = kMT * 4;             // 16-byte units of one plane
+  // LDS planes: A hi, A lo, B hi, B lo
+  __shared__ u32x4_t lds[4 * PU];
+  u32x4_t *Ah = lds, *Al = lds + PU, *Bh = lds + 2 * PU, *Bl = lds + 3 * PU;
+  const bool asplit = !(AF >> 1) || g.A.scale, bsplit = !(BF >> 1) || g.B.scale;
+
   int grp = 0, m0, M, K, r0 = 0;
-  const int n0 = blockIdx.x * kBT;
+  const int n0 = blockIdx.x * kMT;
   if (g.mode == 0) {
-    m0 = blockIdx.y * TM;
+    m0 = blockIdx.y * kMT;
     M = g.M;
     K = g.K;
   } else if (g.mode == 1) {
@@ -296,22 +207,202 @@ __global__ __launch_bounds__(TM * 4) void grouped_gemm_f32(GGemm g) {
       else hi = mid;
     }
     grp = lo;
-    m0 = (q - g.mtile_prefix[lo]) * TM;
+    m0 = (q - g.mtile_prefix[lo]) * kMT;
     M = g.counts[lo];
     K = g.K;
     r0 = g.offsets[lo];
   } else {
-    const int mtiles = (g.M + TM - 1) / TM;
+    const int mtiles = (g.M + kMT - 1) / kMT;
     grp = blockIdx.y / mtiles;
-    m0 = (blockIdx.y - grp * mtiles) * TM;
+    m0 = (blockIdx.y - grp * mtiles) * kMT;
     M = g.M;
     K = g.counts[grp];
     r0 = g.offsets[grp];
   }
   if (m0 >= M || n0 >= g.N) return;  // whole workgroup leaves together
-  __shared__ float As[KB][TM + 4], Bs[KB][kBT + 4];
-  if (g.vec) gemm_tile<TM, KB, AF, BF, true>(g, grp, m0, n0, M, K, r0, As, Bs);
-  else gemm_tile<TM, KB, AF, BF, false>(g, grp, m0, n0, M, K, r0, As, Bs);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  // Run u of a thread: row-major operand: row (tid + 256 u) / 4, chunk
+  // tid % 4; k-major operand: 8 rows from (tid % 16) * 8 at k = 2 (tid / 16) + u,
+  // so a thread's two runs pair up k and k + 1 for each row (4-byte stores).
+  auto place = [&](int u, bool kmajor, int &i, int &k) {
+    if (kmajor) {
+      i = (tid & 15) * 8;
+      k = 2 * (tid >> 4) + u;
+    } else {
+      i = (tid + NT * u) >> 2;
+      k = (tid & 3) * 8;
+    }
+  };
+  int ai[NR], ak[NR], bi[NR], bk[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    place(u, AK, ai[u], ak[u]);
+    place(u, BK, bi[u], bk[u]);
+  }
+  using RA = Runs<AK, (AF >> 1), VEC>;
+  using RB = Runs<BK, (BF >> 1), VEC>;
+  RA ra_[NR];
+  RB rb_[NR];
+  if constexpr (!AK) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) ra_[u].set_row(g.A, m0 + ai[u], M, grp, r0);
+  }
+  if constexpr (!BK) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) rb_[u].set_row(g.B, n0 + bi[u], g.N, grp, r0);
+  }
+  typename RA::Raw ra[NR];
+  typename RB::Raw rb[NR];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      if constexpr (AK) {
+        ra_[u].set_row(g.A, k0 + ak[u], K, grp, r0);
+        ra_[u].issue(g.A, m0 + ai[u], M, ra[u]);
+      } else {
+        ra_[u].issue(g.A, k0 + ak[u], K, ra[u]);
+      }
+      if constexpr (BK) {
+        rb_[u].set_row(g.B, k0 + bk[u], K, grp, r0);
+        rb_[u].issue(g.B, n0 + bi[u], g.N, rb[u]);
+      } else {
+        rb_[u].issue(g.B, k0 + bk[u], K, rb[u]);
+      }
+    }
+  };
+  // One operand's runs of a slice -> its LDS planes.  Exact bf16 operands
+  // (stored as bf16, not scaled, whole 16-byte runs) go in as their raw
+  // words; the others are split into (hi, lo) pairs with the paired
+  // conversion (round to nearest even).  k-major runs pair up k and k + 1
+  // for each row (one 4-byte store per row and plane); row-major runs are
+  // one row's 8 consecutive k (one 16-byte store per plane).
+  auto stash = [&](auto R, auto vecbf, const auto (&raw)[NR], const int (&ri)[NR], const int (&rk)[NR],
+                   bool kmajor, bool split, u32x4_t *H, u32x4_t *L) {
+    using RT = decltype(R);
+    if constexpr (decltype(vecbf)::value) {
+      if (!split) {
+        if (kmajor) {
+          const int k = rk[0];
+          const uint32_t m0 = raw[0].on ? 0xffffffffu : 0u, m1 = raw[1].on ? 0xffffffffu : 0u;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            // element q of run k (low half) and of run k + 1 (high half)
+            const uint32_t w0 = raw[0].w[q >> 1] & m0, w1 = raw[1].w[q >> 1] & m1;
+            const uint32_t d = __builtin_amdgcn_perm(w1, w0, q & 1 ? 0x07060302u : 0x05040100u);
+            reinterpret_cast<uint32_t *>(H)[munit(ri[0] + q, k >> 3) * 4 + ((k & 7) >> 1)] = d;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < NR; ++u) {
+            const uint32_t m = raw[u].on ? 0xffffffffu : 0u;
+            H[munit(ri[u], rk[u] >> 3)] =
+                u32x4_t{raw[u].w[0] & m, raw[u].w[1] & m, raw[u].w[2] & m, raw[u].w[3] & m};
+          }
+        }
+        return;
+      }
+    }
+    float v[NR][8];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) RT::finish(raw[u], v[u]);
+    // (a, b) -> packed bf16 hi pair and lo pair, hi + lo = (a, b) to 2^-18
+    auto split2 = [](float a, float b, uint32_t &hp, uint32_t &lp) {
+      hp = pack_bf16x2(a, b);
+      lp = pack_bf16x2(a - bf16_lo(hp), b - bf16_hi(hp));
+    };
+    if (kmajor) {
+      const int k = rk[0];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uint32_t hp, lp;
+        split2(v[0][q], v[1][q], hp, lp);
+        const int off = munit(ri[0] + q, k >> 3) * 4 + ((k & 7) >> 1);  // dword within the plane
+        reinterpret_cast<uint32_t *>(H)[off] = hp;
+        if (split) reinterpret_cast<uint32_t *>(L)[off] = lp;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        uint32_t hp[4], lp[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) split2(v[u][2 * q], v[u][2 * q + 1], hp[q], lp[q]);
+        const int un = munit(ri[u], rk[u] >> 3);
+        H[un] = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
+        if (split) L[un] = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
+      }
+    }
+  };
+
+  f32x16v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  if (K > 0) load(0);
+  for (int k0 = 0; k0 < K; k0 += kMK) {
+    stash(RA{}, std::bool_constant<VEC && (AF >> 1)>{}, ra, ai, ak, AK, asplit, Ah, Al);
+    stash(RB{}, std::bool_constant<VEC && (BF >> 1)>{}, rb, bi, bk, BK, bsplit, Bh, Bl);
+    __syncthreads();
+    if (k0 + kMK < K) load(k0 + kMK);
+#pragma unroll
+    for (int kk = 0; kk < kMK / 16; ++kk) {
+      const int ch = 2 * kk + lh;
+      u32x4_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = Ah[munit(wm * 64 + i * 32 + l32, ch)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = Bh[munit(wn * 64 + j * 32 + l32, ch)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      if (asplit) {
+        u32x4_t al[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) al[i] = Al[munit(wm * 64 + i * 32 + l32, ch)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
+      }
+      if (bsplit) {
+        u32x4_t bl[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bl[j] = Bl[munit(wn * 64 + j * 32 + l32, ch)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bl[j], acc[i][j]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // lane l holds column l % 32 of each fragment and rows 8 (e / 4) + 4 (l / 32) + e % 4
+  float *C = g.C + (g.mode == 2 ? (size_t)grp * g.cgstride : 0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + l32;
+    if (n >= g.N) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        if (m >= M) continue;
+        float *dst = C + (g.mode == 1 ? (size_t)(r0 + m) : (size_t)m) * g.ldc + n;
+        // weight gradients are written once and not read back here: stream them
+        if (g.mode == 2) __builtin_nontemporal_store(acc[i][j][e], dst);
+        else *dst = acc[i][j][e];
+      }
+    }
+  }
 }
 
 
@@ -814,22 +905,26 @@ __global__ void dx_combine(BackwardArgs a) {
   a.g.dx[i] = s;
 }
 
-template <int TM, int AF>
+template <int AF, int BF>
+void launch_mfma(const GGemm &g, dim3 grid, hipStream_t st) {
+  if (g.vec) hipLaunchKernelGGL((grouped_gemm_mfma<AF, BF, true>), grid, dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((grouped_gemm_mfma<AF, BF, false>), grid, dim3(256), 0, st, g);
+}
+template <int AF>
 void launch_b(const GGemm &g, dim3 grid, hipStream_t st) {
   switch (g.B.kmajor | g.B.bf16 << 1) {
-    case 0: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 0>), grid, dim3(TM * 4), 0, st, g); break;
-    case 1: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 1>), grid, dim3(TM * 4), 0, st, g); break;
-    case 2: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 2>), grid, dim3(TM * 4), 0, st, g); break;
-    default: hipLaunchKernelGGL((grouped_gemm_f32<TM, AF, 3>), grid, dim3(TM * 4), 0, st, g); break;
+    case 0: launch_mfma<AF, 0>(g, grid, st); break;
+    case 1: launch_mfma<AF, 1>(g, grid, st); break;
+    case 2: launch_mfma<AF, 2>(g, grid, st); break;
+    default: launch_mfma<AF, 3>(g, grid, st); break;
   }
 }
-template <int TM>
 void launch_gemm(const GGemm &g, dim3 grid, hipStream_t st) {
   switch (g.A.kmajor | g.A.bf16 << 1) {
-    case 0: launch_b<TM, 0>(g, grid, st); break;
-    case 1: launch_b<TM, 1>(g, grid, st); break;
-    case 2: launch_b<TM, 2>(g, grid, st); break;
-    default: launch_b<TM, 3>(g, grid, st); break;
+    case 0: launch_b<0>(g, grid, st); break;
+    case 1: launch_b<1>(g, grid, st); break;
+    case 2: launch_b<2>(g, grid, st); break;
+    default: launch_b<3>(g, grid, st); break;
   }
 }
 
@@ -846,12 +941,16 @@ bool vec_runs(const GGemm &g) {
   return one(g.A, g.mode == 1 ? 1 : g.M) && one(g.B, g.N) && (g.ksplit <= 1 || g.kchunk % 8 == 0);
 }
 
-// Large tiles: grid_rows row tiles of kBT rows, no split.
-hipError_t gemm(GGemm g, int grid_rows, hipStream_t st) {
-  if (grid_rows <= 0 || g.N <= 0) return hipSuccess;
+// Large tiles on the matrix cores, no split.  rows: M (mode 0), the rows of
+// all groups together (mode 1), or each group's M (mode 2).
+hipError_t gemm(GGemm g, int rows, hipStream_t st) {
+  if (rows <= 0 || g.N <= 0) return hipSuccess;
   g.ksplit = 1; g.kchunk = 0; g.split_stride = 0;
   g.vec = vec_runs(g) ? 1 : 0;
-  launch_gemm<kBT>(g, dim3((g.N + kBT - 1) / kBT, grid_rows), st);
+  int grid_rows = (rows + kMT - 1) / kMT;
+  if (g.mode == 1) grid_rows += g.E;  // a partial tile per group at most
+  if (g.mode == 2) grid_rows *= g.E;
+  launch_gemm(g, dim3((g.N + kMT - 1) / kMT, grid_rows), st);
   return hipGetLastError();
 }
 
@@ -866,11 +965,11 @@ bool skinny_ok(GGemm g, const float *part) {
 }
 
 // Expert products (mode 1) over `rows` rows.  Skinny: 16-row tiles on the
-// matrix cores, the reduction split as split_plan() says, the chunks' partial
-// products in `part` and summed in chunk order into C.  Otherwise 64-row
-// multiply-add tiles.
+// fp32 matrix cores, the reduction split as split_plan() says, the chunks'
+// partial products in `part` and summed in chunk order into C.  Otherwise
+// 128-row tiles on the bf16 matrix cores.
 hipError_t expert_gemm(GGemm g, int rows, bool skinny, float *part, hipStream_t st) {
-  if (!skinny) return gemm(g, (rows + kBT - 1) / kBT + g.E, st);
+  if (!skinny) return gemm(g, rows, st);
   if (rows <= 0 || g.N <= 0) return hipSuccess;
   g.ksplit = 1;
   g.vec = vec_runs(g) ? 1 : 0;  // 1: skinny_ok() held
@@ -999,7 +1098,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   const bool skinny = skinny_rows(rows, E) && skinny_ok(g1, a.part) && skinny_ok(g2, a.part) && skinny_ok(g3, a.part);
   // 1-2. permutation and weights
   BackwardArgs pa = a;
-  pa.tile_rows = skinny ? kSkinnyRows : kBT;
+  pa.tile_rows = skinny ? kSkinnyRows : kMT;
   hipLaunchKernelGGL(stable_permute, dim3(1), dim3(kPermThreads), (size_t)kPermWaves * E * 4, st, pa);
   BW_TRY(hipGetLastError());
   hipLaunchKernelGGL(slot_weights, dim3(blocks(T, 256)), dim3(256), 0, st, a);
@@ -1025,11 +1124,11 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   w.A = op(a.dout, ab, true, H, 0, true, a.row_token, a.row_w);
   w.B = op(a.hact, false, true, I, 0, true);
   w.C = a.g.dw_down; w.ldc = I; w.cgstride = (long)H * I; w.M = H; w.N = I;
-  BW_TRY(gemm(w, E * ((H + kBT - 1) / kBT), st));
+  BW_TRY(gemm(w, H, st));
   w.A = op(a.dpre, false, true, 2 * I, 0, true);
   w.B = op(a.x, ab, true, H, 0, true, a.row_token);
   w.C = a.g.dw_gate_up; w.ldc = H; w.cgstride = (long)2 * I * H; w.M = 2 * I; w.N = H;
-  BW_TRY(gemm(w, E * ((2 * I + kBT - 1) / kBT), st));
+  BW_TRY(gemm(w, 2 * I, st));
   if (a.g.db_down || a.g.db_gate_up) {
     hipLaunchKernelGGL(bias_grads, dim3(blocks(H + 2 * I, 256), E), dim3(256), 0, st, a);
     BW_TRY(hipGetLastError());
@@ -1042,13 +1141,13 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     s.A = op(a.x, ab, false, H);
     s.B = op(a.sh_gate_up, ab, false, H);
     s.C = a.pre_s; s.ldc = 2 * Is; s.N = 2 * Is; s.K = H;
-    BW_TRY(gemm(s, (T + kBT - 1) / kBT, st));
+    BW_TRY(gemm(s, T, st));
     hipLaunchKernelGGL(swiglu_fwd, dim3(blocks((size_t)T * Is, 256)), dim3(256), 0, st, a.pre_s, a.hact_s,
                        (const int32_t *)nullptr, (const void *)nullptr, 0, T, Is, lim, a.act);
     s.A = op(a.dout, ab, false, H);
     s.B = op(a.sh_down, ab, true, Is);
     s.C = a.gd_s; s.ldc = Is; s.N = Is; s.K = H;
-    BW_TRY(gemm(s, (T + kBT - 1) / kBT, st));
+    BW_TRY(gemm(s, T, st));
     const float *gam = nullptr;
     if (a.sh_gate) {
       hipLaunchKernelGGL(shared_gamma, dim3(blocks(T, 4)), dim3(256), 0, st, a);
@@ -1064,17 +1163,17 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     s.A = op(a.dpre_s, false, false, 2 * Is);
     s.B = op(a.sh_gate_up, ab, true, H);
     s.C = a.dx_sh; s.ldc = H; s.N = H; s.K = 2 * Is;
-    BW_TRY(gemm(s, (T + kBT - 1) / kBT, st));
+    BW_TRY(gemm(s, T, st));
     s.M = H; s.K = T;
     s.A = op(a.dout, ab, true, H, 0, false, nullptr, gam);
     s.B = op(a.hact_s, false, true, Is);
     s.C = a.g.dsh_down; s.ldc = Is; s.N = Is;
-    BW_TRY(gemm(s, (H + kBT - 1) / kBT, st));
+    BW_TRY(gemm(s, H, st));
     s.M = 2 * Is;
     s.A = op(a.dpre_s, false, true, 2 * Is);
     s.B = op(a.x, ab, true, H);
     s.C = a.g.dsh_gate_up; s.ldc = H; s.N = H;
-    BW_TRY(gemm(s, (2 * Is + kBT - 1) / kBT, st));
+    BW_TRY(gemm(s, 2 * Is, st));
     if (a.sh_gate) {
       hipLaunchKernelGGL(gate_grad, dim3(blocks(H, 256)), dim3(256), 0, st, a);
       BW_TRY(hipGetLastError());
@@ -1090,12 +1189,12 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   r.A = op(a.dl, false, true, E);
   r.B = op(a.x, ab, true, H);
   r.C = a.g.dgate; r.ldc = H;
-  BW_TRY(gemm(r, (E + kBT - 1) / kBT, st));
+  BW_TRY(gemm(r, E, st));
   r.M = T; r.N = H; r.K = E;
   r.A = op(a.dl, false, false, E);
   r.B = op(a.gate_w, ab, true, H);
   r.C = a.dx_router; r.ldc = H;
-  BW_TRY(gemm(r, (T + kBT - 1) / kBT, st));
+  BW_TRY(gemm(r, T, st));
   if (a.g.drouter_bias) {
     hipLaunchKernelGGL(column_sums, dim3(blocks(E, 256)), dim3(256), 0, st, a.dl, T, E, a.g.drouter_bias);
     BW_TRY(hipGetLastError());
