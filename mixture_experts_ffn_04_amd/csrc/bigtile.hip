@@ -483,20 +483,6 @@ struct DmaPlan {
   static_assert((NSTAGE - 1) * OPS < 64, "vmcnt range");
 };
 
-__device__ __forceinline__ void dma16(const char *g, u32x4_t *l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
-}
-
-
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Scheduling order of a region with NREAD LDS reads (next step's operands)
 // and NMFMA MFMAs (this step's): an MFMA, then two reads, until every read is
 // issued, then the remaining MFMAs.  The reads go out early, behind a
@@ -527,11 +513,6 @@ __device__ __forceinline__ void interleave_reads_valu() {
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);                       // its share of VALU work
     interleave_reads_valu<NREAD, NMFMA - 1, NVALU - V, I>();
   }
-}
-
-// workgroup barrier that the compiler does not move memory operations across
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace

@@ -34,4 +34,28 @@ __device__ __forceinline__ u32x4_t decode_e2m1x8(uint32_t codes, float scale) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3))};
 }
 
+// --------------------------------------------------------------------------
+// Direct-to-LDS loads
+// --------------------------------------------------------------------------
+
+// 16 bytes per lane from global memory straight into LDS: the wavefront's 64
+// lanes fill 1 KB at `l` (uniform across the wavefront), lane i at l + 16 i.
+// Counted by the vector-memory counter like any other load.
+__device__ __forceinline__ void dma16(const char *g, u32x4_t *l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// workgroup barrier that the compiler does not move memory operations across
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace moe

@@ -91,6 +91,14 @@ SMALL = [
        shared_I=128, shared_gated=True, expert_linear_bias_std=0.02, w_std=0.15),
     Wl("oai_stream_mxfp4", T=72, H=352, E=32, I=288, K=4, w_dtype="mxfp4", swiglu_limit=7.0,
        activation="swiglu_oai", expert_linear_bias_std=0.02),
+    # MXFP4 streaming at larger shapes: ragged last reduction slices (1088 =
+    # 4 x 256 + 64, 704 = 2 x 256 + 192), a down column count that is not a
+    # multiple of the item width, several items per workgroup, experts of two
+    # 16-row chunks, with and without biases
+    Wl("mx_stream_t120", T=120, H=1088, E=64, I=704, K=8, w_dtype="mxfp4", swiglu_limit=7.0,
+       expert_linear_bias_std=0.02),
+    Wl("mx_stream_oai_nobias_t72", T=72, H=1536, E=32, I=1024, K=4, w_dtype="mxfp4", swiglu_limit=7.0,
+       activation="swiglu_oai"),
     Wl("oai_tiled_t600", T=600, H=384, E=8, I=160, K=2, shared_I=96, activation="swiglu_oai",
        swiglu_limit=7.0, w_std=0.1),
     Wl("oai_tiled_mxfp4_t520", T=520, H=352, E=8, I=288, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
