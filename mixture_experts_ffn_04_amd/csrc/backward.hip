@@ -763,7 +763,7 @@ __global__ void swiglu_bwd(const float *pre, const float *gd, const float *row_s
   const size_t r = i / I, j = i - r * I;
   const float g = pre[r * 2 * I + j], u = pre[r * 2 * I + I + j];
   const float dh = (row_scale ? row_scale[r] : 1.f) * gd[i];
-  const float gc = fminf(g, limit), uc = fminf(fmaxf(u, -limit), limit);
+  const float gc = clamp_hi(g, limit), uc = clamp_sym(u, limit);
   const float al = act ? kOaiAlpha : 1.f;
   const float sg = 1.f / (1.f + expf(-al * gc));
   const float glu = gc * sg, dglu = sg * (1.f + al * gc * (1.f - sg));

@@ -52,14 +52,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // [SF1073] DeepSeek-V4 family commit note (the clamp).
 constexpr float kOaiAlpha = 1.702f;
 
+
+// The SwiGLU clamps, min(g, L) and clip(u, -L, L), written as selects so that
+// a NaN passes through as the framework's clamp passes it (the hardware's
+// min and max return the other operand of a NaN).  L = +inf: no clamp.
+__device__ __forceinline__ float clamp_hi(float v, float hi) { return v > hi ? hi : v; }
+__device__ __forceinline__ float clamp_sym(float v, float lim) { return v > lim ? lim : (v < -lim ? -lim : v); }
 // With the hardware's exp2 and reciprocal approximations (about 1 ulp each,
 // so a few ulp of f32 on the result: far below the bf16 rounding that
 // follows).  Large |g| behaves as the exact form: exp2 overflows to inf and
 // the reciprocal to 0 (-> -0), or underflows to 0 (-> g).  For act 0 the
 // scale factor is exactly -log2(e).
 __device__ __forceinline__ float swiglu_fast(float g, float u, float lim, int act) {
-  g = fminf(g, lim);
-  u = fminf(fmaxf(u, -lim), lim);
+  g = clamp_hi(g, lim);
+  u = clamp_sym(u, lim);
   const float k = act ? kOaiAlpha * -1.4426950408889634f : -1.4426950408889634f;
   const float e = __builtin_amdgcn_exp2f(g * k);
   return g * __builtin_amdgcn_rcpf(1.f + e) * (act ? u + 1.f : u);
@@ -67,8 +73,8 @@ __device__ __forceinline__ float swiglu_fast(float g, float u, float lim, int ac
 
 // The same with the library expf and an IEEE division.
 __device__ __forceinline__ float swiglu_exact(float g, float u, float lim, int act) {
-  g = fminf(g, lim);
-  u = fminf(fmaxf(u, -lim), lim);
+  g = clamp_hi(g, lim);
+  u = clamp_sym(u, lim);
   return g / (1.f + expf(act ? -kOaiAlpha * g : -g)) * (act ? u + 1.f : u);
 }
 

@@ -15,9 +15,10 @@ constexpr int kKBlock = 128;
 // MXFP4 decoding (OCP MX: E2M1 element, E8M0 scale of 32 elements)
 // --------------------------------------------------------------------------
 
-// E8M0 -> 2^(s-127) as f32 (s = 0 is the subnormal 2^-127; 255 is not used).
+// E8M0 -> 2^(s-127) as f32 (s = 0 is the subnormal 2^-127); s = 255 is NaN
+// in OCP MX, and a NaN scale makes its whole block NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+  return s == 255u ? __uint_as_float(0x7fc00000u) : s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
 }
 
 // 8 codes (4 bytes; element 2j in the low nibble of byte j) -> 8 bf16 values

@@ -22,7 +22,7 @@ from mixture_experts_ffn_04_amd import api
 from mixture_experts_ffn_04_amd import workloads as W
 from oracle import moe_oracle as O
 
-from parity import Case, check_output, check_routing, sync
+from parity import BF16_TOL, Case, check_output, check_routing, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -156,6 +156,36 @@ def test_mxfp4_unaligned_gate_up_scales(name):
     assert shifted.is_contiguous() and shifted.data_ptr() % 16 == 1
     case.lw.w_gate_up_scale = shifted
     _check_whole_layer(case, wl.name + "_unaligned_scales")
+
+
+@pytest.mark.parametrize("name", ["gpt_oss_like_mxfp4", "tiled_mxfp4_t520", "big_mxfp4_top2_t1100"])
+def test_mxfp4_nan_scale_blocks(name):
+    """An E8M0 scale byte of 255 is NaN (OCP Microscaling Formats), so its 32
+    weights are NaN.  One gate_up block of a busy expert (its gate row 3, so
+    every down output of the expert's tokens becomes NaN through h) and one
+    down block of another (its output column 5 only), on the streaming, tiled
+    and big-tile decoders: NaN exactly where the oracle has NaN, the rest to
+    the usual bar.  The SwiGLU clamp keeps the NaN, as a clamp of NaN is NaN."""
+    wl = next(w for w in SMALL if w.name == name)
+    print(f"[case] {wl.name} with NaN scale blocks", flush=True)
+    case = Case(wl)
+    counts = O.expert_counts(case.oracle_route().indices, wl.E)
+    busy = np.nonzero(counts)[0]
+    e1, e2 = int(busy[0]), int(busy[-1])
+    assert e1 != e2
+    case.lw.w_gate_up_scale[e1, 3, 1] = 255
+    case.lw.w_down_scale[e2, 5, 0] = 255
+    out, r = case.forward()
+    o, ref = case.oracle_forward()
+    assert np.array_equal(r.indices.cpu().numpy(), o.indices)
+    got = out.float().cpu().numpy()
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    assert nan_ref.any() and np.array_equal(nan_got, nan_ref), (int(nan_ref.sum()), int(nan_got.sum()))
+    fin = ~nan_ref
+    rms = float(np.sqrt(np.mean(ref[fin] ** 2)))
+    err = float(np.max(np.abs(got[fin] - ref[fin])))
+    assert err <= BF16_TOL * rms, (err, rms)
+    print(f"[parity] {wl.name} NaN blocks: {int(nan_ref.sum())} NaN outputs, max|err|/rms={err / rms:.3e}")
 
 
 def test_route_entry_point_matches_forward():
