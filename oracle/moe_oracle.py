@@ -672,6 +672,75 @@ def weights_backward(picked64: np.ndarray, dweights: np.ndarray, norm_topk_prob:
     return rs * dw / d - rs * np.dot(dw, s) / (d * d)
 
 
+def _scores64(x, gate, router_bias, score_fn):
+    """fp64 logits [T, E] and scores [T, E], not rounded: the point at which
+    the backward differentiates (the score functions of route())."""
+    logits = x @ gate.T
+    if router_bias is not None:
+        logits = logits + np.asarray(router_bias, dtype=F64)
+    if score_fn == "softmax":
+        z = np.exp(logits - logits.max(axis=-1, keepdims=True))
+        scores = z / z.sum(axis=-1, keepdims=True)
+    elif score_fn == "sigmoid":
+        scores = 1.0 / (1.0 + np.exp(-logits))
+    else:
+        scores = np.sqrt(np.maximum(logits, 0.0) + np.log1p(np.exp(-np.abs(logits))))
+    return logits, scores
+
+
+def _picked_weights(picked, norm_topk_prob, route_scale):
+    """Routing weights of the picked scores (last axis: the k slots), as the
+    forward forms them: renormalised with the +1e-20 guard, times route_scale."""
+    if norm_topk_prob:
+        return route_scale * picked / (picked.sum(axis=-1, keepdims=True) + float(RENORM_EPS))
+    return route_scale * picked
+
+
+def backward_routing_weights(x64, gate64, indices, *, score_fn="softmax", norm_topk_prob=True,
+                             route_scale=1.0, router_bias=None) -> np.ndarray:
+    """fp64 routing weights [T, K] at the given selection: the weights at
+    which ffn_backward differentiates the experts (fp64 scores of fp64 logits,
+    picked, renormalised and scaled as the forward does)."""
+    _, scores = _scores64(np.asarray(x64, dtype=F64), np.asarray(gate64, dtype=F64), router_bias, score_fn)
+    picked = np.take_along_axis(scores, np.asarray(indices, dtype=np.int64), axis=1)
+    return _picked_weights(picked, norm_topk_prob, route_scale)
+
+
+def expert_grad_rows(x64, dout64, tokens, weights, ew: "ExpertWeights", cols, *,
+                     limit=math.inf, activation="swiglu"):
+    """Sampled entries of one routed expert's weight gradients.
+
+    [SF1073] V4.1 port note (forward and every gradient compared).  The
+    expert adds w * y to the output of each token routed to it (token ids
+    `tokens`, routing weights `weights`), with pre = W_gu x (+ b_gu),
+    h_j = act(pre_j, pre_{I+j}), y = W_d h (+ b_d).  Differentiating:
+    dy = w dout, (dh)_j = W_d[:, j] . dy, the SwiGLU derivative gives
+    d pre_j and d pre_{I+j}, and
+        dW_gu[j, :]   = sum over the tokens of d pre_j   x,
+        dW_gu[I+j, :] = sum over the tokens of d pre_{I+j} x,
+        dW_d[:, j]    = sum over the tokens of h_j dy.
+    Column j of h needs only rows j and I + j of W_gu and column j of W_d,
+    so these entries cost a few dot products per token, at any layer size.
+    Returns (dW_gu rows [2, len(cols), H]: the gate rows, then the up rows;
+    dW_d columns [H, len(cols)])."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    x = np.asarray(x64, dtype=F64)[tokens]
+    dy = np.asarray(weights, dtype=F64)[:, None] * np.asarray(dout64, dtype=F64)[tokens]
+    wgu = np.asarray(ew.w_gate_up, dtype=F64)
+    wd = np.asarray(ew.w_down, dtype=F64)
+    inter = wgu.shape[0] // 2
+    pg = x @ wgu[cols].T
+    pu = x @ wgu[inter + cols].T
+    if ew.b_gate_up is not None:
+        b = np.asarray(ew.b_gate_up, dtype=F64)
+        pg, pu = pg + b[cols], pu + b[inter + cols]
+    h = swiglu(pg, pu, limit, activation)
+    dh = dy @ wd[:, cols]
+    dg, du = swiglu_backward(pg, pu, limit, dh, activation)
+    return np.stack([dg.T @ x, du.T @ x]), dy.T @ h
+
+
 def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="softmax",
                  n_group=1, topk_group=1, norm_topk_prob=True, route_scale=1.0,
                  expert_bias=None, router_bias=None, limit=math.inf,
@@ -695,16 +764,7 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
               expert_bias=expert_bias, router_bias=router_bias)
     idx = r.indices
     t_count, h_dim = x.shape
-    logits = x @ gate.T
-    if router_bias is not None:
-        logits = logits + np.asarray(router_bias, dtype=F64)
-    if score_fn == "softmax":
-        z = np.exp(logits - logits.max(axis=-1, keepdims=True))
-        scores = z / z.sum(axis=-1, keepdims=True)
-    elif score_fn == "sigmoid":
-        scores = 1.0 / (1.0 + np.exp(-logits))
-    else:
-        scores = np.sqrt(np.maximum(logits, 0.0) + np.log1p(np.exp(-np.abs(logits))))
+    logits, scores = _scores64(x, gate, router_bias, score_fn)
 
     dx = np.zeros_like(x)
     dgate = np.zeros_like(gate)
@@ -720,10 +780,7 @@ def ffn_backward(x64, gate64, get_expert, dout64, *, n_experts, k, score_fn="sof
     for t in range(t_count):
         xt, dt = x[t], dout[t]
         picked = scores[t, idx[t]]
-        if norm_topk_prob:
-            w = route_scale * picked / (picked.sum() + float(RENORM_EPS))
-        else:
-            w = route_scale * picked
+        w = _picked_weights(picked, norm_topk_prob, route_scale)
         dweights = np.zeros(k)
         for kk in range(k):
             e = int(idx[t, kk])

@@ -109,6 +109,55 @@ def test_backward_matches_oracle(wl):
           flush=True)
 
 
+def test_backward_full_size_sampled():
+    """The DeepSeek-V4-style layer at its T=4096 shape (256 experts x 2048,
+    top-8 of 8 groups, ungated shared expert, clamp at 7): dx of four sampled
+    tokens, from the oracle's backward of those tokens alone (a token's input
+    gradient depends only on its own input and output gradient), and sampled
+    entries of three experts' weight gradients (the busiest, a median and the
+    least busy non-empty expert; six h columns each: their gate and up rows of
+    dW_gate_up and their columns of dW_down) from expert_grad_rows over the
+    expert's own tokens, each within 2e-4 of its RMS.  The router's gradient
+    needs every token's expert outputs and is covered at the smaller sizes."""
+    wl = W.workload("deepseek_v4_style", T=4096)
+    print(f"[backward] {wl.name} T={wl.T} full size, sampled", flush=True)
+    c = Case(wl)
+    out, r = c.forward()
+    dout = W.gen_dout(wl, "cuda")
+    g = api.ffn_backward(c.cfg, c.x, c.lw, dout, r)
+    sync()
+    x64, gate64 = c.x64(), c.gate64()
+    d64 = O.to_f64(host(dout), wl.act_dtype)
+    idx = host(r.indices)
+    assert np.array_equal(idx, c.oracle_route().indices), "selection differs from the oracle's"
+    rep = {}
+    toks = np.array([0, 1337, 2718, 4095])
+    sh_gu, sh_d, sh_g = c.shared64()
+    route_kw = dict(score_fn=wl.score_fn, norm_topk_prob=wl.norm_topk_prob, route_scale=wl.route_scale,
+                    router_bias=c.bias(c.lw.router_bias))
+    og = O.ffn_backward(x64[toks], gate64, c.expert, d64[toks], n_experts=wl.E, k=wl.K,
+                        n_group=wl.n_group, topk_group=wl.topk_group, expert_bias=c.bias(c.lw.expert_bias),
+                        limit=wl.swiglu_limit, activation=wl.activation, sh_gate_up64=sh_gu,
+                        sh_down64=sh_d, sh_gate64=sh_g, **route_kw)
+    _check("dx[sampled tokens]", g.dx[torch.as_tensor(toks, device=g.dx.device)], og.dx, rep)
+    w64 = O.backward_routing_weights(x64, gate64, idx, **route_kw)
+    counts = np.bincount(idx.ravel(), minlength=wl.E)
+    order = np.argsort(counts, kind="stable")
+    nz = order[counts[order] > 0]
+    rng = np.random.default_rng(5)
+    for e in (int(nz[-1]), int(nz[len(nz) // 2]), int(nz[0])):
+        tokens, slots = np.nonzero(idx == e)
+        cols = np.sort(rng.choice(wl.I, 6, replace=False))
+        gu, dd = O.expert_grad_rows(x64, d64, tokens, w64[tokens, slots], c.expert(e), cols,
+                                    limit=wl.swiglu_limit, activation=wl.activation)
+        ct = torch.as_tensor(cols, device=g.dw_gate_up.device)
+        _check(f"dw_gate_up[{e}] gate rows ({counts[e]} rows)", g.dw_gate_up[e][ct], gu[0], rep)
+        _check(f"dw_gate_up[{e}] up rows", g.dw_gate_up[e][ct + wl.I], gu[1], rep)
+        _check(f"dw_down[{e}] columns", g.dw_down[e][:, ct], dd, rep)
+    print(f"[backward] {wl.name} T=4096: " + ", ".join(f"{k} {e / max(r_, 1e-30):.2e}" for k, (e, r_) in rep.items()),
+          flush=True)
+
+
 def test_backward_no_tokens_gives_zeros():
     wl = Wl("bwd_t0", T=0, H=64, E=4, I=32, K=2, shared_I=32, shared_gated=True, router_bias_std=0.1)
     c = Case(wl)

@@ -171,6 +171,34 @@ def test_backward_matches_autograd(kw, variant):
         np.testing.assert_allclose(g.dsh_gate, tg["sg"], **tol)
 
 
+@pytest.mark.parametrize("kw", [KW_CASES[1], KW_CASES[6]], ids=["sigmoid", "oai_clamp"])
+def test_expert_grad_rows_match_autograd(kw):
+    """expert_grad_rows (sampled weight-gradient entries from one expert's
+    tokens) against autograd's full weight gradients, with biases and both
+    activations; backward_routing_weights gives the weights it needs."""
+    c = make_case(11, T=9, biases=True, router_bias=True)
+    idx = oracle_indices(c, **kw)
+    tg = torch_grads(c, idx, **kw)
+    w = O.backward_routing_weights(c["x"], c["gate"], idx, router_bias=c["rb"],
+                                   **{k: v for k, v in kw.items() if k in ("score_fn", "route_scale")})
+    lim, act = kw.get("limit", math.inf), kw.get("activation", "swiglu")
+    cols = np.array([0, 3, 7, 5])
+    I = c["I"]
+    seen = 0
+    for e in range(c["E"]):
+        tokens, slots = np.nonzero(idx == e)
+        if tokens.size == 0:
+            continue
+        ew = O.ExpertWeights(c["wgu"][e], c["wd"][e], c["bgu"][e], c["bd"][e])
+        gu, d = O.expert_grad_rows(c["x"], c["dout"], tokens, w[tokens, slots], ew, cols, limit=lim,
+                                   activation=act)
+        np.testing.assert_allclose(gu[0], tg["wgu"][e][cols], rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(gu[1], tg["wgu"][e][I + cols], rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(d, tg["wd"][e][:, cols], rtol=1e-9, atol=1e-11)
+        seen += 1
+    assert seen >= 3
+
+
 def test_backward_matches_finite_differences():
     c = make_case(8, biases=True, router_bias=True)
     kw = dict(score_fn="sigmoid", route_scale=2.5)
