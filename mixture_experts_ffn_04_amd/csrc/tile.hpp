@@ -15,10 +15,12 @@ constexpr int kKBlock = 128;
 // MXFP4 decoding (OCP MX: E2M1 element, E8M0 scale of 32 elements)
 // --------------------------------------------------------------------------
 
-// E8M0 -> 2^(s-127) as f32 (s = 0 is the subnormal 2^-127); s = 255 is NaN
-// in OCP MX, and a NaN scale makes its whole block NaN.
+// E8M0 -> 2^(s-127) as f32, by ldexp (s = 0 gives the subnormal 2^-127); s =
+// 255 is NaN in OCP MX, and a NaN scale makes its whole block NaN.  One
+// select beside the ldexp: a form with a second select (for s = 0) slowed the
+// MXFP4 decode loops by 12-16%.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  return s == 255u ? __uint_as_float(0x7fc00000u) : s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+  return __builtin_amdgcn_ldexpf(s == 255u ? __uint_as_float(0x7fc00000u) : 1.0f, (int)s - 127);
 }
 
 // 8 codes (4 bytes; element 2j in the low nibble of byte j) -> 8 bf16 values
