@@ -167,6 +167,10 @@ struct Runs {
 // (row r, chunk c at r * 4 + (c ^ (r / 4) % 4)), so the 32 rows of a fragment
 // read and the 16 rows of a row-major store hit distinct banks.  The next
 // slice's global loads are in flight while the current slice is multiplied.
+// The weight-gradient products reduce over an expert's rows only (a hundred
+// or so at T*K/E of that size), a few slices per tile, so each tile's first
+// loads are exposed: three workgroups per CU (registers held to 168 per lane
+// in the 16-byte-run forms, without spills) overlap them.
 constexpr int kMT = 128;  // output tile rows and columns of the matrix-core kernel
 constexpr int kMK = 32;   // reduction slice
 
@@ -181,7 +185,7 @@ __device__ __forceinline__ f32x16v mfma32(u32x4_t a, u32x4_t b, f32x16v c) {
 __device__ __forceinline__ int munit(int row, int ch) { return row * 4 + (ch ^ ((row >> 2) & 3)); }
 
 template <int AF, int BF, bool VEC>
-__global__ __launch_bounds__(256) void grouped_gemm_mfma(GGemm g) {
+__global__ __launch_bounds__(256, VEC ? 3 : 2) void grouped_gemm_mfma(GGemm g) {
   constexpr int AK = AF & 1, BK = BF & 1;
   constexpr int NT = 256;
   constexpr int NR = kMT * kMK / 8 / NT;  // 8-element runs per thread, operand and slice (2)

@@ -42,12 +42,6 @@ constexpr int BM = 256;  // tokens per tile
 constexpr int BN = 256;  // weight rows per tile
 constexpr int kThreads = 256;
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                 c, 0, 0, 0);
-}
 
 // 16-byte unit of (row, chunk) in a tile with CH chunks per row.  Rows
 // that share a 256-byte bank window get different chunk permutations.

@@ -91,6 +91,16 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16), one wavefront.  Lane l
+// supplies row (l % 32) of A and column (l % 32) of B with the 8 consecutive
+// reduction elements 8*(l/32) .. +7; it receives
+// acc[i] = D[8*(i/4) + 4*(l/32) + i%4][l % 32], i = 0..15.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
 // Streaming (read-once) 16-byte load that does not displace reused lines.
 __device__ __forceinline__ u32x4_t load_stream16(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));

@@ -67,6 +67,13 @@ SMALL = [
        swiglu_limit=7.0, expert_linear_bias_std=0.02),
     Wl("tiled_top1_direct_t640", T=640, H=256, E=4, I=128, K=1),
     Wl("tiled_shared_only_t300", T=300, H=256, E=16, I=64, K=4, shared_I=320, expert_bias_std=0.05),
+    # the tiled kernels at a long reduction (2048 for gate_up, 1024 for the
+    # hi + lo down): partial row tiles (130 rows per expert on average),
+    # biases, the gated shared expert, and the direct weighted output of
+    # top-1 routing
+    Wl("tiled_long_k_t520", T=520, H=2048, E=8, I=1024, K=2, shared_I=1024, shared_gated=True,
+       expert_linear_bias_std=0.02),
+    Wl("tiled_long_k_direct_t600", T=600, H=2048, E=4, I=1024, K=1),
     # second row tiles of 87-113 rows: 2, 3 and 4 filled 16-row token
     # fragments in the second token half of the tiled kernel (its main loop
     # is compiled once per count)
