@@ -2,15 +2,20 @@
 //
 // Same operations as the streaming kernels in experts.hip (gate_up + SwiGLU,
 // down + optional per-expert bias; bf16 or MXFP4 weights, bf16 activations),
-// organised for operand reuse: a workgroup computes a 128-token x 256-weight-
-// row tile, staging 64-deep slices of both operands in LDS (double-buffered:
+// organised for operand reuse: a workgroup computes a 128-token x TBN-weight-
+// row tile, staging TBK-deep slices of both operands in LDS (double-buffered:
 // the next slice's global loads are issued before the current slice's MFMAs
 // and stored to the other buffer afterwards).  Four waves each compute a
-// 64-token x 128-weight-row sub-tile with 16x16x32 bf16 MFMAs (weights as
+// 64-token x TBN/2-weight-row sub-tile with 16x16x32 bf16 MFMAs (weights as
 // operand A, tokens as operand B, so a lane ends with four adjacent output
-// columns of one token).  gate_up tiles hold 128 gate rows and the matching
-// 128 up rows, and each wave takes 64 of each, so SwiGLU pairs meet in one
+// columns of one token).  gate_up tiles hold TBN/2 gate rows and the matching
+// up rows, and each wave takes half of each, so SwiGLU pairs meet in one
 // lane.  MXFP4 codes are decoded to bf16 on their way into LDS.
+//
+// Tile shapes: 256 x 32, and 128 x 64 for bf16 gate_up when experts hold
+// about one row tile: its weight slice visits each of 128 rows 128 bytes at
+// a time instead of 256 rows 64 bytes at a time (the same 16 KB), and HBM
+// streams many rows at once better in longer runs.
 //
 // A persistent grid walks the (expert, column tile, row tile) list built from
 // the per-expert row counts (mtile_prefix); row tiles of one column tile are
@@ -30,9 +35,9 @@ namespace moe {
 namespace {
 
 constexpr int TBM = 128;          // tokens per tile
-constexpr int TBN = 256;          // weight rows per tile
-constexpr int TBK = 32;           // reduction slice
-constexpr int TLD = TBK + 8;      // padded LDS row (80 B): conflict-free 16 B fragment reads
+// weight rows per tile and reduction slice
+constexpr int kTN = 256, kTK = 32;
+constexpr int kTNg = 128, kTKg = 64;    // bf16 gate_up of experts with about one row tile
 constexpr int TTHREADS = 256;
 
 struct TileCoord {
@@ -71,8 +76,11 @@ __device__ __forceinline__ bool tile_coord(const TiledGemmArgs &t, int tile, int
 
 }  // namespace
 
-template <bool GATE_UP, int WF, bool GATHER, bool LO>
+template <bool GATE_UP, int WF, bool GATHER, bool LO, int TBN, int TBK>
 __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
+  constexpr int TLD = TBK + 8;  // padded LDS row: conflict-free 16-byte fragment reads
+  constexpr int CF = TBN / 32;  // 16-row weight fragments per wave (half the tile's weight rows)
+  static_assert(WF != W_MXFP4 || (TBN == 256 && TBK == 32), "MXFP4 tiles: 256 rows, 32-deep slices");
   const ExpertGemmArgs &a = ta.g;
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t *Xs = smem;                         // [2][TBM][TLD]
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
     constexpr int WCH = (WF == W_MXFP4) ? TBN / TTHREADS : TBN * (TBK / 8) / TTHREADS;
     u32x4_t xbuf[XCH], xlbuf[XCH], wbuf[WCH];
     uint32_t sbuf[WCH] = {};
-    static_assert(TBK == 32, "one MXFP4 scale block per slice: slice ks reads block ks");
+    static_assert(WF != W_MXFP4 || TBK == 32, "one MXFP4 scale block per slice: slice ks reads block ks");
     int wr_l[WCH], wkc[WCH];
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
@@ -223,16 +231,17 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
       }
     };
 
-    f32x4_t acc[8][4];
+    f32x4_t acc[CF][4];
 #pragma unroll
-    for (int cf = 0; cf < 8; ++cf)
+    for (int cf = 0; cf < CF; ++cf)
 #pragma unroll
       for (int tf = 0; tf < 4; ++tf) acc[cf][tf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // LDS row of this wave's column fragment cf
     auto wfrag_row = [&](int cf) {
-      if constexpr (GATE_UP) return cf < 4 ? wn * 64 + cf * 16 : TBN / 2 + wn * 64 + (cf - 4) * 16;
-      else return wn * 128 + cf * 16;
+      if constexpr (GATE_UP)
+        return cf < CF / 2 ? wn * (TBN / 4) + cf * 16 : TBN / 2 + wn * (TBN / 4) + (cf - CF / 2) * 16;
+      else return wn * (TBN / 2) + cf * 16;
     };
 
     // 16-row token fragments of this wave that hold rows of the group
@@ -246,17 +255,17 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
       const uint16_t *ws = Ws + buf * TBN * TLD;
 #pragma unroll
       for (int kk = 0; kk < TBK / 32; ++kk) {
-        u32x4_t xf[4], wf[8];
+        u32x4_t xf[4], wf[CF];
 #pragma unroll
         for (int tf = 0; tf < TFC; ++tf)
           xf[tf] = *reinterpret_cast<const u32x4_t *>(xs + (wm * 64 + tf * 16 + lr) * TLD + kk * 32 + lg * 8);
         if constexpr (TFC > 0) {
 #pragma unroll
-          for (int cf = 0; cf < 8; ++cf)
+          for (int cf = 0; cf < CF; ++cf)
             wf[cf] = *reinterpret_cast<const u32x4_t *>(ws + (wfrag_row(cf) + lr) * TLD + kk * 32 + lg * 8);
         }
 #pragma unroll
-        for (int cf = 0; cf < 8; ++cf)
+        for (int cf = 0; cf < CF; ++cf)
 #pragma unroll
           for (int tf = 0; tf < TFC; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
         if constexpr (LO) {  // same weight fragments times the low halves of h
@@ -265,7 +274,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
           for (int tf = 0; tf < TFC; ++tf)
             xf[tf] = *reinterpret_cast<const u32x4_t *>(xl + (wm * 64 + tf * 16 + lr) * TLD + kk * 32 + lg * 8);
 #pragma unroll
-          for (int cf = 0; cf < 8; ++cf)
+          for (int cf = 0; cf < CF; ++cf)
 #pragma unroll
             for (int tf = 0; tf < TFC; ++tf) acc[cf][tf] = mfma_16x16x32(wf[cf], xf[tf], acc[cf][tf]);
         }
@@ -301,8 +310,8 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
       if (row >= c.nrows) continue;
       if constexpr (GATE_UP) {
 #pragma unroll
-        for (int cf = 0; cf < 4; ++cf) {
-          const int col = col0 + wn * 64 + cf * 16 + 4 * lg;
+        for (int cf = 0; cf < CF / 2; ++cf) {
+          const int col = col0 + wn * (TBN / 4) + cf * 16 + 4 * lg;
           if (col >= a.N) continue;
           float gb[4] = {0.f, 0.f, 0.f, 0.f}, ub[4] = {0.f, 0.f, 0.f, 0.f};
           if (a.bias) {
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
           }
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = swiglu_fast(acc[cf][tf][q] + gb[q], acc[cf + 4][tf][q] + ub[q], a.limit, a.act);
+          for (int q = 0; q < 4; ++q) hv[q] = swiglu_fast(acc[cf][tf][q] + gb[q], acc[cf + CF / 2][tf][q] + ub[q], a.limit, a.act);
           const uint32_t h01 = pack_bf16x2(hv[0], hv[1]), h23 = pack_bf16x2(hv[2], hv[3]);
           const size_t off = (size_t)(c.row0 + row) * a.N + col;
           *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) = make_uint2(h01, h23);
@@ -332,8 +341,8 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
           wt = a.weights[slot];
         }
 #pragma unroll
-        for (int cf = 0; cf < 8; ++cf) {
-          const int col = col0 + wn * 128 + cf * 16 + 4 * lg;
+        for (int cf = 0; cf < CF; ++cf) {
+          const int col = col0 + wn * (TBN / 2) + cf * 16 + 4 * lg;
           if (col >= a.N) continue;
           float4 v = make_float4(acc[cf][tf][0], acc[cf][tf][1], acc[cf][tf][2], acc[cf][tf][3]);
           if (a.bias) {
@@ -355,46 +364,49 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
   }
 }
 
+template <int TN, int TK>
 static size_t tiled_lds_bytes(bool lo) {
-  return (size_t)2 * (TBM + TBN + (lo ? TBM : 0)) * TLD * sizeof(uint16_t);
+  return (size_t)2 * (TBM + TN + (lo ? TBM : 0)) * (TK + 8) * sizeof(uint16_t);
 }
 
-template <bool GATE_UP, int WF, bool GATHER, bool LO>
-static hipError_t launch_tiled_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
-  auto kern = expert_tiled<GATE_UP, WF, GATHER, LO>;
-  static bool attr_set = false;  // LDS above 64 KB must be allowed once per kernel
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)tiled_lds_bytes(LO));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int grid = (int)std::max(1L, std::min(tiles_bound, 512L));  // two per CU
-  enqueue_kernel(kern, dim3(grid), dim3(TTHREADS), tiled_lds_bytes(LO), st, t);
+template <bool GATE_UP, int WF, bool GATHER, bool LO, int TN, int TK>
+static hipError_t launch_tiled_t(const TiledGemmArgs &t, long mtiles_bound, hipStream_t st) {
+  auto kern = expert_tiled<GATE_UP, WF, GATHER, LO, TN, TK>;
+  const size_t lds = tiled_lds_bytes<TN, TK>(LO);
+  static const hipError_t attr =  // LDS above 64 KB must be allowed once per kernel
+      hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const long n_tiles = (t.g.N + (GATE_UP ? TN / 2 : TN) - 1) / (GATE_UP ? TN / 2 : TN);
+  const int grid = (int)std::max(1L, std::min(mtiles_bound * n_tiles, 512L));  // two per CU
+  enqueue_kernel(kern, dim3(grid), dim3(TTHREADS), lds, st, t);
   return hipGetLastError();
 }
 
 hipError_t launch_tiled(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total,
                         int max_groups, hipStream_t st) {
   const ExpertGemmArgs &a = t.g;
-  const int cols_per_tile = gate_up ? TBN / 2 : TBN;
-  const long n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
   const long mtiles_bound = (max_rows_total + TBM - 1) / TBM + max_groups;
-  const long tiles_bound = mtiles_bound * n_tiles;
   const bool gather = gate_up && a.perm != nullptr;
   if (gate_up) {
     if (wf == W_MXFP4)
-      return gather ? launch_tiled_t<true, W_MXFP4, true, false>(t, tiles_bound, st)
-                    : launch_tiled_t<true, W_MXFP4, false, false>(t, tiles_bound, st);
-    return gather ? launch_tiled_t<true, W_BF16, true, false>(t, tiles_bound, st)
-                  : launch_tiled_t<true, W_BF16, false, false>(t, tiles_bound, st);
+      return gather ? launch_tiled_t<true, W_MXFP4, true, false, kTN, kTK>(t, mtiles_bound, st)
+                    : launch_tiled_t<true, W_MXFP4, false, false, kTN, kTK>(t, mtiles_bound, st);
+    // 128 x 64 tiles pay for themselves where experts hold about one row tile
+    // (qwen3_5_moe at T=4096, 80 rows: gate_up 1254 -> 1162 us); with many
+    // row tiles per expert (deepseek_v4 at T=4096: 128 on average, up to 602)
+    // the doubled re-reads of their token rows cost more (2373 -> 2446 us)
+    if (max_rows_total <= 96L * max_groups)
+      return gather ? launch_tiled_t<true, W_BF16, true, false, kTNg, kTKg>(t, mtiles_bound, st)
+                    : launch_tiled_t<true, W_BF16, false, false, kTNg, kTKg>(t, mtiles_bound, st);
+    return gather ? launch_tiled_t<true, W_BF16, true, false, kTN, kTK>(t, mtiles_bound, st)
+                  : launch_tiled_t<true, W_BF16, false, false, kTN, kTK>(t, mtiles_bound, st);
   }
   if (a.A_lo) {
-    if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, true>(t, tiles_bound, st);
-    return launch_tiled_t<false, W_BF16, false, true>(t, tiles_bound, st);
+    if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, true, kTN, kTK>(t, mtiles_bound, st);
+    return launch_tiled_t<false, W_BF16, false, true, kTN, kTK>(t, mtiles_bound, st);
   }
-  if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, false>(t, tiles_bound, st);
-  return launch_tiled_t<false, W_BF16, false, false>(t, tiles_bound, st);
+  if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, false, kTN, kTK>(t, mtiles_bound, st);
+  return launch_tiled_t<false, W_BF16, false, false, kTN, kTK>(t, mtiles_bound, st);
 }
 
 int tiled_tile_rows() { return TBM; }

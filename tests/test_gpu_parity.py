@@ -66,6 +66,9 @@ SMALL = [
     Wl("tiled_mxfp4_paired_scales_t600", T=600, H=320, E=8, I=192, K=2, w_dtype="mxfp4",
        swiglu_limit=7.0, expert_linear_bias_std=0.02),
     Wl("tiled_top1_direct_t640", T=640, H=256, E=4, I=128, K=1),
+    # bf16 gate_up on 128 x 64 tiles (65 rows per expert on average): ragged
+    # 64-deep slices (352) and partial 64-column tiles (160)
+    Wl("tiled_g128_ragged_t520", T=520, H=352, E=16, I=160, K=2, expert_linear_bias_std=0.02),
     Wl("tiled_shared_only_t300", T=300, H=256, E=16, I=64, K=4, shared_I=320, expert_bias_std=0.05),
     # the tiled kernels at a long reduction (2048 for gate_up, 1024 for the
     # hi + lo down): partial row tiles (130 rows per expert on average),
