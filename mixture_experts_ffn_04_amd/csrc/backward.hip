@@ -97,12 +97,28 @@ struct Runs {
   size_t base;  // element offset of the row
   float sc;
   bool ok;
+  // a row's source (through gather) and scale: fetched ahead of the loads
+  // that use them when the row changes from slice to slice (k-major)
+  struct Ix {
+    long src;
+    float sc;
+    bool ok;
+  };
+  __device__ __forceinline__ static Ix fetch(const GOp &o, int row, int nrow, int r0) {
+    Ix x;
+    x.ok = row < nrow;
+    const int rix = (o.token_rows ? r0 : 0) + (x.ok ? row : nrow - 1);
+    x.src = o.gather ? o.gather[rix] : rix;
+    x.sc = o.scale ? o.scale[rix] : 1.f;
+    return x;
+  }
+  __device__ __forceinline__ void set(const GOp &o, const Ix &x, int grp) {
+    ok = x.ok;
+    base = (size_t)grp * o.gstride + (size_t)x.src * o.ld;
+    sc = x.sc;
+  }
   __device__ __forceinline__ void set_row(const GOp &o, int row, int nrow, int grp, int r0) {
-    ok = row < nrow;
-    const int rix = (o.token_rows ? r0 : 0) + (ok ? row : nrow - 1);
-    const long src = o.gather ? o.gather[rix] : rix;
-    base = (size_t)grp * o.gstride + (size_t)src * o.ld;
-    sc = o.scale ? o.scale[rix] : 1.f;
+    set(o, fetch(o, row, nrow, r0), grp);
   }
   // issue(): the loads of one run, kept raw; finish(): decode, scale and
   // mask.  Between the two the loads stay in flight.
@@ -260,21 +276,39 @@ __global__ __launch_bounds__(256, VEC ? 3 : 2) void grouped_gemm_mfma(GGemm g) {
   }
   typename RA::Raw ra[NR];
   typename RB::Raw rb[NR];
-  auto load = [&](int k0) {
+  // Slice s of nsl (indices past the end load the last slice again: every
+  // iteration issues the same loads, so the compiler's wait counts stay
+  // exact).  A k-major operand's rows change with the slice; their sources
+  // and scales (a gather and a scale load each) are fetched one slice ahead
+  // of the data loads that use them, and issued before those data loads:
+  // waiting for the indices (the addresses of the next slice) then leaves
+  // the data loads in flight.
+  const int nsl = (K + kMK - 1) / kMK;
+  typename RA::Ix ixa[NR];
+  typename RB::Ix ixb[NR];
+  auto fetch_ix = [&](int sl) {
+    const int k0 = min(sl, nsl - 1) * kMK;
 #pragma unroll
     for (int u = 0; u < NR; ++u) {
-      if constexpr (AK) {
-        ra_[u].set_row(g.A, k0 + ak[u], K, grp, r0);
-        ra_[u].issue(g.A, m0 + ai[u], M, ra[u]);
-      } else {
-        ra_[u].issue(g.A, k0 + ak[u], K, ra[u]);
-      }
-      if constexpr (BK) {
-        rb_[u].set_row(g.B, k0 + bk[u], K, grp, r0);
-        rb_[u].issue(g.B, n0 + bi[u], g.N, rb[u]);
-      } else {
-        rb_[u].issue(g.B, k0 + bk[u], K, rb[u]);
-      }
+      if constexpr (AK) ixa[u] = RA::fetch(g.A, k0 + ak[u], K, r0);
+      if constexpr (BK) ixb[u] = RB::fetch(g.B, k0 + bk[u], K, r0);
+    }
+  };
+  auto set_bases = [&]() {  // k-major rows of the slice whose indices are in ixa / ixb
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      if constexpr (AK) ra_[u].set(g.A, ixa[u], grp);
+      if constexpr (BK) rb_[u].set(g.B, ixb[u], grp);
+    }
+  };
+  auto issue_data = [&](int sl) {
+    const int k0 = min(sl, nsl - 1) * kMK;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      if constexpr (AK) ra_[u].issue(g.A, m0 + ai[u], M, ra[u]);
+      else ra_[u].issue(g.A, k0 + ak[u], K, ra[u]);
+      if constexpr (BK) rb_[u].issue(g.B, n0 + bi[u], g.N, rb[u]);
+      else rb_[u].issue(g.B, k0 + bk[u], K, rb[u]);
     }
   };
   // One operand's runs of a slice -> its LDS planes.  Exact bf16 operands
@@ -348,12 +382,19 @@ __global__ __launch_bounds__(256, VEC ? 3 : 2) void grouped_gemm_mfma(GGemm g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  if (K > 0) load(0);
-  for (int k0 = 0; k0 < K; k0 += kMK) {
+  if (nsl > 0) {
+    fetch_ix(0);
+    set_bases();
+    fetch_ix(1);
+    issue_data(0);
+  }
+  for (int sl = 0; sl < nsl; ++sl) {
     stash(RA{}, std::bool_constant<VEC && (AF >> 1)>{}, ra, ai, ak, AK, asplit, Ah, Al);
     stash(RB{}, std::bool_constant<VEC && (BF >> 1)>{}, rb, bi, bk, BK, bsplit, Bh, Bl);
     __syncthreads();
-    if (k0 + kMK < K) load(k0 + kMK);
+    set_bases();       // slice sl + 1
+    fetch_ix(sl + 2);
+    issue_data(sl + 1);
 #pragma unroll
     for (int kk = 0; kk < kMK / 16; ++kk) {
       const int ch = 2 * kk + lh;
