@@ -349,6 +349,48 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, const d
   // topk_group groups with the largest top-2 sums, drop the other experts.
   if (a.n_group > 1) {
     const int gsize = a.E / a.n_group;
+    uint64_t kept = 0;
+    if (gsize == 32 && a.E == 64 * J) {
+      // expert lane + 64 j is in group 2 j + lane / 32: each half-wavefront
+      // holds one group per register, so one 5-step butterfly over the half
+      // gives every group's top-2 at once; the other half's group scores come
+      // with one exchange, and every lane ranks the 2J group scores itself
+      // (larger sum first, lower group on equal sums)
+      float b1[J], b2[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        b1[j] = c[j];
+        b2[j] = NEG_INF;
+      }
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const float o1 = __shfl_xor(b1[j], off, kWave);
+          const float o2 = __shfl_xor(b2[j], off, kWave);
+          const float n1 = fmaxf(b1[j], o1);
+          const float n2 = fmaxf(fminf(b1[j], o1), fmaxf(b2[j], o2));
+          b1[j] = n1;
+          b2[j] = n2;
+        }
+      }
+      float gs[2 * J];
+      const int hf = lane >> 5;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const float mine = b1[j] + b2[j];
+        const float other = __shfl_xor(mine, 32, kWave);
+        gs[2 * j] = hf ? other : mine;
+        gs[2 * j + 1] = hf ? mine : other;
+      }
+#pragma unroll
+      for (int g = 0; g < 2 * J; ++g) {
+        int rank = 0;
+#pragma unroll
+        for (int h = 0; h < 2 * J; ++h) rank += (gs[h] > gs[g] || (gs[h] == gs[g] && h < g)) ? 1 : 0;
+        if (rank < a.topk_group) kept |= 1ull << g;
+      }
+    } else {
     float my_gscore = NEG_INF;  // lane g holds the score of group g
     for (int g = 0; g < a.n_group; ++g) {
       float b1 = NEG_INF, b2 = NEG_INF;
@@ -376,13 +418,13 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, const d
       }
       if (lane == g) my_gscore = b1 + b2;
     }
-    uint64_t kept = 0;
     for (int r = 0; r < a.topk_group; ++r) {
       float v = (lane < a.n_group && !((kept >> lane) & 1ull)) ? my_gscore : NEG_INF;
       int gi = lane < a.n_group ? lane : 1 << 30;
       float dummy = 0.f;
       wave_argmax(v, gi, dummy);
       kept |= 1ull << gi;
+    }
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -391,28 +433,92 @@ __device__ __forceinline__ void select_token(const SelectArgs &a, int t, const d
     }
   }
 
-  // top-K: K rounds of a wavefront argmax (largest value, lowest id on ties)
+  // top-K in rounds of four picks (larger value first, lower id on equal
+  // values): every lane keeps its best four untaken candidates, sorted; a
+  // 6-step butterfly merges the lists (two sorted 4-lists -> the top four:
+  // the better of A[q] and B[3 - q] is a bitonic sequence holding them,
+  // sorted by two compare-exchange layers), and the four winners are the
+  // next four picks.  Four times fewer dependent reductions than one
+  // wavefront argmax per pick.
+  // (K <= 2: one or two plain wavefront argmax rounds are shorter.)
+  auto better = [](float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); };
   uint32_t taken = 0;
   int my_idx = 0;
-  float my_score = 0.f;
-  for (int k = 0; k < a.K; ++k) {
-    // lane-local best; ids grow with j, so a strict '>' keeps the lower id
-    float bv = NEG_INF, bs = 0.f;
-    int bi = 1 << 30;
+  if (a.K <= 2) {
+    for (int k = 0; k < a.K; ++k) {
+      // lane-local best; ids grow with j, so a strict '>' keeps the lower id
+      float bv = NEG_INF, bs = 0.f;
+      int bi = 1 << 30;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (valid[j] && !((taken >> j) & 1u) && (bi == (1 << 30) || c[j] > bv)) {
+          bv = c[j];
+          bi = lane + 64 * j;
+        }
+      }
+      wave_argmax(bv, bi, bs);
+      if (bi < a.E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == k) my_idx = bi;
+    }
+  }
+  for (int k0 = 0; a.K > 2 && k0 < a.K; k0 += 4) {
+    float lv[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    int li[4] = {1 << 30, 1 << 30, 1 << 30, 1 << 30};
+    auto cx = [&](int p, int q) {  // larger of positions p < q first
+      if (better(lv[q], li[q], lv[p], li[p])) {
+        const float tv = lv[p];
+        const int ti = li[p];
+        lv[p] = lv[q];
+        li[p] = li[q];
+        lv[q] = tv;
+        li[q] = ti;
+      }
+    };
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (valid[j] && !((taken >> j) & 1u) && (bi == (1 << 30) || c[j] > bv)) {
-        bv = c[j];
-        bi = lane + 64 * j;
-        bs = s[j];
+      if (valid[j] && !((taken >> j) & 1u) && better(c[j], lane + 64 * j, lv[3], li[3])) {
+        lv[3] = c[j];
+        li[3] = lane + 64 * j;
+        cx(2, 3);
+        cx(1, 2);
+        cx(0, 1);
       }
     }
-    wave_argmax(bv, bi, bs);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == k) {
-      my_idx = bi;
-      my_score = bs;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      float ov[4];
+      int oi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ov[q] = __shfl_xor(lv[q], off, kWave);
+        oi[q] = __shfl_xor(li[q], off, kWave);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (better(ov[3 - q], oi[3 - q], lv[q], li[q])) {
+          lv[q] = ov[3 - q];
+          li[q] = oi[3 - q];
+        }
+      }
+      cx(0, 2);
+      cx(1, 3);
+      cx(0, 1);
+      cx(2, 3);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (k0 + q < a.K) {
+        if (li[q] < a.E && (li[q] & 63) == lane) taken |= 1u << (li[q] >> 6);
+        if (lane == k0 + q) my_idx = li[q];
+      }
+    }
+  }
+  // the unshifted score of the lane's pick, from the lane that holds it
+  float my_score = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const float sv = __shfl(s[j], my_idx & 63, kWave);
+    if ((my_idx >> 6) == j) my_score = sv;
   }
 
   // routing weights from the unshifted scores ([SF1033] Router table, row
