@@ -117,21 +117,35 @@ class HipEvents:
                 self.rt.hipEventDestroy(arr[i])
 
 
+def shared_in_routed(wl):
+    """Whether the library runs the shared expert's gate_up items inside the
+    routed gate_up launch: both on the streaming kernels (T below 256) with
+    bf16 weights and activations."""
+    return bool(wl.shared_I) and wl.T < 256 and wl.w_dtype == "bf16" and wl.act_dtype == "bf16"
+
+
 def kernel_cost(wl, active, stage):
     """Algorithmic bytes and flops of one routed gate_up (or down) launch: the
     active experts' weights (+ MXFP4 scales, + linear biases) read once, the
     activation rows read (gate_up: x; down: h), the output written (gate_up:
     h in bf16; down: y in f32, or out in bf16 when each token has one expert
-    and no shared expert)."""
-    H, I, K, T = wl.H, wl.I, wl.K, wl.T
+    and no shared expert); where the gate_up launch also runs the shared
+    expert's items, its weights and its h."""
+    H, I, K, T, Is = wl.H, wl.I, wl.K, wl.T, wl.shared_I
     act = 4 if wl.act_dtype == "f32" else 2
+    sh = shared_in_routed(wl)
     if stage == "gate_up":
         if wl.w_dtype == "mxfp4":
             w = 2 * I * H // 2 + 2 * I * H // 32
         else:
             w = 2 * I * H * (4 if wl.w_dtype == "f32" else 2)
         b = 2 * I * act if wl.expert_linear_bias_std else 0
-        return active * (w + b) + T * H * act + T * K * I * act, 4 * T * K * H * I
+        byt = active * (w + b) + T * H * act + T * K * I * act
+        flops = 4 * T * K * H * I
+        if sh:
+            byt += 2 * Is * H * act + T * Is * act
+            flops += 4 * T * H * Is
+        return byt, flops
     if wl.w_dtype == "mxfp4":
         w = H * I // 2 + H * I // 32
     else:
@@ -147,6 +161,8 @@ def kernel_roofline(wl, active, stage, us):
     t = us * 1e-6
     hbm_bound = b / (PEAK_HBM_GBS * 1e9) >= f / (PEAK_BF16_TFLOPS * 1e12)
     name = "routed gate_up + SwiGLU" if stage == "gate_up" else "routed down"
+    if stage == "gate_up" and shared_in_routed(wl):
+        name += " (with the shared expert's items)"
     if hbm_bound:
         ach = b / t / 1e9
         return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,

@@ -377,7 +377,11 @@ enum moe_stage {
   MOE_STAGE_ROUTER_SELECT = 1,   /* score, select, routing weights             */
   MOE_STAGE_PERMUTE = 2,         /* counts, offsets, slot <-> row maps         */
   MOE_STAGE_GATE_UP = 3,         /* routed gate_up GEMM + SwiGLU               */
-  MOE_STAGE_SHARED_GATE_UP = 4,  /* shared-expert gate_up GEMM + SwiGLU        */
+  MOE_STAGE_SHARED_GATE_UP = 4,  /* shared-expert gate_up GEMM + SwiGLU; no
+                                    kernel of its own (an empty interval)
+                                    where its items run in the routed gate_up
+                                    launch: bf16 weights and activations,
+                                    T < 256                                   */
   MOE_STAGE_DOWN = 5,            /* routed down GEMM                           */
   MOE_STAGE_SHARED_DOWN = 6,     /* shared-expert down GEMM                    */
   MOE_STAGE_COMBINE = 7,         /* weighted combine (+ shared expert)         */

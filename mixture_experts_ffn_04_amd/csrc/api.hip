@@ -487,6 +487,14 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
   // chunks at small T, so that enough work items stream its weights)
   const int sh_chunk_rows = c.T <= 128 ? 16 : 32;
   const long sh_chunks = ((long)c.T + sh_chunk_rows - 1) / sh_chunk_rows;
+  // where routed and shared experts both run on the streaming kernels with
+  // bf16 operands, the shared expert's gate_up items ride in the routed
+  // gate_up launch.  Measured at T=72 (DeepSeek-V4-style / qwen3_5_moe
+  // layers): gate_up 924 -> 914 and 615 -> 608 us against two launches.  Its
+  // down items are not carried: each holds 16 rows of h (hi and lo) where a
+  // routed item holds two or three, and carried they cost more than their own
+  // launch (down 465 -> 471 and 327 -> 358 us).
+  const bool fold = has_shared(c) && !plan.tiled && !plan.tiled_shared && wf == W_BF16 && af == W_BF16;
 
   // routed gate_up + SwiGLU over x rows gathered by slot
   ExpertGemmArgs g1{};
@@ -513,6 +521,15 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
   if (hilo) g1.out_lo = h_lo;
   g1.limit = c.swiglu_limit;
   g1.act = c.activation;
+  if (fold) {
+    g1.rows2 = c.T;
+    g1.A2 = x;
+    g1.W2 = wt->sh_gate_up;
+    g1.Kdim2 = c.H;
+    g1.N2 = c.shared_I;
+    g1.out2 = ws + L.sh_h;
+    if (hilo) g1.out2_lo = sh_h_lo;
+  }
   HIP_TRY(profile_mark(MOE_STAGE_GATE_UP, true, st), "profile event");
   if (wf == W_F32) {
     HIP_TRY(launch_gate_up_f32(g1, max_groups, st), "routed gate_up launch");
@@ -539,7 +556,9 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
     s1.limit = c.swiglu_limit;
     s1.act = c.activation;
     HIP_TRY(profile_mark(MOE_STAGE_SHARED_GATE_UP, true, st), "profile event");
-    if (af == W_F32) {
+    if (fold) {
+      // ran in the routed launch
+    } else if (af == W_F32) {
       HIP_TRY(launch_gate_up_f32(s1, 1, st), "shared gate_up launch");
     } else if (plan.tiled_shared) {
       TiledGemmArgs ts{s1, nullptr, nullptr, nullptr};
@@ -580,6 +599,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
     g2.perm = perm_ws;
     g2.weights = rb.weights;
   }
+
   HIP_TRY(profile_mark(MOE_STAGE_DOWN, true, st), "profile event");
   if (wf == W_F32) {
     HIP_TRY(launch_down_f32(g2, max_groups, st), "routed down launch");

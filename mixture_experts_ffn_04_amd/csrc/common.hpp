@@ -252,6 +252,15 @@ struct ExpertGemmArgs {
   // every token has one expert and there is no shared expert
   void *direct_out;
   const float *weights;     // [T*K] routing weights by slot
+  // streaming kernels, bf16 weights: a second segment of work items after the
+  // grouped ones, one group of rows2 rows with operands of its own and no
+  // bias or gather (the shared expert in the routed launch); rows2 = 0: none
+  int rows2;
+  const void *A2;           // [rows2, Kdim2] activation rows
+  const void *A2_lo;        // down with bf16 h: low halves; or null
+  const void *W2;           // gate_up [2*N2, Kdim2] or down [N2, Kdim2], bf16
+  int Kdim2, N2, n_tiles2;
+  void *out2, *out2_lo;     // as out / out_lo, [rows2, N2]
 };
 
 // Tiled grouped GEMM (large token counts): same operands and epilogues as

@@ -34,6 +34,12 @@
 // there without bank conflicts.  The activation rows of the chunk take the
 // same path (they are L2 hits after the first column tile).
 //
+// Second segment: with bf16 weights a launch may carry, besides the grouped
+// items, the items of one more group with operands of its own (the shared
+// expert's gate_up, whose few items would leave a launch of their own short
+// of work: carried, they stream among the routed items, and one dependent
+// launch goes away).
+//
 // Reduction split: the four wavefronts take the four 32-element MFMA steps
 // of each bf16 stage (two steps each of an MXFP4 stage) and merge their
 // partial sums in LDS in wave order at the end, so results do not depend on
@@ -107,6 +113,17 @@ __device__ __forceinline__ Chunk chunk_of(const ExpertGemmArgs &a, int c, int n_
 // the chunks that share a weight tile read it at about the same time.
 constexpr int kTileBlock = 8;
 
+// item `local` of a group of `count` chunks and n_tiles column tiles ->
+// (chunk of the group, column tile)
+__device__ __forceinline__ void blocked(int local, int count, int n_tiles, int &c, int &ct) {
+  const int per_block = count * kTileBlock;
+  const int b = local / per_block;
+  const int rem = local - b * per_block;
+  const int width = min(kTileBlock, n_tiles - b * kTileBlock);
+  c = rem / width;
+  ct = b * kTileBlock + (rem - c * width);
+}
+
 __device__ __forceinline__ void item_coords(const ExpertGemmArgs &a, int item, int n_chunks, Chunk &C,
                                             int &ct) {
   const Chunk C0 = chunk_of(a, item / a.n_tiles, n_chunks);
@@ -115,14 +132,22 @@ __device__ __forceinline__ void item_coords(const ExpertGemmArgs &a, int item, i
     ct = item - (item / a.n_tiles) * a.n_tiles;
     return;
   }
-  const int local = item - C0.first * a.n_tiles;
-  const int per_block = C0.count * kTileBlock;
-  const int b = local / per_block;
-  const int rem = local - b * per_block;
-  const int width = min(kTileBlock, a.n_tiles - b * kTileBlock);
-  const int c = rem / width;
-  ct = b * kTileBlock + (rem - c * width);
+  int c;
+  blocked(item - C0.first * a.n_tiles, C0.count, a.n_tiles, c, ct);
   C = chunk_of(a, C0.first + c, n_chunks);
+}
+
+// Item `local` of the second segment (one group of rows2 rows, chunks of
+// chunk_rows rows, the same blocked order).
+__device__ __forceinline__ void seg2_coords(const ExpertGemmArgs &a, int local, int chunks2, int chunk_rows,
+                                            Chunk &C, int &ct) {
+  int c;
+  blocked(local, chunks2, a.n_tiles2, c, ct);
+  C.g = 0;
+  C.row0 = c * chunk_rows;
+  C.nrows = min(chunk_rows, a.rows2 - C.row0);
+  C.first = 0;
+  C.count = chunks2;
 }
 
 // Per-variant layout: stage sizes, LDS carve-up and the load pipeline depth
@@ -177,31 +202,47 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int n_chunks = a.chunks ? a.n_chunks[0] : (a.single_rows + a.chunk_rows - 1) / a.chunk_rows;
-  const int total = n_chunks * a.n_tiles;
-  const int nst = (a.Kdim + SK - 1) / SK;
-  const uint16_t *A = static_cast<const uint16_t *>(a.A);
-  const uint16_t *Alo = static_cast<const uint16_t *>(a.A_lo);
+  const int items1 = n_chunks * a.n_tiles;
+  // second segment (bf16 weights only): chunks of this kernel's chunk height
+  const int chunks2 = (WF == W_BF16 && a.rows2 > 0) ? (a.rows2 + 16 * MT - 1) / (16 * MT) : 0;
+  const int items2 = chunks2 * a.n_tiles2;
 
   // XCD-aware order: the items of one contiguous range run on one XCD, so
   // an XCD keeps the activation rows of only a few experts in its L2 while
   // the weights stream past (item_coords gives the order inside a range).
+  // Each segment is cut into one range per XCD, so every XCD gets its share
+  // of both; an XCD runs its second-segment items first (they may have the
+  // longer reduction).
   const int nx = gridDim.x % 8 == 0 ? 8 : 1;
   const int xcd = blockIdx.x % nx, per = gridDim.x / nx;
-  const int span = (total + nx - 1) / nx;
+  const int span1 = (items1 + nx - 1) / nx, span2 = (items2 + nx - 1) / nx;
+  const int lo1 = min(xcd * span1, items1), n1 = min(span1, items1 - lo1);
+  const int lo2 = min(xcd * span2, items2), n2 = min(span2, items2 - lo2);
 
-  for (int local = blockIdx.x / nx; local < span; local += per) {
-    const int item = xcd * span + local;
-    if (item >= total) break;
+  for (int local = blockIdx.x / nx; local < n1 + n2; local += per) {
+    // the item's segment and operands (uniform across the workgroup)
+    const bool seg2 = local < n2;
     Chunk C;
     int ct;
-    item_coords(a, item, n_chunks, C, ct);
+    if (!seg2) item_coords(a, lo1 + (local - n2), n_chunks, C, ct);
+    else seg2_coords(a, lo2 + local, chunks2, 16 * MT, C, ct);
     const int mt_count = (C.nrows + 15) >> 4;
+    const int Kd = seg2 ? a.Kdim2 : a.Kdim;
+    const int N = seg2 ? a.N2 : a.N;
+    const int nst = (Kd + SK - 1) / SK;
+    const uint16_t *A = static_cast<const uint16_t *>(seg2 ? a.A2 : a.A);
+    const uint16_t *Alo = static_cast<const uint16_t *>(seg2 ? a.A2_lo : a.A_lo);
+    const void *Wb = seg2 ? a.W2 : a.W;
+    const void *bias = seg2 ? nullptr : a.bias;
+    void *out = seg2 ? a.out2 : a.out;
+    void *out_lo = seg2 ? a.out2_lo : a.out_lo;
+    void *direct_out = seg2 ? nullptr : a.direct_out;
 
     // ---- this thread's load sources ------------------------------------
     // weight rows of the thread's loads
     // weight row (in the expert's matrix) of tile row r
     auto wrow = [&](int r) {
-      return GATE_UP ? (r < HC ? ct * HC + r : a.N + ct * HC + (r - HC)) : ct * G::ROWS + r;
+      return GATE_UP ? (r < HC ? ct * HC + r : N + ct * HC + (r - HC)) : ct * G::ROWS + r;
     };
     const uint16_t *wp[G::W_LOADS];
     const uint8_t *cp[G::W_LOADS], *sp[G::S_LOADS > 0 ? G::S_LOADS : 1];
@@ -210,19 +251,19 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
       wch = tid & 15;  // 16 chunks of 16 bytes per row and stage
 #pragma unroll
       for (int j = 0; j < G::W_LOADS; ++j)
-        wp[j] = static_cast<const uint16_t *>(a.W) + (size_t)C.g * a.w_stride +
-                (size_t)wrow(j * 16 + (tid >> 4)) * a.Kdim + wch * 8;
+        wp[j] = static_cast<const uint16_t *>(Wb) + (size_t)C.g * a.w_stride +
+                (size_t)wrow(j * 16 + (tid >> 4)) * Kd + wch * 8;
     } else {
       wch = tid & 7;  // 8 chunks of 32 codes per row and stage
       sb = tid & 7;   // 8 scales per row and stage
 #pragma unroll
       for (int j = 0; j < G::W_LOADS; ++j)
-        cp[j] = static_cast<const uint8_t *>(a.W) + (size_t)C.g * a.w_stride +
-                (size_t)wrow(j * 32 + (tid >> 3)) * (a.Kdim / 2) + wch * 16;
+        cp[j] = static_cast<const uint8_t *>(Wb) + (size_t)C.g * a.w_stride +
+                (size_t)wrow(j * 32 + (tid >> 3)) * (Kd / 2) + wch * 16;
       if constexpr (!TAB) {
 #pragma unroll
         for (int j = 0; j < G::S_LOADS; ++j)
-          sp[j] = a.Wscale + (size_t)C.g * a.s_stride + (size_t)wrow(j * 32 + (tid >> 3)) * (a.Kdim / 32) + sb;
+          sp[j] = a.Wscale + (size_t)C.g * a.s_stride + (size_t)wrow(j * 32 + (tid >> 3)) * (Kd / 32) + sb;
       }
     }
     // TAB: this thread's 16-byte units of the item's scale table (unit u of
@@ -230,11 +271,11 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
     // unit again and store nothing)
     constexpr int TL = 2;  // units per thread: 2 HC * K/32 / 16 <= 512 for K <= 4096
     u32x4_t tv[TL];
-    const int t_units = TAB ? 2 * HC * (a.Kdim / 32) / 16 : 0;
+    const int t_units = TAB ? 2 * HC * (Kd / 32) / 16 : 0;
     if constexpr (TAB) {
       const int run = t_units / 2;
       const char *gs = reinterpret_cast<const char *>(a.Wscale) + (size_t)C.g * a.s_stride;
-      const char *g0 = gs + (size_t)(ct * HC) * (a.Kdim / 32), *u0 = gs + (size_t)(a.N + ct * HC) * (a.Kdim / 32);
+      const char *g0 = gs + (size_t)(ct * HC) * (Kd / 32), *u0 = gs + (size_t)(N + ct * HC) * (Kd / 32);
 #pragma unroll
       for (int j = 0; j < TL; ++j) {
         const int u = min(j * kThreads + tid, t_units - 1);
@@ -252,12 +293,12 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
       const int r = (j * kThreads + tid) / XCH;
       const int rr = min(r, C.nrows - 1);
       size_t ar;
-      if constexpr (GATHER)
+      if (GATHER && !seg2)
         ar = (size_t)(a.perm[C.row0 + rr] / a.topk);
       else
         ar = (size_t)(C.row0 + rr);
-      xp[j] = A + ar * a.Kdim + xch * 8;
-      if constexpr (LO) xlp[j] = Alo + (size_t)(C.row0 + rr) * a.Kdim + xch * 8;
+      xp[j] = A + ar * Kd + xch * 8;
+      if constexpr (LO) xlp[j] = Alo + (size_t)(C.row0 + rr) * Kd + xch * 8;
     }
 
     // ---- register stages -------------------------------------------------
@@ -271,7 +312,7 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
     u32x4_t xv[kDepth][NXS][X_LOADS];
 
     auto issue = [&](int d, int s) {
-      const int k0 = s * SK, kv = min(SK, a.Kdim - k0);
+      const int k0 = s * SK, kv = min(SK, Kd - k0);
       if constexpr (WF == W_BF16) {
         const int kw = wch * 8 < kv ? k0 : -wch * 8;
 #pragma unroll
@@ -328,7 +369,7 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
     // so no step is skipped (no exec-mask branches around the MFMAs)
     auto compute = [&](int buf, int s, auto full) {
       constexpr bool FULL = decltype(full)::value;
-      const int kv = min(SK, a.Kdim - s * SK);
+      const int kv = min(SK, Kd - s * SK);
       constexpr int STEPS = SK / 32 / 4;  // MFMA steps per wave per stage
 #pragma unroll
       for (int i = 0; i < STEPS; ++i) {
@@ -343,7 +384,7 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
             } else {
               const uint32_t *u = reinterpret_cast<const uint32_t *>(&Wl[buf * G::W_UNITS + unit8(row, q)]);
               if constexpr (TAB)  // block s * 8 + q of tile row `row`
-                wa[sx] = decode_e2m1x8(u[lg], e8m0_to_f32(tab[row * (a.Kdim / 32) + s * 8 + q]));
+                wa[sx] = decode_e2m1x8(u[lg], e8m0_to_f32(tab[row * (Kd / 32) + s * 8 + q]));
               else
                 wa[sx] = decode_e2m1x8(u[lg], Sl[buf * G::S_BYTES + row * 8 + q]);
             }
@@ -425,12 +466,12 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
             for (int c2 = 0; c2 < NS / 2; ++c2) {
               const int col = ct * HC + c2 * 16 + 4 * lg;
               float gb[4] = {0.f, 0.f, 0.f, 0.f}, ub[4] = {0.f, 0.f, 0.f, 0.f};
-              if (a.bias) {
-                const uint16_t *b = static_cast<const uint16_t *>(a.bias) + (size_t)C.g * a.bias_stride;
+              if (bias) {
+                const uint16_t *b = static_cast<const uint16_t *>(bias) + (size_t)C.g * a.bias_stride;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                   gb[q] = bf16_to_f32(b[col + q]);
-                  ub[q] = bf16_to_f32(b[a.N + col + q]);
+                  ub[q] = bf16_to_f32(b[N + col + q]);
                 }
               }
               uint32_t hb[4], lb[4];
@@ -440,17 +481,17 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
                 hb[q] = f32_to_bf16(hv);
                 lb[q] = f32_to_bf16(hv - bf16_to_f32(hb[q]));  // h = hi + lo to ~16 bits
               }
-              const size_t off = (size_t)(C.row0 + row) * a.N + col;
-              *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + off) =
+              const size_t off = (size_t)(C.row0 + row) * N + col;
+              *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + off) =
                   make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-              if (a.out_lo)
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out_lo) + off) =
+              if (out_lo)
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out_lo) + off) =
                     make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
             }
           } else {
             int slot = 0;
             float wt = 0.f;
-            if (a.direct_out) {  // one expert per token: out = weight * y
+            if (direct_out) {  // one expert per token: out = weight * y
               slot = a.perm[C.row0 + row];
               wt = a.weights[slot];
             }
@@ -458,19 +499,19 @@ __global__ __launch_bounds__(kThreads, (Plan<MT, WF, NS, LO>::MIN_WAVES)) void e
             for (int sx = 0; sx < NS; ++sx) {
               const int col = ct * G::ROWS + sx * 16 + 4 * lg;
               float4 o = make_float4(v[sx][0], v[sx][1], v[sx][2], v[sx][3]);
-              if (a.bias) {
-                const uint16_t *b = static_cast<const uint16_t *>(a.bias) + (size_t)C.g * a.bias_stride + col;
+              if (bias) {
+                const uint16_t *b = static_cast<const uint16_t *>(bias) + (size_t)C.g * a.bias_stride + col;
                 o.x += bf16_to_f32(b[0]);
                 o.y += bf16_to_f32(b[1]);
                 o.z += bf16_to_f32(b[2]);
                 o.w += bf16_to_f32(b[3]);
               }
-              if (a.direct_out) {
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.direct_out) + (size_t)slot * a.N + col) =
+              if (direct_out) {
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(direct_out) + (size_t)slot * N + col) =
                     make_uint2(f32_to_bf16(wt * o.x) | (f32_to_bf16(wt * o.y) << 16),
                                f32_to_bf16(wt * o.z) | (f32_to_bf16(wt * o.w) << 16));
               } else {
-                *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + (size_t)(C.row0 + row) * a.N + col) = o;
+                *reinterpret_cast<float4 *>(static_cast<float *>(out) + (size_t)(C.row0 + row) * N + col) = o;
               }
             }
           }
@@ -495,7 +536,9 @@ void launch_one(ExpertGemmArgs a, long max_chunks, hipStream_t st) {
     (void)attr;
   }
   a.n_tiles = a.N / (GATE_UP ? 8 * NS : 16 * NS);
-  const long items = max_chunks * a.n_tiles;
+  a.n_tiles2 = WF == W_BF16 && a.rows2 > 0 ? a.N2 / (GATE_UP ? 8 * NS : 16 * NS) : 0;
+  const long chunks2 = WF == W_BF16 && a.rows2 > 0 ? (a.rows2 + 16 * MT - 1) / (16 * MT) : 0;
+  const long items = max_chunks * a.n_tiles + chunks2 * a.n_tiles2;
   const dim3 g((unsigned)std::max(1L, std::min(items, (long)kGridCap))), b(kThreads);
   enqueue_kernel(k, g, b, lds, st, a);
 }
@@ -524,7 +567,7 @@ void launch_mt(const ExpertGemmArgs &a, WFormat wf, bool gather, bool lo, long m
     launch_ns<MT, W_MXFP4, 4, GATE_UP>(a, gather, lo, max_chunks, st);
   else if (wf == W_MXFP4)
     launch_ns<MT, W_MXFP4, 2, GATE_UP>(a, gather, lo, max_chunks, st);
-  else if (!GATE_UP && MT == 1 && a.N % 64 == 0)
+  else if (!GATE_UP && MT == 1 && a.N % 64 == 0 && (a.rows2 == 0 || a.N2 % 64 == 0))
     launch_ns<MT, W_BF16, 4, GATE_UP>(a, gather, lo, max_chunks, st);
   else
     launch_ns<MT, W_BF16, 2, GATE_UP>(a, gather, lo, max_chunks, st);
@@ -543,6 +586,9 @@ hipError_t launch_stream(const ExpertGemmArgs &a, bool gate_up, WFormat wf, long
   if (wf != W_BF16 && wf != W_MXFP4) return hipErrorInvalidValue;
   if (a.chunk_rows != 16 && a.chunk_rows != 32) return hipErrorInvalidValue;
   if (a.Kdim % 32 || a.N % (gate_up ? 16 : 32)) return hipErrorInvalidValue;
+  if (a.rows2 > 0 && (wf != W_BF16 || !a.A2 || !a.W2 || !a.out2 || a.Kdim2 % 32 || a.N2 % (gate_up ? 16 : 32) ||
+                      (!gate_up && !a.A_lo != !a.A2_lo)))
+    return hipErrorInvalidValue;
   const bool gather = gate_up && a.perm != nullptr;
   const bool lo = !gate_up && a.A_lo != nullptr;
   if (a.chunk_rows == 16) {

@@ -53,6 +53,11 @@ SMALL = [
     Wl("mxfp4_wide_scales", T=40, H=512, E=8, I=256, K=2, w_dtype="mxfp4", mx_scale_lo=-40,
        mx_scale_hi=20),
     Wl("top1_with_shared", T=40, H=256, E=8, I=64, K=1, shared_I=64, shared_gated=True),
+    # shared expert carried by the routed streaming launches with 32-row
+    # chunks (50 rows per expert): 7 shared chunks, the last of 8 rows, a
+    # shared width unlike the routed one, routed linear biases only
+    Wl("stream_shared_mt2_t200", T=200, H=384, E=8, I=160, K=2, shared_I=96, shared_gated=True,
+       expert_linear_bias_std=0.02),
     Wl("all_experts_k_eq_e", T=20, H=256, E=8, I=64, K=8),
     Wl("single_expert_dense", T=24, H=256, E=1, I=96, K=1),
     Wl("e1024_top16", T=24, H=256, E=1024, I=32, K=16),
