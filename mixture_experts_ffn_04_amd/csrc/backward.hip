@@ -690,27 +690,12 @@ SplitPlan split_plan(int rows, int E, int N, int K, int cols) {
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 
-__global__ __launch_bounds__(kPermThreads) void stable_permute(BackwardArgs a) {
-  extern __shared__ int hist[];  // [kPermWaves][E]: counts, then each wave's base
-  __shared__ int wsum[kPermWaves][2];
+// Expert counts -> counts, offsets and the tile prefix (exclusive offsets
+// returned for tid < E).  One workgroup of kPermThreads; `total` is the
+// expert's count (tid < E), 0 elsewhere.
+__device__ __forceinline__ int perm_scan(const BackwardArgs &a, int total, int (*wsum)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = a.T * a.K;
-  const int L = (n + kPermWaves - 1) / kPermWaves;
-  for (int i = tid; i < kPermWaves * a.E; i += kPermThreads) hist[i] = 0;
-  __syncthreads();
-  const int s0 = wave * L, s1 = min(n, s0 + L);
-  for (int s = s0 + lane; s < s1; s += 64) atomicAdd(&hist[wave * a.E + clamp_id(a.indices[s], a.E)], 1);
-  __syncthreads();
-  // per expert: bases of the waves, the total, then a scan over experts
-  int total = 0, tiles = 0;
-  if (tid < a.E) {
-    for (int w = 0; w < kPermWaves; ++w) {
-      const int c = hist[w * a.E + tid];
-      hist[w * a.E + tid] = total;
-      total += c;
-    }
-    tiles = (total + a.tile_rows - 1) / a.tile_rows;
-  }
+  const int tiles = tid < a.E ? (total + a.tile_rows - 1) / a.tile_rows : 0;
   int v0 = total, v1 = tiles;  // inclusive scans of (count, tiles) over experts
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -736,29 +721,120 @@ __global__ __launch_bounds__(kPermThreads) void stable_permute(BackwardArgs a) {
     if (tid == 0) a.mtile_prefix[0] = 0;
     if (tid == a.E - 1) a.offsets[a.E] = v0;
   }
+  return v0 - total;
+}
+
+// Rows of the 64 slots [c0, c0 + 64) ∩ [.., s1) of one wavefront, in slot
+// order within each expert: base[e] is the wave's first row of expert e
+// (LDS) and advances past the wave's slots of e.
+__device__ __forceinline__ void perm_rank_chunk(const BackwardArgs &a, int c0, int s1, int *base) {
+  const int lane = threadIdx.x & 63;
+  const int s = c0 + lane;
+  const bool valid = s < s1;
+  const int id = valid ? clamp_id(a.indices[s], a.E) : -1;
+  uint64_t left = __ballot(valid);
+  while (left) {
+    const int leader = __ffsll((unsigned long long)left) - 1;
+    const int lid = __builtin_amdgcn_readlane(id, leader);
+    const uint64_t m = __ballot(valid && id == lid);
+    if (valid && id == lid) {
+      const int row = base[lid] + __popcll(m & ((1ull << lane) - 1ull));
+      a.row_slot[row] = s;
+      a.row_token[row] = s / a.K;
+      a.row_expert[row] = lid;
+      a.slot_row[s] = row;
+    }
+    left &= ~m;
+    if (lane == leader) base[lid] += __popcll(m);
+  }
+}
+
+// Stable expert-sorted order of the slots (rows of an expert in slot order),
+// one workgroup: each wave counts and ranks a contiguous range of slots.
+__global__ __launch_bounds__(kPermThreads) void stable_permute(BackwardArgs a) {
+  extern __shared__ int hist[];  // [kPermWaves][E]: counts, then each wave's first row
+  __shared__ int wsum[kPermWaves][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.T * a.K;
+  const int L = (n + kPermWaves - 1) / kPermWaves;
+  for (int i = tid; i < kPermWaves * a.E; i += kPermThreads) hist[i] = 0;
   __syncthreads();
-  // rank the wave's slots in order
-  for (int c0 = s0; c0 < s1; c0 += 64) {
-    const int s = c0 + lane;
-    const bool valid = s < s1;
-    const int id = valid ? clamp_id(a.indices[s], a.E) : -1;
-    uint64_t left = __ballot(valid);
-    while (left) {
-      const int leader = __ffsll((unsigned long long)left) - 1;
-      const int lid = __shfl(id, leader, 64);
-      const uint64_t m = __ballot(valid && id == lid);
-      if (valid && id == lid) {
-        const int rank = __popcll(m & ((1ull << lane) - 1ull));
-        const int row = a.offsets[lid] + hist[wave * a.E + lid] + rank;
-        a.row_slot[row] = s;
-        a.row_token[row] = s / a.K;
-        a.row_expert[row] = lid;
-        a.slot_row[s] = row;
-      }
-      left &= ~m;
-      if (lane == leader) hist[wave * a.E + lid] += __popcll(m);
+  const int s0 = wave * L, s1 = min(n, s0 + L);
+  for (int s = s0 + lane; s < s1; s += 64) atomicAdd(&hist[wave * a.E + clamp_id(a.indices[s], a.E)], 1);
+  __syncthreads();
+  int total = 0;
+  if (tid < a.E) {  // each wave's first row within the expert
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = hist[w * a.E + tid];
+      hist[w * a.E + tid] = total;
+      total += c;
     }
   }
+  const int off = perm_scan(a, total, wsum);
+  if (tid < a.E)
+    for (int w = 0; w < kPermWaves; ++w) hist[w * a.E + tid] += off;
+  __syncthreads();
+  for (int c0 = s0; c0 < s1; c0 += 64) perm_rank_chunk(a, c0, s1, hist + wave * a.E);
+}
+
+// The same order for many slots, in three launches over blocks of
+// kPermThreads slots: (1) each block's expert counts; (2) one workgroup:
+// counts, offsets, tile prefix and each block's first row per expert (the
+// blocks in slot order); (3) each block ranks its slots, a wave per 64.
+__global__ __launch_bounds__(kPermThreads) void perm_block_counts(BackwardArgs a) {
+  extern __shared__ int h[];  // [E]
+  const int tid = threadIdx.x, n = a.T * a.K;
+  for (int i = tid; i < a.E; i += kPermThreads) h[i] = 0;
+  __syncthreads();
+  const int s = blockIdx.x * kPermThreads + tid;
+  if (s < n) atomicAdd(&h[clamp_id(a.indices[s], a.E)], 1);
+  __syncthreads();
+  for (int i = tid; i < a.E; i += kPermThreads) a.blk[(size_t)blockIdx.x * a.E + i] = h[i];
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_block_scan(BackwardArgs a, int nb) {
+  __shared__ int wsum[kPermWaves][2];
+  const int tid = threadIdx.x;
+  int *col = a.blk + tid;  // this expert's count of each block, E apart
+  int total = 0;
+  if (tid < a.E)
+    for (int b = 0; b < nb; ++b) total += col[(size_t)b * a.E];
+  const int off = perm_scan(a, total, wsum);
+  if (tid < a.E) {  // each block's first row of the expert, in batches of loads
+    int run = off;
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = b0 + j < nb ? col[(size_t)(b0 + j) * a.E] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b0 + j < nb) col[(size_t)(b0 + j) * a.E] = run;
+        run += c[j];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kPermThreads) void perm_block_rank(BackwardArgs a) {
+  extern __shared__ int hist[];  // [kPermWaves][E]: counts, then each wave's first row
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int n = a.T * a.K;
+  for (int i = tid; i < kPermWaves * a.E; i += kPermThreads) hist[i] = 0;
+  __syncthreads();
+  const int s = blockIdx.x * kPermThreads + tid;
+  if (s < n) atomicAdd(&hist[wave * a.E + clamp_id(a.indices[s], a.E)], 1);
+  __syncthreads();
+  if (tid < a.E) {
+    int base = a.blk[(size_t)blockIdx.x * a.E + tid];
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = hist[w * a.E + tid];
+      hist[w * a.E + tid] = base;
+      base += c;
+    }
+  }
+  __syncthreads();
+  const int c0 = blockIdx.x * kPermThreads + wave * 64;
+  perm_rank_chunk(a, c0, n, hist + wave * a.E);
 }
 
 // ---- 2. routing weights per slot (the forward's arithmetic) ------------------
@@ -1069,6 +1145,7 @@ size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *
   b.counts = reinterpret_cast<int32_t *>(take((size_t)E * 4));
   b.offsets = reinterpret_cast<int32_t *>(take((size_t)(E + 1) * 4));
   b.mtile_prefix = reinterpret_cast<int32_t *>(take((size_t)(E + 1) * 4));
+  b.blk = reinterpret_cast<int32_t *>(take((rows + kPermThreads - 1) / kPermThreads * (size_t)E * 4));
   b.slot_w = reinterpret_cast<float *>(take(rows * 4));
   b.row_w = reinterpret_cast<float *>(take(rows * 4));
   b.pre = reinterpret_cast<float *>(take(rows * 2 * I * 4));
@@ -1103,7 +1180,7 @@ size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *
     // keep the caller's inputs, outputs and sizes; fill in the scratch
     BackwardArgs c = *a;
     c.row_slot = b.row_slot; c.row_token = b.row_token; c.row_expert = b.row_expert; c.slot_row = b.slot_row;
-    c.counts = b.counts; c.offsets = b.offsets; c.mtile_prefix = b.mtile_prefix; c.part = b.part;
+    c.counts = b.counts; c.offsets = b.offsets; c.mtile_prefix = b.mtile_prefix; c.blk = b.blk; c.part = b.part;
     c.slot_w = b.slot_w; c.row_w = b.row_w; c.pre = b.pre; c.hact = b.hact; c.gd = b.gd; c.dpre = b.dpre;
     c.dx_rows = b.dx_rows; c.dweights = b.dweights; c.dl = b.dl; c.dx_router = b.dx_router;
     c.pre_s = b.pre_s; c.hact_s = b.hact_s; c.gd_s = b.gd_s; c.dpre_s = b.dpre_s; c.dx_sh = b.dx_sh;
@@ -1144,7 +1221,14 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   // 1-2. permutation and weights
   BackwardArgs pa = a;
   pa.tile_rows = skinny ? kSkinnyRows : kMT;
-  hipLaunchKernelGGL(stable_permute, dim3(1), dim3(kPermThreads), (size_t)kPermWaves * E * 4, st, pa);
+  const int nb = (rows + kPermThreads - 1) / kPermThreads;
+  if (nb <= 1) {
+    hipLaunchKernelGGL(stable_permute, dim3(1), dim3(kPermThreads), (size_t)kPermWaves * E * 4, st, pa);
+  } else {
+    hipLaunchKernelGGL(perm_block_counts, dim3(nb), dim3(kPermThreads), (size_t)E * 4, st, pa);
+    hipLaunchKernelGGL(perm_block_scan, dim3(1), dim3(kPermThreads), 0, st, pa, nb);
+    hipLaunchKernelGGL(perm_block_rank, dim3(nb), dim3(kPermThreads), (size_t)kPermWaves * E * 4, st, pa);
+  }
   BW_TRY(hipGetLastError());
   hipLaunchKernelGGL(slot_weights, dim3(blocks(T, 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(rows_weight, dim3(blocks(rows, 256)), dim3(256), 0, st, a);

@@ -308,6 +308,7 @@ struct BackwardArgs {
   GradPtrs g;
   // scratch
   int32_t *row_slot, *row_token, *row_expert, *slot_row, *counts, *offsets, *mtile_prefix;
+  int32_t *blk;   // [slot blocks][E]: expert counts of each block, then its first row per expert
   int tile_rows;  // row height of the tiles that mtile_prefix counts
   float *part;    // partial products of split reductions
   float *slot_w, *row_w, *pre, *hact, *gd, *dpre, *dx_rows, *dweights, *dl, *dx_router;

@@ -42,6 +42,9 @@ CASES = [
     # few rows per expert with a long reduction: split into chunks (a ragged
     # last chunk and ragged column tiles)
     Wl("bwd_split_ragged", T=40, H=992, E=4, I=224, K=2, shared_I=96, shared_gated=True),
+    # more than 1024 slots: the permutation runs over blocks of 1024 slots
+    # (2800 slots, a ragged third block, 64 experts)
+    Wl("bwd_perm_blocks_t700", T=700, H=96, E=64, I=64, K=4, score_fn="sigmoid", expert_bias_std=0.05),
     # the serving-size draft layer at its real shape (8 experts x 1536, top-1, H=4096)
     W.workload("qwen3_8b_moe_draft", T=72),
 ]
