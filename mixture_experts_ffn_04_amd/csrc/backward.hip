@@ -995,22 +995,50 @@ __global__ void router_bwd(BackwardArgs a) {
   }
 }
 
-// drouter_bias[e] = sum_t dl[t, e] (token order)
-__global__ void column_sums(const float *m, int rows, int cols, float *out) {
+// Column sums out[c] = sum_r w[r] m[r, c] (w = 1 when null) of a [rows, cols]
+// matrix, f32 or bf16, in a fixed order and over many workgroups: the rows
+// are cut into nch chunks; a workgroup of 4 x 64 threads takes 64 columns
+// of one chunk, thread q summing rows q, q + 4, ... of it, and the four
+// partial sums are added in q order (col_partials); then each column's
+// chunk sums are added in chunk order (col_finish).  Used for
+// drouter_bias[e] = sum_t dl[t, e] and dsh_gate[h] = sum_t dz[t] x[t, h].
+constexpr int kColChunksMax = 64;
+
+__global__ __launch_bounds__(256) void col_partials(const void *m, int bf16, const float *w, int rows, int cols,
+                                                    int chunk, float *part) {
+  __shared__ float red[4][64];
+  const int l = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + l;
+  const int r0 = blockIdx.y * chunk, r1 = min(rows, r0 + chunk);
+  float s = 0.f;
+  if (c < cols) {
+    if (w) {
+      for (int r = r0 + q; r < r1; r += 4) s = fmaf(w[r], ld_elem(m, bf16, (size_t)r * cols + c), s);
+    } else {
+      for (int r = r0 + q; r < r1; r += 4) s += ld_elem(m, bf16, (size_t)r * cols + c);
+    }
+  }
+  red[q][l] = s;
+  __syncthreads();
+  if (q == 0 && c < cols) part[(size_t)blockIdx.y * cols + c] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+}
+
+__global__ void col_finish(const float *part, int nch, int cols, float *out) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= cols) return;
   float s = 0.f;
-  for (int r = 0; r < rows; ++r) s += m[(size_t)r * cols + c];
+  for (int k = 0; k < nch; ++k) s += part[(size_t)k * cols + c];
   out[c] = s;
 }
 
-// dsh_gate[h] = sum_t dz[t] x[t, h] (token order)
-__global__ void gate_grad(BackwardArgs a) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= a.H) return;
-  float s = 0.f;
-  for (int t = 0; t < a.T; ++t) s = fmaf(a.dz[t], ld_elem(a.x, a.act_bf16, (size_t)t * a.H + h), s);
-  a.g.dsh_gate[h] = s;
+hipError_t column_sums(const void *m, int bf16, const float *w, int rows, int cols, float *part, float *out,
+                       hipStream_t st) {
+  const int nch = std::max(1, std::min(kColChunksMax, (rows + 63) / 64));
+  const int chunk = (rows + nch - 1) / nch;
+  hipLaunchKernelGGL(col_partials, dim3((cols + 63) / 64, nch), dim3(256), 0, st, m, bf16, w, rows, cols, chunk,
+                     part);
+  hipLaunchKernelGGL(col_finish, dim3(blocks(cols, 256)), dim3(256), 0, st, part, nch, cols, out);
+  return hipGetLastError();
 }
 
 // ---- 9. dx --------------------------------------------------------------------
@@ -1155,6 +1183,7 @@ size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *
   b.dx_rows = reinterpret_cast<float *>(take(rows * H * 4));
   b.dweights = reinterpret_cast<float *>(take(rows * 4));
   b.dl = reinterpret_cast<float *>(take((size_t)T * E * 4));
+  b.colpart = reinterpret_cast<float *>(take((size_t)kColChunksMax * std::max(H, E) * 4));
   if (skinny_rows((int)rows, E)) {
     size_t part = 0;
     const int nk[3][2] = {{2 * I, H}, {I, H}, {H, 2 * I}};  // pre, gd, dx_rows
@@ -1182,7 +1211,7 @@ size_t backward_layout(int T, int K, int E, int H, int I, int Is, BackwardArgs *
     c.row_slot = b.row_slot; c.row_token = b.row_token; c.row_expert = b.row_expert; c.slot_row = b.slot_row;
     c.counts = b.counts; c.offsets = b.offsets; c.mtile_prefix = b.mtile_prefix; c.blk = b.blk; c.part = b.part;
     c.slot_w = b.slot_w; c.row_w = b.row_w; c.pre = b.pre; c.hact = b.hact; c.gd = b.gd; c.dpre = b.dpre;
-    c.dx_rows = b.dx_rows; c.dweights = b.dweights; c.dl = b.dl; c.dx_router = b.dx_router;
+    c.dx_rows = b.dx_rows; c.dweights = b.dweights; c.dl = b.dl; c.colpart = b.colpart; c.dx_router = b.dx_router;
     c.pre_s = b.pre_s; c.hact_s = b.hact_s; c.gd_s = b.gd_s; c.dpre_s = b.dpre_s; c.dx_sh = b.dx_sh;
     c.gamma = b.gamma; c.dgam = b.dgam; c.dz = b.dz;
     if (!c.sh_gate) c.dz = nullptr;
@@ -1303,10 +1332,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
     s.B = op(a.x, ab, true, H);
     s.C = a.g.dsh_gate_up; s.ldc = H; s.N = H;
     BW_TRY(gemm(s, 2 * Is, st));
-    if (a.sh_gate) {
-      hipLaunchKernelGGL(gate_grad, dim3(blocks(H, 256)), dim3(256), 0, st, a);
-      BW_TRY(hipGetLastError());
-    }
+    if (a.sh_gate) BW_TRY(column_sums(a.x, ab ? 1 : 0, a.dz, T, H, a.colpart, a.g.dsh_gate, st));
   }
 
   // 8. router
@@ -1324,10 +1350,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t st) {
   r.B = op(a.gate_w, ab, true, H);
   r.C = a.dx_router; r.ldc = H;
   BW_TRY(gemm(r, T, st));
-  if (a.g.drouter_bias) {
-    hipLaunchKernelGGL(column_sums, dim3(blocks(E, 256)), dim3(256), 0, st, a.dl, T, E, a.g.drouter_bias);
-    BW_TRY(hipGetLastError());
-  }
+  if (a.g.drouter_bias) BW_TRY(column_sums(a.dl, 0, nullptr, T, E, a.colpart, a.g.drouter_bias, st));
 
   // 9. dx
   hipLaunchKernelGGL(dx_combine, dim3(blocks((size_t)T * H, 256)), dim3(256), 0, st, a);

@@ -311,6 +311,7 @@ struct BackwardArgs {
   int32_t *blk;   // [slot blocks][E]: expert counts of each block, then its first row per expert
   int tile_rows;  // row height of the tiles that mtile_prefix counts
   float *part;    // partial products of split reductions
+  float *colpart; // chunk sums of the column reductions
   float *slot_w, *row_w, *pre, *hact, *gd, *dpre, *dx_rows, *dweights, *dl, *dx_router;
   float *pre_s, *hact_s, *gd_s, *dpre_s, *dx_sh, *gamma, *dgam, *dz;
 };
