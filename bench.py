@@ -18,7 +18,7 @@ T=4096, and the other workloads at the token counts they are quoted on.
 
 Prints ONE JSON line.  `value` is tokens/s of the whole layer, from a timed
 loop of back-to-back forwards (`ms_per_step`); `ms_per_step_graph` replays the
-same forwards captured in a HIP graph.  `roofline` covers the dominant kernel
+same forwards captured in a HIP graph (four or more per graph).  `roofline` covers the dominant kernel
 (routed gate_up + SwiGLU): algorithmic bytes (or flops) per launch divided by
 its mean duration over a second timed loop of the same forwards, in which the
 launch of that kernel carries HIP start/stop events that the GPU records at
@@ -250,18 +250,20 @@ def run_gpu(wl, steps, warmup, copies=None, graph=True):
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
 
-    # the same forwards replayed from a HIP graph (one captured forward per
-    # weight copy)
+    # the same forwards replayed from a HIP graph: at least four captured
+    # forwards per graph (cycling over the weight copies), as a serving graph
+    # holds many layers, so one graph launch is not charged to a single layer
     graph_ms = None
     if graph:
+        per_graph = max(copies, 4)
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            for i in range(copies):
-                api.ffn_forward(cfg, x, sets[i], out=out, routing=routing, workspace=ws)
-        reps = max(1, steps // copies)
+            for i in range(per_graph):
+                api.ffn_forward(cfg, x, sets[i % copies], out=out, routing=routing, workspace=ws)
+        reps = max(1, steps // per_graph)
         g.replay()
         torch.cuda.synchronize()
         t0.record()
@@ -269,7 +271,7 @@ def run_gpu(wl, steps, warmup, copies=None, graph=True):
             g.replay()
         t1.record()
         torch.cuda.synchronize()
-        graph_ms = t0.elapsed_time(t1) / (reps * copies)
+        graph_ms = t0.elapsed_time(t1) / (reps * per_graph)
         del g
 
     L = _lib.lib()
