@@ -5,8 +5,7 @@
 // organised for operand reuse: a workgroup computes a 128-token x TBN-weight-
 // row tile, staging TBK-deep slices of both operands in LDS (double-buffered:
 // the next slice's global loads are issued before the current slice's MFMAs
-// and stored to the other buffer afterwards; bf16 gate_up on 256 x 32 tiles
-// loads two slices at a time, 128-byte runs per row, into both buffers).  Four waves each compute a
+// and stored to the other buffer afterwards).  Four waves each compute a
 // 64-token x TBN/2-weight-row sub-tile with 16x16x32 bf16 MFMAs (weights as
 // operand A, tokens as operand B, so a lane ends with four adjacent output
 // columns of one token).  gate_up tiles hold TBN/2 gate rows and the matching
