@@ -76,13 +76,9 @@ __device__ __forceinline__ bool tile_coord(const TiledGemmArgs &t, int tile, int
 
 }  // namespace
 
-template <bool GATE_UP, int WF, bool GATHER, bool LO, int TBN, int TBK, int PAIR = 1>
+template <bool GATE_UP, int WF, bool GATHER, bool LO, int TBN, int TBK>
 __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
   constexpr int TLD = TBK + 8;  // padded LDS row: conflict-free 16-byte fragment reads
-  // PAIR = 2: each global load covers two consecutive slices (2 * TBK
-  // elements, 128-byte runs per row), split between the two LDS buffers
-  static_assert(PAIR == 1 || (PAIR == 2 && WF == W_BF16 && !LO), "paired slices: bf16, no low halves");
-  constexpr int RCH = PAIR * TBK / 8;  // 16-byte chunks per row and load
   constexpr int CF = TBN / 32;  // 16-row weight fragments per wave (half the tile's weight rows)
   static_assert(WF != W_MXFP4 || (TBN == 256 && TBK == 32), "MXFP4 tiles: 256 rows, 32-deep slices");
   const ExpertGemmArgs &a = ta.g;
@@ -120,15 +116,15 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
     const int col0 = c.n0 * cols_per_tile;
 
     // ---- per-thread global source rows for the loads of every slice ----
-    // X: 128 rows x RCH chunks of 16 B: chunk id = tid + 256 i
-    constexpr int XCH = TBM * RCH / TTHREADS;
+    // X: 128 rows x 4 chunks of 16 B: chunk id = tid + 256 i, i < 2
+    constexpr int XCH = TBM * (TBK / 8) / TTHREADS;
     const uint16_t *xsrc[XCH];
     int xrow[XCH], xkc[XCH];
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int cid = tid + TTHREADS * i;
-      xrow[i] = cid / RCH;
-      xkc[i] = cid % RCH;
+      xrow[i] = cid / (TBK / 8);
+      xkc[i] = cid % (TBK / 8);
       const int r = min(c.m0 + xrow[i], c.nrows - 1);
       size_t ar;
       if constexpr (GATHER)
@@ -155,7 +151,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
 
     // W: bf16 256 rows x 4 chunks of 8 elements; MXFP4 256 rows x one 32-element
     // block (16 code bytes + 1 scale)
-    constexpr int WCH = (WF == W_MXFP4) ? TBN / TTHREADS : TBN * RCH / TTHREADS;
+    constexpr int WCH = (WF == W_MXFP4) ? TBN / TTHREADS : TBN * (TBK / 8) / TTHREADS;
     u32x4_t xbuf[XCH], xlbuf[XCH], wbuf[WCH];
     uint32_t sbuf[WCH] = {};
     static_assert(WF != W_MXFP4 || TBK == 32, "one MXFP4 scale block per slice: slice ks reads block ks");
@@ -167,8 +163,8 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
         wr_l[i] = cid;
         wkc[i] = 0;
       } else {
-        wr_l[i] = cid / RCH;
-        wkc[i] = cid % RCH;
+        wr_l[i] = cid / (TBK / 8);
+        wkc[i] = cid % (TBK / 8);
       }
     }
     const size_t wbase_rows = (size_t)c.g;
@@ -209,15 +205,11 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
         }
       }
     };
-    // LDS buffer and column of a loaded chunk: with paired slices, chunk c of
-    // a row belongs to slice c / (TBK / 8), i.e. buffer c / (TBK / 8)
-    auto lbuf = [&](int buf, int kc) { return PAIR == 1 ? buf : kc / (TBK / 8); };
-    auto lcol = [&](int kc) { return (PAIR == 1 ? kc : kc % (TBK / 8)) * 8; };
     auto lstore = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < XCH; ++i)
-        *reinterpret_cast<u32x4_t *>(Xs + lbuf(buf, xkc[i]) * TBM * TLD + xrow[i] * TLD + lcol(xkc[i])) = xbuf[i];
+      uint16_t *xs = Xs + buf * TBM * TLD;
       uint16_t *ws = Ws + buf * TBN * TLD;
+#pragma unroll
+      for (int i = 0; i < XCH; ++i) *reinterpret_cast<u32x4_t *>(xs + xrow[i] * TLD + xkc[i] * 8) = xbuf[i];
       if constexpr (LO) {
         uint16_t *xl = Xl + buf * TBM * TLD;
 #pragma unroll
@@ -234,7 +226,7 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
           *reinterpret_cast<u32x4_t *>(dst + 16) = decode_e2m1x8(wbuf[i].z, sc);
           *reinterpret_cast<u32x4_t *>(dst + 24) = decode_e2m1x8(wbuf[i].w, sc);
         } else {
-          *reinterpret_cast<u32x4_t *>(Ws + lbuf(buf, wkc[i]) * TBN * TLD + wr_l[i] * TLD + lcol(wkc[i])) = wbuf[i];
+          *reinterpret_cast<u32x4_t *>(ws + wr_l[i] * TLD + wkc[i] * 8) = wbuf[i];
         }
       }
     };
@@ -295,26 +287,12 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
       gload(0);
       lstore(0);
       __syncthreads();
-      if constexpr (PAIR == 1) {
-        for (int ks = 0; ks < nks; ++ks) {
-          const int buf = ks & 1;
-          if (ks + 1 < nks) gload(ks + 1);
-          compute(buf, tfc_c);
-          if (ks + 1 < nks) lstore(buf ^ 1);
-          __syncthreads();
-        }
-      } else {
-        // the next pair's loads are in flight while both buffers are multiplied
-        for (int ks = 0; ks < nks; ks += 2) {
-          if (ks + 2 < nks) gload(ks + 2);
-          compute(0, tfc_c);
-          if (ks + 1 < nks) compute(1, tfc_c);
-          if (ks + 2 < nks) {
-            __syncthreads();  // every wave is done with both buffers
-            lstore(0);
-          }
-          __syncthreads();
-        }
+      for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nks) gload(ks + 1);
+        compute(buf, tfc_c);
+        if (ks + 1 < nks) lstore(buf ^ 1);
+        __syncthreads();
       }
     };
     switch (tf_count) {
@@ -391,9 +369,9 @@ static size_t tiled_lds_bytes(bool lo) {
   return (size_t)2 * (TBM + TN + (lo ? TBM : 0)) * (TK + 8) * sizeof(uint16_t);
 }
 
-template <bool GATE_UP, int WF, bool GATHER, bool LO, int TN, int TK, int PAIR = 1>
+template <bool GATE_UP, int WF, bool GATHER, bool LO, int TN, int TK>
 static hipError_t launch_tiled_t(const TiledGemmArgs &t, long mtiles_bound, hipStream_t st) {
-  auto kern = expert_tiled<GATE_UP, WF, GATHER, LO, TN, TK, PAIR>;
+  auto kern = expert_tiled<GATE_UP, WF, GATHER, LO, TN, TK>;
   const size_t lds = tiled_lds_bytes<TN, TK>(LO);
   static const hipError_t attr =  // LDS above 64 KB must be allowed once per kernel
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -420,8 +398,8 @@ hipError_t launch_tiled(const TiledGemmArgs &t, bool gate_up, WFormat wf, long m
     if (max_rows_total <= 96L * max_groups)
       return gather ? launch_tiled_t<true, W_BF16, true, false, kTNg, kTKg>(t, mtiles_bound, st)
                     : launch_tiled_t<true, W_BF16, false, false, kTNg, kTKg>(t, mtiles_bound, st);
-    return gather ? launch_tiled_t<true, W_BF16, true, false, kTN, kTK, 2>(t, mtiles_bound, st)
-                  : launch_tiled_t<true, W_BF16, false, false, kTN, kTK, 2>(t, mtiles_bound, st);
+    return gather ? launch_tiled_t<true, W_BF16, true, false, kTN, kTK>(t, mtiles_bound, st)
+                  : launch_tiled_t<true, W_BF16, false, false, kTN, kTK>(t, mtiles_bound, st);
   }
   if (a.A_lo) {
     if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, true, kTN, kTK>(t, mtiles_bound, st);

@@ -64,9 +64,6 @@ SMALL = [
     # tiled kernels (routed from 512 tokens, shared from 256), ragged column
     # tiles (160 = 128 + 32) and ragged 64-deep reduction slices (160, 96)
     Wl("tiled_routed_t600", T=600, H=384, E=8, I=160, K=2, shared_I=96, shared_gated=True),
-    # gate_up loading two 32-deep slices per load, with an odd count of
-    # slices (352 = 11 x 32: the last pair holds one)
-    Wl("tiled_pair_odd_t600", T=600, H=352, E=8, I=160, K=2, expert_linear_bias_std=0.02),
     Wl("tiled_mxfp4_t520", T=520, H=352, E=8, I=288, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
        expert_linear_bias_std=0.02),
     # even numbers of scale blocks per row (10 for gate_up, 6 for down): the
