@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-from mixture_experts_ffn_04_amd import api
+from mixture_experts_ffn_04_amd import _lib, api
 from mixture_experts_ffn_04_amd import workloads as W
 from oracle import moe_oracle as O
 
@@ -304,6 +304,38 @@ def test_hip_graph_replay_matches_eager():
         sync()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
         torch.randn(1000, device="cuda").sum().item()   # eager work between replays
+
+
+def test_profile_stage_events():
+    """The measurement hook: every stage of a forward records a positive
+    interval, except the shared expert's gate_up, which has no kernel of its
+    own where its items run in the routed launch (bf16, T < 256): an empty
+    interval (an event pair recorded back to back, a few us), under half the
+    routed gate_up's (134 MB of expert weights here)."""
+    from bench import HipEvents
+    wl = Wl("profiled", T=72, H=2048, E=32, I=512, K=4, shared_I=512, shared_gated=True)
+    case = Case(wl)
+    ws = api.alloc_workspace(case.cfg)
+    L = _lib.lib()
+    ms = {}
+    for stage, name in enumerate(_lib.STAGES):
+        ev = HipEvents(3)
+        _lib.check(L.moe_profile_stage(stage, ev.start, ev.stop, 3))
+        try:
+            out, _ = case.forward(ws)
+            out, _ = case.forward(ws)
+            out, _ = case.forward(ws)
+            sync()
+        finally:
+            _lib.check(L.moe_profile_stage(-1, None, None, 0))
+        ms[name] = ev.elapsed_ms()
+        ev.close()
+    print("[profile] " + ", ".join(f"{k} {1e3 * min(v):.1f}-{1e3 * max(v):.1f} us" for k, v in ms.items()))
+    for name, v in ms.items():
+        if name == "shared_gate_up":
+            assert max(v) < 0.5 * min(ms["gate_up"]), (v, ms["gate_up"])
+        else:
+            assert min(v) > 0.0, (name, v)
 
 
 def test_generator_device_equals_host():

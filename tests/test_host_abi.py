@@ -244,3 +244,13 @@ def test_backward_refuses_bad_arguments(L):
     cs = cfg(shared_I=2048, shared_gated=True)
     assert bw(cc=cs, ww=_lib.MoeWeights(gate_w=FAKE, w_gate_up=FAKE, w_down=FAKE, sh_gate_up=FAKE,
                                         sh_down=FAKE, sh_gate=FAKE)) == -1            # dsh_* missing
+
+
+def test_profile_stage_refusals(L):
+    """moe_profile_stage refuses a stage past the last and missing events,
+    and disarms with a negative stage; none of this touches the GPU."""
+    ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    assert L.moe_profile_stage(len(_lib.STAGES), ev, ev, 2) == _lib.MOE_ERR_INVALID
+    assert L.moe_profile_stage(0, None, None, 2) == _lib.MOE_ERR_INVALID
+    assert L.moe_profile_stage(0, ev, ev, 0) == _lib.MOE_ERR_INVALID
+    assert L.moe_profile_stage(-1, None, None, 0) == _lib.MOE_OK
