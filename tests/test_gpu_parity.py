@@ -100,6 +100,10 @@ SMALL = [
     # keeps the output's own bf16 rounding near 1.4% of RMS, clear of the bar
     Wl("big_bf16_fragments_t1300", T=1300, H=256, E=4, I=256, K=1),
     Wl("big_bf16_fragments_t1700", T=1700, H=256, E=4, I=256, K=1),
+    # more large tiles (about 324: 4-5 row tiles x 18 column tiles per expert)
+    # than workgroups (256), so workgroups take second tiles; partially
+    # filled last row tiles, per-expert biases
+    Wl("big_many_tiles_t4096", T=4096, H=192, E=4, I=2304, K=1, expert_linear_bias_std=0.02),
     # gpt-oss's swigluoai on every GEMM path (streaming bf16 and MXFP4 with
     # the shared expert, tiled, big tile, f32) with an active clamp
     Wl("oai_stream_shared", T=72, H=384, E=32, I=160, K=4, swiglu_limit=7.0, activation="swiglu_oai",
@@ -278,6 +282,38 @@ def test_bitwise_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(ra.indices, rb.indices)
     assert torch.equal(ra.weights.view(torch.int32), rb.weights.view(torch.int32))
+
+
+def test_big_tiles_deterministic_under_graph_replay():
+    """The large-tile path with more tiles than workgroups: the same bits on
+    every call whatever the workspace held before, eagerly and under HIP
+    graph replay."""
+    wl = next(w for w in SMALL if w.name == "big_many_tiles_t4096")
+    case = Case(wl)
+    ws = api.alloc_workspace(case.cfg)
+    ws.fill_(0xA5)
+    a, _ = case.forward(ws)
+    ws.fill_(0x5A)
+    b, _ = case.forward(ws)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    out = torch.empty_like(a)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.ffn_forward(case.cfg, case.x, case.lw, out=out, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.ffn_forward(case.cfg, case.x, case.lw, out=out, workspace=ws)
+    for i in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0x33 + i)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(out.view(torch.int16), a.view(torch.int16)), f"replay {i}"
+        torch.randn(1000, device="cuda").sum().item()   # eager work between replays
 
 
 def test_hip_graph_replay_matches_eager():
