@@ -53,11 +53,12 @@ MALL_BYTES = 256 << 20
 STAGE_GATE_UP, STAGE_DOWN = 3, 5
 
 # workload specs: family[:T][:option]; options: sqrtsoftplus (score function),
-# selbias (the qwen3_5_moe drafter with its bias as the selection-only expert bias)
+# selbias (the qwen3_5_moe drafter with its bias as the selection-only expert bias),
+# blockscaled (MXFP4 gate_up at large T on the block-scaled matrix cores)
 HEADLINE = "deepseek_v4_style:72"
 EXTRA = ("deepseek_v4_style:4096,qwen3_8b_moe_draft:72,qwen3_8b_moe_draft:8192,"
          "qwen3_5_moe_drafter:4096:selbias,qwen3_5_moe_drafter:4096,"
-         "gpt_oss_style_mxfp4:72,gpt_oss_style_mxfp4:2048")
+         "gpt_oss_style_mxfp4:72,gpt_oss_style_mxfp4:2048,gpt_oss_style_mxfp4:2048:blockscaled")
 
 
 def log(msg):
@@ -76,6 +77,8 @@ def parse_spec(spec):
             kw["score_fn"] = opt
         elif opt == "selbias":
             kw["selection_bias"] = True
+        elif opt == "blockscaled":
+            kw["mx_gemm"] = "block_scaled"
         else:
             raise ValueError(f"unknown option {opt!r} in {spec!r}")
     if fam == "tiny_f32":
@@ -571,6 +574,8 @@ def main(argv=None):
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--score-fn", default=None)
     ap.add_argument("--selection-bias", action="store_true")
+    ap.add_argument("--mx-block-scaled", action="store_true",
+                    help="MXFP4 gate_up at large T on the block-scaled matrix cores")
     ap.add_argument("--copies", type=int, default=None)
     ap.add_argument("--extra", default=EXTRA, help="comma-separated family:T[:option] specs")
     ap.add_argument("--no-extra", action="store_true")
@@ -607,6 +612,8 @@ def main(argv=None):
             spec += f":{args.score_fn}"
         if args.selection_bias:
             spec += ":selbias"
+        if args.mx_block_scaled:
+            spec += ":blockscaled"
         wl = parse_spec(spec)
     if args.T and args.workload is None:
         wl = wl.with_T(args.T)

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 2
+#define MOE_FFN_ABI_VERSION 3
 
 /* Symbols of the shared library are exported explicitly. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -105,6 +105,24 @@ enum moe_activation {
 };
 #define MOE_SWIGLU_OAI_ALPHA 1.702f
 
+/* How the MXFP4 experts' gate_up product is computed where experts hold
+ * hundreds of rows (the large-tile kernels; elsewhere the decode path runs):
+ *   MOE_MX_DECODE        codes decoded to bf16 (exact), bf16 matrix cores
+ *   MOE_MX_BLOCK_SCALED  codes fed as they are to gfx950's block-scaled
+ *                        matrix cores (E2M1 x E4M3 with E8M0 scales per 32
+ *                        inputs), the bf16 activations split into two MXFP8
+ *                        terms hi + lo per 32-input block, scale 2^(floor(
+ *                        log2 max|x|) - 7); hi + lo equals x up to remainders
+ *                        below the smallest E4M3 subnormal of their block.
+ *                        Taken when H is a multiple of 64, H <= 4096 and the
+ *                        gate_up scale array starts on 16 bytes; otherwise,
+ *                        and for the down product, the decode path runs.
+ * The four-bit code layout and scales are those of [SF1073] / [MI143]. */
+enum moe_mx_gemm {
+  MOE_MX_DECODE = 0,
+  MOE_MX_BLOCK_SCALED = 1
+};
+
 /* Status codes. */
 enum moe_status {
   MOE_OK = 0,
@@ -146,6 +164,7 @@ enum moe_status {
  *              Both kinds take w_gate_up's gate rows first, then its up rows
  *              (a checkpoint that interleaves them is de-interleaved once when
  *              the weights are laid out).
+ *   mx_gemm    enum moe_mx_gemm (MXFP4 experts only; ignored otherwise).
  */
 typedef struct moe_config {
   int32_t T, H, E, I, K;
@@ -160,6 +179,7 @@ typedef struct moe_config {
   int32_t shared_I;
   int32_t shared_gated;
   int32_t activation;
+  int32_t mx_gemm;
 } moe_config;
 
 /*

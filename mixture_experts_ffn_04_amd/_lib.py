@@ -12,11 +12,12 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 MOE_DTYPE = {"f32": 0, "bf16": 1, "mxfp4": 2}
 MOE_SCORE = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 MOE_ACT = {"swiglu": 0, "swiglu_oai": 1}
+MOE_MX_GEMM = {"decode": 0, "block_scaled": 1}
 # MOE_NOALLOC_SCRATCH_BYTES: the scratch array of moe_ffn_forward_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
@@ -39,7 +40,7 @@ class MoeConfig(ctypes.Structure):
         ("topk_group", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
         ("route_scale", ctypes.c_float), ("swiglu_limit", ctypes.c_float),
         ("shared_I", ctypes.c_int32), ("shared_gated", ctypes.c_int32),
-        ("activation", ctypes.c_int32),
+        ("activation", ctypes.c_int32), ("mx_gemm", ctypes.c_int32),
     ]
 
 

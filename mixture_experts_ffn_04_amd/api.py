@@ -21,13 +21,15 @@ from ._lib import MoeConfig, MoeGrads, MoeWeights, check, lib
 
 def make_config(T, H, E, I, K, *, act_dtype="bf16", w_dtype="bf16", score_fn="softmax",
                 n_group=1, topk_group=1, norm_topk_prob=True, route_scale=1.0,
-                swiglu_limit=math.inf, shared_I=0, shared_gated=False, activation="swiglu") -> MoeConfig:
+                swiglu_limit=math.inf, shared_I=0, shared_gated=False, activation="swiglu",
+                mx_gemm="decode") -> MoeConfig:
     return MoeConfig(T=T, H=H, E=E, I=I, K=K, act_dtype=_lib.MOE_DTYPE[act_dtype],
                      w_dtype=_lib.MOE_DTYPE[w_dtype], score_fn=_lib.MOE_SCORE[score_fn],
                      n_group=n_group, topk_group=topk_group,
                      norm_topk_prob=int(bool(norm_topk_prob)), route_scale=float(route_scale),
                      swiglu_limit=float(swiglu_limit), shared_I=shared_I,
-                     shared_gated=int(bool(shared_gated)), activation=_lib.MOE_ACT[activation])
+                     shared_gated=int(bool(shared_gated)), activation=_lib.MOE_ACT[activation],
+                     mx_gemm=_lib.MOE_MX_GEMM[mx_gemm])
 
 
 def config_from_workload(w) -> MoeConfig:
@@ -36,7 +38,7 @@ def config_from_workload(w) -> MoeConfig:
                        score_fn=w.score_fn, n_group=w.n_group, topk_group=w.topk_group,
                        norm_topk_prob=w.norm_topk_prob, route_scale=w.route_scale,
                        swiglu_limit=w.swiglu_limit, shared_I=w.shared_I,
-                       shared_gated=w.shared_gated, activation=w.activation)
+                       shared_gated=w.shared_gated, activation=w.activation, mx_gemm=w.mx_gemm)
 
 
 def validate(cfg: MoeConfig) -> None:

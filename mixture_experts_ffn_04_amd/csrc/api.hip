@@ -94,6 +94,7 @@ int logits_ld(const moe_config &c) { return c.E + (has_shared_gate(c) ? 1 : 0); 
 struct GemmPlan {
   bool tiled, big;        // routed experts
   bool tiled_shared, big_shared;
+  bool mx_scaled;         // MXFP4 routed gate_up on the block-scaled matrix cores
   int chunk_rows;         // streaming kernel chunks, or the big-tile kernel's row tile
 };
 
@@ -117,6 +118,8 @@ GemmPlan gemm_plan(const moe_config &c) {
   p.big = p.tiled && slots / active >= kBigTileRows && big_fits(c, slots);
   p.tiled_shared = c.act_dtype != MOE_DTYPE_F32 && c.T >= kTiledMinTokensShared;
   p.big_shared = p.tiled_shared && c.T >= kBigTileRows && big_fits(c, c.T);
+  p.mx_scaled = p.big && c.w_dtype == MOE_DTYPE_MXFP4 && c.mx_gemm == MOE_MX_BLOCK_SCALED && c.H % 64 == 0 &&
+                c.H <= 4096;
   p.chunk_rows = p.big ? bigtile_rows() : p.tiled ? tiled_tile_rows() : stream_chunk_rows(slots, c.E);
   return p;
 }
@@ -125,7 +128,7 @@ GemmPlan gemm_plan(const moe_config &c) {
 struct Layout {
   size_t logits, gamma, scores, indices, weights, counts, offsets, active_all, n_active_all,
       mtile_prefix, mtile_prefix2, chunks, n_chunks, perm, inv;
-  size_t h, y, sh_h, sh_y, total;
+  size_t h, y, sh_h, sh_y, mxq, mxs, total;
 };
 
 Layout make_layout(const moe_config &c) {
@@ -160,6 +163,10 @@ Layout make_layout(const moe_config &c) {
   L.y = take(T * K * H * 4);
   L.sh_h = take(hparts * T * Is * act_bytes(c));
   L.sh_y = take(Is ? T * H * 4 : 0);
+  // the activations as two MXFP8 terms for the block-scaled gate_up
+  const bool mxs = gemm_plan(c).mx_scaled;
+  L.mxq = take(mxs ? T * H * 2 : 0);
+  L.mxs = take(mxs ? T * (H / 32) * 2 : 0);
   L.total = off;
   return L;
 }
@@ -355,6 +362,8 @@ MOE_API int moe_validate(const moe_config *cfg) {
   if (c.shared_gated != 0 && c.shared_gated != 1) return fail(MOE_ERR_INVALID, "shared_gated must be 0 or 1");
   if (c.activation != MOE_ACT_SWIGLU && c.activation != MOE_ACT_SWIGLU_OAI)
     return fail(MOE_ERR_INVALID, "activation %d is unknown", c.activation);
+  if (c.mx_gemm != MOE_MX_DECODE && c.mx_gemm != MOE_MX_BLOCK_SCALED)
+    return fail(MOE_ERR_INVALID, "mx_gemm %d is unknown", c.mx_gemm);
 
   if (c.E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", c.E, MOE_MAX_EXPERTS);
   if (c.K > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "K = %d > %d", c.K, MOE_MAX_TOPK);
@@ -535,7 +544,13 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
     HIP_TRY(launch_gate_up_f32(g1, max_groups, st), "routed gate_up launch");
   } else if (plan.tiled) {
     TiledGemmArgs t1{g1, active_all_ws, n_active_all_ws, mtile_prefix_ws};
-    if (plan.big) HIP_TRY(launch_bigtile(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
+    if (plan.mx_scaled && bigtile_mx_scaled_applies(t1)) {
+      const MxActs xa{reinterpret_cast<uint8_t *>(ws + L.mxq), reinterpret_cast<uint16_t *>(ws + L.mxs)};
+      HIP_TRY(launch_mxfp8_split(static_cast<const uint16_t *>(x), c.T, c.H, xa, st), "activation split launch");
+      HIP_TRY(launch_bigtile_mx_scaled(t1, xa, slots, max_groups, st), "routed gate_up launch");
+    } else if (plan.big) {
+      HIP_TRY(launch_bigtile(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
+    }
     else HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
   } else {
     HIP_TRY(launch_stream(g1, true, wf, max_chunks, st), "routed gate_up launch");

@@ -752,6 +752,275 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 gate_up on the block-scaled matrix cores of gfx950
+// (v_mfma_scale_f32_32x32x64_f8f6f4: E2M1 codes times E4M3 values, every
+// 32-element block of either operand with its own E8M0 scale), so the expert
+// weights enter the multiplication as they are stored.  The activations are
+// first split (mxfp8_split) into two MXFP8 terms x = hi + lo: per block of 32
+// the scale 2^(floor(log2 max|x|) - 7) keeps every |x| / scale at or below
+// 256 (no E4M3 saturation), hi is x / scale rounded to E4M3, lo the remainder
+// rounded to E4M3 under a scale of its own.  A bf16 value has 8 significant
+// bits and each term carries 4, so hi + lo reproduces x up to remainders
+// below the smallest E4M3 subnormal of their block; each stage multiplies
+// the codes by both terms.
+//
+// Operand layouts (measured on the GPU): lane l of the FP4 operand holds row
+// l % 32 with reduction index 32 (l / 32) + p in nibble p (byte p / 2, low
+// nibble first); lane l of the FP8 operand holds column l % 32 with index
+// 16 (l / 32) + j in byte j < 16 and 32 + 16 (l / 32) + (j - 16) in byte
+// j >= 16; the A scale of lane l scales its own block, the B scale of lane l
+// block l / 32 of column l % 32; the result has the layout of the 32x32 bf16
+// instruction.
+//
+// Tile and epilogue as in the direct-to-LDS big tile (256 tokens x 256 weight
+// rows, four wavefronts of 128 x 128), stages of 64 reduction elements (one
+// MFMA step) in a ring of three.  A stage holds the weight codes as two planes
+// (reduction halves) of 256 rows x 16 bytes, the activations as eight planes
+// of 256 rows x 16 bytes ([hi | lo] of its two blocks, 16 bytes each) and the
+// activation scales as 256 rows x 4 bytes; each plane is read by 32 lanes at
+// consecutive rows.  The tile's weight-scale table follows the ring.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct MxsPlan {
+  static constexpr int BK = 64;
+  static constexpr int WUN = 2 * BN;             // weight code planes
+  static constexpr int XUN = 8 * BM;             // activation planes
+  static constexpr int SUN = BM * 4 / 16;        // activation scales
+  static constexpr int SLOT = WUN + XUN + SUN;   // 2624 units (41 KB)
+  static constexpr int NSTAGE = 3;
+  static constexpr int OPS = WUN / 256 + XUN / 256 + 1;  // load instructions per wave and stage
+  static constexpr int MAX_K = 4096;             // the scale table beside the ring
+  static constexpr size_t RING_BYTES = (size_t)NSTAGE * SLOT * 16;
+  static __host__ __device__ constexpr int table_units(int K) { return (K / 2 + 63) & ~63; }
+  static_assert((NSTAGE - 1) * OPS < 64, "vmcnt range");
+};
+static_assert(MxsPlan::RING_BYTES + (size_t)MxsPlan::table_units(MxsPlan::MAX_K) * 16 <= 160 * 1024, "LDS");
+
+// 4 bytes per lane from global memory straight into LDS (lane i at l + 4 i)
+__device__ __forceinline__ void dma4(const char *g, void *l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 4, 0, 0);
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16_t mfma_mx(i32x8_t a_fp4, i32x8_t b_fp8, f32x16_t c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a_fp4, b_fp8, c, 4, 0, 0, scale_a, 0, scale_b);
+}
+
+}  // namespace
+
+template <bool GATHER>
+__global__ __launch_bounds__(kThreads, 1) void expert_bigtile_mxs(TiledGemmArgs ta, MxActs xa) {
+  using P = MxsPlan;
+  constexpr int SLOT = P::SLOT, NSTAGE = P::NSTAGE, OPS = P::OPS, MF = 4;
+  const ExpertGemmArgs &a = ta.g;
+  extern __shared__ u32x4_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  const int cols_per_tile = BN / 2;
+  const int n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
+  const int total = a.counts ? ta.mtile_prefix[ta.n_active_all[0]] * n_tiles
+                             : ((a.single_rows + BM - 1) / BM) * n_tiles;
+  const int nst = a.Kdim / P::BK;   // the launcher checks Kdim % 64 == 0
+  const int nblk = a.Kdim / 32;     // blocks of 32 per row
+
+  const int nx = gridDim.x % 8 == 0 ? 8 : 1;
+  const int xcd = blockIdx.x % nx, per = gridDim.x / nx;
+  const int span = (total + nx - 1) / nx;
+  for (int local = blockIdx.x / nx; local < span; local += per) {
+    const int tile = xcd * span + local;
+    if (tile >= total) break;
+    BigCoord c;
+    big_coord(ta, tile, n_tiles, c, BM);
+    const int col0 = c.n0 * cols_per_tile;
+
+    // weight tile row -> weight row of the expert (clamped into the matrix)
+    auto wrow = [&](int row) {
+      const int wr = row < BN / 2 ? col0 + row : a.N + col0 + (row - BN / 2);
+      const int lim = row < BN / 2 ? a.N - 1 : 2 * a.N - 1;
+      return (uint32_t)min(wr, lim);
+    };
+    const char *wbase = static_cast<const char *>(a.W) + (size_t)c.g * a.w_stride;
+    // this lane's sources.  Load instruction g (of 8 weight, 32 activation
+    // and 4 scale instructions per stage, spread over the waves) covers tile
+    // rows (g % 4) * 64 + lane of plane g / 4; the scale instruction of wave w
+    // rows w * 64 + lane.
+    uint32_t wof[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int g = wave * 2 + i;
+      wof[i] = wrow((g & 3) * 64 + lane) * (uint32_t)(a.Kdim / 2) + (g >> 2) * 16;
+    }
+    uint32_t xrow[4];  // activation row of tile rows rg * 64 + lane
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int r = min(c.m0 + rg * 64 + lane, c.nrows - 1);
+      xrow[rg] = GATHER ? (uint32_t)(a.perm[c.row0 + r] / a.topk) : (uint32_t)(c.row0 + r);
+    }
+    const uint32_t srow = xrow[wave];
+    const char *xq = reinterpret_cast<const char *>(xa.q);
+    const char *xs = reinterpret_cast<const char *>(xa.s);
+    const uint32_t xrow_bytes = (uint32_t)a.Kdim * 2u;  // [hi | lo] of every block: 64 bytes per block
+
+    auto issue = [&](int st) __attribute__((always_inline)) {  // stage st into ring slot st % NSTAGE
+      u32x4_t *sl = smem + (st % NSTAGE) * SLOT;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(wbase + wof[i] + (uint32_t)st * 32u, sl + (wave * 2 + i) * 64);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int g = wave * 8 + i;  // plane g / 4, row group g % 4
+        dma16(xq + xrow[g & 3] * xrow_bytes + (uint32_t)st * 128u + (g >> 2) * 16, sl + P::WUN + g * 64);
+      }
+      dma4(xs + (srow * (uint32_t)nblk + 2u * st) * 2u, reinterpret_cast<char *>(sl + P::WUN + P::XUN) + wave * 256);
+    };
+
+    f32x16_t acc[MF][4];
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mf][nf][i] = 0.f;
+
+    const int mf_count = min(MF, max(0, (c.nrows - c.m0 - wm * (BM / 2) + 31) / 32));
+    auto wfrag = [&](int nf) { return nf < 2 ? wn * 64 + nf * 32 : BN / 2 + wn * 64 + (nf - 2) * 32; };
+    const uint8_t *stab = reinterpret_cast<const uint8_t *>(smem + NSTAGE * SLOT);
+
+    // one stage: its fragments read from LDS, then its MFMAs (a second
+    // register set, to read the next stage under these MFMAs, does not fit
+    // beside the accumulators: it spills)
+    auto compute = [&](int st, auto cnt) __attribute__((always_inline)) {
+      constexpr int C = decltype(cnt)::value;
+      const u32x4_t *sl = smem + (st % NSTAGE) * SLOT;
+      const u32x4_t *Wt = sl, *Xt = sl + P::WUN;
+      const uint32_t *St = reinterpret_cast<const uint32_t *>(sl + P::WUN + P::XUN);
+      i32x8_t af[4];
+      int sa[4];
+      if constexpr (C > 0) {
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          const int row = wfrag(nf) + l32;
+          const u32x4_t v = Wt[lh * 256 + row];
+          af[nf] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          sa[nf] = stab[row * nblk + 2 * st + lh];
+        }
+      }
+#pragma unroll
+      for (int mf = 0; mf < C; ++mf) {
+        const int tr = wm * (BM / 2) + mf * 32 + l32;
+        const u32x4_t h0 = Xt[(0 + lh) * 256 + tr], h1 = Xt[(4 + lh) * 256 + tr];
+        const u32x4_t o0 = Xt[(2 + lh) * 256 + tr], o1 = Xt[(6 + lh) * 256 + tr];
+        const uint32_t sc = St[tr];
+        const i32x8_t bh = {(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+        const i32x8_t bl = {(int)o0.x, (int)o0.y, (int)o0.z, (int)o0.w, (int)o1.x, (int)o1.y, (int)o1.z, (int)o1.w};
+        const int sbh = (int)((sc >> (16 * lh)) & 0xffu), sbl = (int)((sc >> (16 * lh + 8)) & 0xffu);
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+          acc[mf][nf] = mfma_mx(af[nf], bh, acc[mf][nf], sa[nf], sbh);
+          acc[mf][nf] = mfma_mx(af[nf], bl, acc[mf][nf], sa[nf], sbl);
+        }
+      }
+    };
+
+    auto run = [&](auto cnt) __attribute__((always_inline)) {
+      // the tile's weight-scale table: LDS unit p holds bytes 16 q .. 16 q + 15
+      // of the gate rows' run (p < K/4, q = p) or of the up rows' run (q = p -
+      // K/4); units past a run's valid rows (a partial last column tile) and
+      // the padding read the run's start instead and are never used.  These
+      // loads precede stage 0's, so stage 0's wait covers them.
+      const int hu = a.Kdim / 4;
+      const int nv = min(BN / 2, a.N - col0) * nblk / 16;
+      const char *gs = reinterpret_cast<const char *>(a.Wscale) + (size_t)c.g * a.s_stride;
+      const char *g0 = gs + (size_t)col0 * nblk, *u0 = gs + (size_t)(a.N + col0) * nblk;
+      u32x4_t *tab = smem + NSTAGE * SLOT;
+      const int n_inst = P::table_units(a.Kdim) / 64;
+      for (int j = wave; j < n_inst; j += 4) {
+        const int p = j * 64 + lane;
+        const int q = p < hu ? p : p - hu;
+        const char *src = (p < hu ? g0 : u0) + (p < 2 * hu && q < nv ? q * 16 : 0);
+        dma16(src, tab + j * 64);
+      }
+#pragma unroll
+      for (int d = 0; d < NSTAGE - 1; ++d)
+        if (d < nst) issue(d);
+      for (int st = 0; st < nst; ++st) {
+        // stage st + 1, issued before, may stay in flight
+        if (st + 1 < nst) wait_vmem<OPS>();
+        else wait_vmem<0>();
+        barrier_lds();
+        if (st + NSTAGE - 1 < nst) issue(st + NSTAGE - 1);  // into the slot stage st - 1 used
+        compute(st, cnt);
+      }
+    };
+    if (mf_count == MF) run(std::integral_constant<int, MF>{});  // uniform per wave
+    else if (mf_count == 0) run(std::integral_constant<int, 0>{});
+    else if (mf_count == 1) run(std::integral_constant<int, 1>{});
+    else if (mf_count == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 3>{});
+    barrier_lds();  // every wave is done with the ring
+    big_epilogue<true, MF>(a, c, col0, acc, smem);
+    barrier_lds();  // the next tile's first loads overwrite the ring
+  }
+}
+
+// x (bf16 [rows, K]) -> two MXFP8 terms per block of 32: q[rows][K/32][hi 32
+// bytes | lo 32 bytes] (E4M3) and s[rows][K/32] = hi scale | lo scale << 8
+// (E8M0).  One thread per block.
+__global__ __launch_bounds__(256) void mxfp8_split(const uint16_t *x, long n_blocks, uint8_t *q, uint16_t *s) {
+  const long b = blockIdx.x * 256L + threadIdx.x;
+  if (b >= n_blocks) return;
+  float v[32];
+  const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + b * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t w = src[i];
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[i * 8 + 2 * j] = __uint_as_float(d[j] << 16);
+      v[i * 8 + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+    }
+  }
+  // one term: scale exponent e = floor(log2 max|t|) - 7 (0 for an all-zero
+  // block), codes of t / 2^e, and what they leave over
+  auto term = [&](float (&t)[32], uint32_t (&out)[8]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(t[j]));
+    int e = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 8 : 0;  // frexp: amax = m 2^E, m in [0.5, 1)
+    e = min(127, max(-127, e));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(t[4 * j], -e),
+                                              __builtin_amdgcn_ldexpf(t[4 * j + 1], -e), 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(t[4 * j + 2], -e),
+                                          __builtin_amdgcn_ldexpf(t[4 * j + 3], -e), w, true);
+      out[j] = (uint32_t)w;
+      // the remainder is exact in f32
+      t[4 * j] -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 0), e);
+      t[4 * j + 1] -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 1), e);
+      t[4 * j + 2] -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 2), e);
+      t[4 * j + 3] -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(w, 3), e);
+    }
+    return e + 127;
+  };
+  uint32_t hi[8], lo[8];
+  const int sh = term(v, hi);
+  const int sl = term(v, lo);
+  u32x4_t *dst = reinterpret_cast<u32x4_t *>(q + b * 64);
+  dst[0] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+  dst[1] = u32x4_t{hi[4], hi[5], hi[6], hi[7]};
+  dst[2] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+  dst[3] = u32x4_t{lo[4], lo[5], lo[6], lo[7]};
+  s[b] = (uint16_t)(sh | (sl << 8));
+}
+
 namespace {
 
 template <bool GATE_UP, bool GATHER, bool LO, int TM = BM, int WF = W_BF16>
@@ -822,5 +1091,40 @@ hipError_t launch_bigtile(const TiledGemmArgs &t, bool gate_up, WFormat wf, long
 }
 
 int bigtile_rows() { return BM; }
+
+bool bigtile_mx_scaled_applies(const TiledGemmArgs &t) {
+  const ExpertGemmArgs &a = t.g;
+  return a.Kdim % MxsPlan::BK == 0 && a.Kdim <= MxsPlan::MAX_K && (reinterpret_cast<uintptr_t>(a.Wscale) & 15) == 0;
+}
+
+hipError_t launch_mxfp8_split(const uint16_t *x, long rows, int K, const MxActs &xa, hipStream_t st) {
+  if (K % 32) return hipErrorInvalidValue;
+  const long nb = rows * (K / 32);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_split, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, x, nb, xa.q, xa.s);
+  return hipGetLastError();
+}
+
+hipError_t launch_bigtile_mx_scaled(const TiledGemmArgs &t, const MxActs &xa, long max_rows_total, int max_groups,
+                                    hipStream_t st) {
+  const ExpertGemmArgs &a = t.g;
+  if (!bigtile_mx_scaled_applies(t)) return hipErrorInvalidValue;
+  const long n_tiles = (a.N + BN / 2 - 1) / (BN / 2);
+  const long tiles_bound = ((max_rows_total + BM - 1) / BM + max_groups) * n_tiles;
+  auto kern = a.perm ? expert_bigtile_mxs<true> : expert_bigtile_mxs<false>;
+  constexpr size_t lds_max = 160 * 1024;
+  const size_t ring = MxsPlan::RING_BYTES + (size_t)MxsPlan::table_units(a.Kdim) * 16;
+  const size_t lds = std::max(ring, epi_gate_up_bytes<4>());
+  if (lds > lds_max) return hipErrorInvalidValue;
+  static const hipError_t attr1 = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bigtile_mxs<true>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+  static const hipError_t attr0 = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bigtile_mxs<false>),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+  if (attr1 != hipSuccess) return attr1;
+  if (attr0 != hipSuccess) return attr0;
+  const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));  // one per CU
+  enqueue_kernel(kern, dim3(grid), dim3(kThreads), lds, st, t, xa);
+  return hipGetLastError();
+}
 
 }  // namespace moe

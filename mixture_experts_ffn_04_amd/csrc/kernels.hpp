@@ -40,6 +40,20 @@ hipError_t launch_bigtile(const TiledGemmArgs &t, bool gate_up, WFormat wf, long
                           int max_groups, hipStream_t st);
 int bigtile_rows();
 
+// MXFP4 gate_up on the block-scaled matrix cores: the activations as two
+// MXFP8 terms (q: [rows][K/32][hi 32 B | lo 32 B] E4M3, s: [rows][K/32] hi
+// scale | lo scale << 8, E8M0), written by launch_mxfp8_split from bf16 rows.
+struct MxActs {
+  uint8_t *q;
+  uint16_t *s;
+};
+hipError_t launch_mxfp8_split(const uint16_t *x, long rows, int K, const MxActs &xa, hipStream_t st);
+// Whether the block-scaled large tile takes this product (reduction a
+// multiple of 64 and at most 4096, scale array on 16 bytes).
+bool bigtile_mx_scaled_applies(const TiledGemmArgs &t);
+hipError_t launch_bigtile_mx_scaled(const TiledGemmArgs &t, const MxActs &xa, long max_rows_total, int max_groups,
+                                    hipStream_t st);
+
 hipError_t launch_combine(const CombineArgs &a, bool bf16_out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t st);
 

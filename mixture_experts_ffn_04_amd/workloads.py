@@ -182,6 +182,7 @@ class Workload:
     route_scale: float = 1.0
     swiglu_limit: float = math.inf
     activation: str = "swiglu"         # "swiglu" | "swiglu_oai" (gpt-oss's swigluoai)
+    mx_gemm: str = "decode"            # MXFP4 gate_up at large T: "decode" | "block_scaled"
     shared_I: int = 0
     shared_gated: bool = False
     x_std: float = 1.0
@@ -231,11 +232,13 @@ def _c4(T=72, score_fn="sigmoid"):
                     expert_bias_std=0.05)
 
 
-def _c5(T=72, activation="swiglu"):
-    # activation "swiglu_oai": the same experts with gpt-oss's own activation
-    name = "gpt_oss_style_mxfp4_e32_top4" + ("_oai" if activation == "swiglu_oai" else "")
+def _c5(T=72, activation="swiglu", mx_gemm="decode"):
+    # activation "swiglu_oai": the same experts with gpt-oss's own activation;
+    # mx_gemm "block_scaled": the large-T gate_up on the block-scaled matrix cores
+    name = ("gpt_oss_style_mxfp4_e32_top4" + ("_oai" if activation == "swiglu_oai" else "")
+            + ("_blockscaled" if mx_gemm == "block_scaled" else ""))
     return Workload(name, T=T, H=2880, E=32, I=2880, K=4, w_dtype="mxfp4", swiglu_limit=7.0,
-                    activation=activation, expert_linear_bias_std=0.02)
+                    activation=activation, expert_linear_bias_std=0.02, mx_gemm=mx_gemm)
 
 
 WORKLOADS = {
@@ -260,6 +263,7 @@ FULL_CASES = [
     ("gpt_oss_style_mxfp4", {"T": 72}), ("gpt_oss_style_mxfp4", {"T": 2048}),
     ("gpt_oss_style_mxfp4", {"T": 72, "activation": "swiglu_oai"}),
     ("gpt_oss_style_mxfp4", {"T": 2048, "activation": "swiglu_oai"}),
+    ("gpt_oss_style_mxfp4", {"T": 2048, "mx_gemm": "block_scaled"}),
 ]
 
 

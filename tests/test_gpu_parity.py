@@ -104,6 +104,22 @@ SMALL = [
     # than workgroups (256), so workgroups take second tiles; partially
     # filled last row tiles, per-expert biases
     Wl("big_many_tiles_t4096", T=4096, H=192, E=4, I=2304, K=1, expert_linear_bias_std=0.02),
+    # MXFP4 gate_up on the block-scaled matrix cores (hidden size a multiple
+    # of 64): the codes against two MXFP8 terms of the activations; partial
+    # column tiles (288 = 2 x 128 + 32, 96), last row tiles with 0 to 3 filled
+    # 32-row fragments, biases, the clamp, a shared expert beside the routed
+    # ones, swigluoai (shapes whose output's own bf16 rounding stays at
+    # 1.3-1.7% of RMS, under the bar)
+    Wl("big_mx_scaled_t1100", T=1100, H=320, E=8, I=288, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
+       expert_linear_bias_std=0.02, mx_gemm="block_scaled"),
+    Wl("big_mx_scaled_shared_t1300", T=1300, H=448, E=8, I=96, K=2, w_dtype="mxfp4", swiglu_limit=7.0,
+       shared_I=64, shared_gated=True, mx_gemm="block_scaled"),
+    Wl("oai_big_mx_scaled_t1030", T=1030, H=256, E=4, I=288, K=1, w_dtype="mxfp4", swiglu_limit=7.0,
+       activation="swiglu_oai", expert_linear_bias_std=0.02, mx_gemm="block_scaled"),
+    # the block-scaled choice where it cannot apply (hidden size 352 is not a
+    # multiple of 64): the decode path runs
+    Wl("big_mx_scaled_fallback_t1030", T=1030, H=352, E=4, I=288, K=1, w_dtype="mxfp4",
+       swiglu_limit=7.0, mx_gemm="block_scaled"),
     # gpt-oss's swigluoai on every GEMM path (streaming bf16 and MXFP4 with
     # the shared expert, tiled, big tile, f32) with an active clamp
     Wl("oai_stream_shared", T=72, H=384, E=32, I=160, K=4, swiglu_limit=7.0, activation="swiglu_oai",

@@ -67,7 +67,7 @@ int main(void) {
   F(moe_config, act_dtype) F(moe_config, w_dtype) F(moe_config, score_fn)
   F(moe_config, n_group) F(moe_config, topk_group) F(moe_config, norm_topk_prob)
   F(moe_config, route_scale) F(moe_config, swiglu_limit) F(moe_config, shared_I)
-  F(moe_config, shared_gated) F(moe_config, activation)
+  F(moe_config, shared_gated) F(moe_config, activation) F(moe_config, mx_gemm)
   F(moe_weights, gate_w) F(moe_weights, router_bias) F(moe_weights, expert_bias)
   F(moe_weights, w_gate_up) F(moe_weights, w_down) F(moe_weights, w_gate_up_scale)
   F(moe_weights, w_down_scale) F(moe_weights, b_gate_up) F(moe_weights, b_down)
@@ -147,7 +147,8 @@ def test_validate_refusals(L, kw, code):
 
 def test_bad_enum_values(L):
     for field, val in (("act_dtype", 7), ("w_dtype", 9), ("score_fn", 3), ("norm_topk_prob", 2),
-                       ("shared_gated", 5), ("activation", 2), ("activation", -1)):
+                       ("shared_gated", 5), ("activation", 2), ("activation", -1), ("mx_gemm", 2),
+                       ("mx_gemm", -1)):
         c = cfg()
         setattr(c, field, val)
         assert status(L, c) == -1, field
