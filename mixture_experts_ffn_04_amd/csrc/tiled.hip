@@ -19,7 +19,8 @@
 //
 // A persistent grid walks the (expert, column tile, row tile) list built from
 // the per-expert row counts (mtile_prefix); row tiles of one column tile are
-// consecutive, so the weight tile is reused from L2.
+// consecutive (in blocks of at most eight), so the weight tile is reused from
+// L2.
 //
 // [SF1073] SpecForge PR #1073 "MoE drafts: DeepSeek-V4.1's own DSpark draft
 // (stacked on #1035)" (clamped SwiGLU; stacked gate_up_proj; FP4 experts two
@@ -39,6 +40,13 @@ constexpr int TBM = 128;          // tokens per tile
 constexpr int kTN = 256, kTK = 32;
 constexpr int kTNg = 128, kTKg = 64;    // bf16 gate_up of experts with about one row tile
 constexpr int TTHREADS = 256;
+
+// Tile order inside an expert: its row tiles fastest, in blocks of at most
+// kRowBlock.  Measured on the selection-bias qwen3_5_moe drafter at T=4096
+// (collapsed routing, experts of up to 32 row tiles): gate_up 746 -> 712 us,
+// down 636 -> 596 us against every row tile per column tile; walking column
+// tiles fastest everywhere instead slowed the DeepSeek-V4 gate_up by 9%.
+constexpr int kRowBlock = 8;
 
 struct TileCoord {
   int g, nrows, row0;  // group
@@ -69,8 +77,28 @@ __device__ __forceinline__ bool tile_coord(const TiledGemmArgs &t, int tile, int
   c.g = t.active_all[lo];
   c.nrows = a.counts[c.g];
   c.row0 = a.offsets[c.g];
-  c.m0 = (local % mt_e) * TBM;
-  c.n0 = local / mt_e;  // column tile index; scaled by the caller
+  if (mt_e <= kRowBlock) {  // every row tile of the expert per column tile
+    c.m0 = (local % mt_e) * TBM;
+    c.n0 = local / mt_e;  // column tile index; scaled by the caller
+    return true;
+  }
+  // an expert with many row tiles (collapsed routing): row tiles fastest
+  // within blocks of kRowBlock, every column tile per block, so the tiles
+  // in flight on an XCD share both token and weight tiles
+  const int nfb = mt_e / kRowBlock;  // full blocks
+  const int in_full = nfb * kRowBlock * n_tiles;
+  int rb, w, bh;
+  if (local < in_full) {
+    bh = kRowBlock;
+    rb = local / (kRowBlock * n_tiles);
+    w = local - rb * kRowBlock * n_tiles;
+  } else {
+    bh = mt_e - nfb * kRowBlock;
+    rb = nfb;
+    w = local - in_full;
+  }
+  c.m0 = (rb * kRowBlock + w % bh) * TBM;
+  c.n0 = w / bh;
   return true;
 }
 

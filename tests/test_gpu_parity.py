@@ -86,6 +86,12 @@ SMALL = [
     # fragments in the second token half of the tiled kernel (its main loop
     # is compiled once per count)
     Wl("tiled_fragments_t912", T=912, H=256, E=4, I=256, K=1),
+    # collapsed routing on the tiled kernels (a selection-only bias far above
+    # the scores): experts of 12 row tiles walk them in blocks of 8 (a full
+    # block and a partial one), ragged last row tiles, partial column tiles
+    Wl("tiled_collapsed_t1500", T=1500, H=256, E=64, I=96, K=4, expert_bias_std=0.1, shared_I=64,
+       shared_gated=True),
+    Wl("tiled_collapsed_k2_t1500", T=1500, H=256, E=64, I=160, K=2, expert_bias_std=0.1),
     # large-tile kernels (>= 256 rows per expert on average, shared expert
     # from 256 tokens): ragged 64-deep slices (352), partial column tiles
     Wl("big_routed_t1100", T=1100, H=352, E=4, I=160, K=1, shared_I=96, shared_gated=True),
