@@ -99,6 +99,7 @@ struct GemmPlan {
 };
 
 constexpr long kBigTileRows = 256;
+constexpr int kTiledLaunches = 4;  // routed and shared gate_up and down
 
 // 32-bit offsets of the big-tile kernel: activations, h and one expert's
 // weights below 4 GiB
@@ -128,7 +129,7 @@ GemmPlan gemm_plan(const moe_config &c) {
 struct Layout {
   size_t logits, gamma, scores, indices, weights, counts, offsets, active_all, n_active_all,
       mtile_prefix, mtile_prefix2, chunks, n_chunks, perm, inv;
-  size_t h, y, sh_h, sh_y, mxq, mxs, total;
+  size_t h, y, sh_h, sh_y, mxq, mxs, tile_queue, total;
 };
 
 Layout make_layout(const moe_config &c) {
@@ -167,6 +168,8 @@ Layout make_layout(const moe_config &c) {
   const bool mxs = gemm_plan(c).mx_scaled;
   L.mxq = take(mxs ? T * H * 2 : 0);
   L.mxs = take(mxs ? T * (H / 32) * 2 : 0);
+  // tile counters of the tiled launches (routed and shared gate_up and down)
+  L.tile_queue = take(kTiledLaunches * kTiledQueueInts * 4);
   L.total = off;
   return L;
 }
@@ -496,6 +499,11 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
   // chunks at small T, so that enough work items stream its weights)
   const int sh_chunk_rows = c.T <= 128 ? 16 : 32;
   const long sh_chunks = ((long)c.T + sh_chunk_rows - 1) / sh_chunk_rows;
+  // the tiled launches' tile counters start at zero (one fill for all four)
+  int32_t *queue = reinterpret_cast<int32_t *>(ws + L.tile_queue);
+  auto tile_queue = [&](int launch) { return queue + launch * kTiledQueueInts; };
+  if (plan.tiled || plan.tiled_shared)
+    HIP_TRY(launch_fill_i32(queue, 0, kTiledLaunches * kTiledQueueInts, st), "fill launch");
   // where routed and shared experts both run on the streaming kernels with
   // bf16 operands, the shared expert's gate_up items ride in the routed
   // gate_up launch.  Measured at T=72 (DeepSeek-V4-style / qwen3_5_moe
@@ -551,7 +559,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
     } else if (plan.big) {
       HIP_TRY(launch_bigtile(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
     }
-    else HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
+    else HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, tile_queue(0), st), "routed gate_up launch");
   } else {
     HIP_TRY(launch_stream(g1, true, wf, max_chunks, st), "routed gate_up launch");
   }
@@ -578,7 +586,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
     } else if (plan.tiled_shared) {
       TiledGemmArgs ts{s1, nullptr, nullptr, nullptr};
       if (plan.big_shared) HIP_TRY(launch_bigtile(ts, true, af, c.T, 1, st), "shared gate_up launch");
-      else HIP_TRY(launch_tiled(ts, true, af, c.T, 1, st), "shared gate_up launch");
+      else HIP_TRY(launch_tiled(ts, true, af, c.T, 1, tile_queue(1), st), "shared gate_up launch");
     } else {
       HIP_TRY(launch_stream(s1, true, af, sh_chunks, st), "shared gate_up launch");
     }
@@ -620,7 +628,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
     HIP_TRY(launch_down_f32(g2, max_groups, st), "routed down launch");
   } else if (plan.tiled) {
     TiledGemmArgs t2{g2, active_all_ws, n_active_all_ws, plan.big ? mtile_prefix2_ws : mtile_prefix_ws};
-    HIP_TRY(launch_tiled(t2, false, wf, slots, max_groups, st), "routed down launch");
+    HIP_TRY(launch_tiled(t2, false, wf, slots, max_groups, tile_queue(2), st), "routed down launch");
   } else {
     HIP_TRY(launch_stream(g2, false, wf, max_chunks, st), "routed down launch");
   }
@@ -642,7 +650,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
       HIP_TRY(launch_down_f32(s2, 1, st), "shared down launch");
     } else if (plan.tiled_shared) {
       TiledGemmArgs ts{s2, nullptr, nullptr, nullptr};
-      HIP_TRY(launch_tiled(ts, false, af, c.T, 1, st), "shared down launch");
+      HIP_TRY(launch_tiled(ts, false, af, c.T, 1, tile_queue(3), st), "shared down launch");
     } else {
       HIP_TRY(launch_stream(s2, false, af, sh_chunks, st), "shared down launch");
     }

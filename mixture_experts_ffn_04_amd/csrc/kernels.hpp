@@ -29,9 +29,11 @@ hipError_t launch_stream(const ExpertGemmArgs &a, bool gate_up, WFormat wf, long
 int stream_chunk_rows(long slots, int E);
 
 // Tiled grouped GEMM (large token counts).  max_rows_total bounds the rows of
-// all groups together, max_groups the number of groups.
+// all groups together, max_groups the number of groups.  queue: kTiledQueueInts
+// tile counters of this launch, zero when it starts (left past the tile count).
+constexpr int kTiledQueueInts = 8;
 hipError_t launch_tiled(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total,
-                        int max_groups, hipStream_t st);
+                        int max_groups, int32_t *queue, hipStream_t st);
 int tiled_tile_rows();
 
 // Large-tile grouped GEMM (experts with hundreds of rows: matrix-core bound).

@@ -105,7 +105,7 @@ __device__ __forceinline__ bool tile_coord(const TiledGemmArgs &t, int tile, int
 }  // namespace
 
 template <bool GATE_UP, int WF, bool GATHER, bool LO, int TBN, int TBK>
-__global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
+__global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta, int32_t *queue) {
   constexpr int TLD = TBK + 8;  // padded LDS row: conflict-free 16-byte fragment reads
   constexpr int CF = TBN / 32;  // 16-row weight fragments per wave (half the tile's weight rows)
   static_assert(WF != W_MXFP4 || (TBN == 256 && TBK == 32), "MXFP4 tiles: 256 rows, 32-deep slices");
@@ -132,11 +132,23 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta) {
 
   // Workgroups are dispatched to the 8 XCDs round-robin; the tile list is cut
   // into 8 contiguous chunks so that the workgroups of one XCD walk one chunk
-  // and share its weight and token tiles through their L2.
+  // and share its weight and token tiles through their L2.  Inside a chunk a
+  // workgroup takes the next tile from the XCD's counter when it is free, so
+  // the tiles in flight on an XCD stay neighbours in the list (an expert's
+  // tiles, which share token rows and weights) however long each tile took;
+  // with a fixed stride they drift apart over the rounds.  Every tile is
+  // computed the same way by whichever workgroup takes it.
   const int nx = gridDim.x % 8 == 0 ? 8 : 1;
-  const int xcd = blockIdx.x % nx, wg_in_xcd = blockIdx.x / nx, wgs_per_xcd = gridDim.x / nx;
+  const int xcd = blockIdx.x % nx;
   const int chunk = (total + nx - 1) / nx;
-  for (int local = wg_in_xcd; local < chunk; local += wgs_per_xcd) {
+  int *next = reinterpret_cast<int *>(smem);  // the LDS is free between tiles
+  for (;;) {
+    __syncthreads();  // the previous tile's LDS reads are done
+    if (tid == 0) next[0] = atomicAdd(queue + xcd, 1);
+    __syncthreads();
+    const int local = next[0];
+    __syncthreads();  // read before the tile's first LDS stores
+    if (local >= chunk) break;
     const int tile = xcd * chunk + local;
     if (tile >= total) break;
     TileCoord c;
@@ -398,7 +410,7 @@ static size_t tiled_lds_bytes(bool lo) {
 }
 
 template <bool GATE_UP, int WF, bool GATHER, bool LO, int TN, int TK>
-static hipError_t launch_tiled_t(const TiledGemmArgs &t, long mtiles_bound, hipStream_t st) {
+static hipError_t launch_tiled_t(const TiledGemmArgs &t, long mtiles_bound, int32_t *queue, hipStream_t st) {
   auto kern = expert_tiled<GATE_UP, WF, GATHER, LO, TN, TK>;
   const size_t lds = tiled_lds_bytes<TN, TK>(LO);
   static const hipError_t attr =  // LDS above 64 KB must be allowed once per kernel
@@ -406,35 +418,36 @@ static hipError_t launch_tiled_t(const TiledGemmArgs &t, long mtiles_bound, hipS
   if (attr != hipSuccess) return attr;
   const long n_tiles = (t.g.N + (GATE_UP ? TN / 2 : TN) - 1) / (GATE_UP ? TN / 2 : TN);
   const int grid = (int)std::max(1L, std::min(mtiles_bound * n_tiles, 512L));  // two per CU
-  enqueue_kernel(kern, dim3(grid), dim3(TTHREADS), lds, st, t);
+  enqueue_kernel(kern, dim3(grid), dim3(TTHREADS), lds, st, t, queue);
   return hipGetLastError();
 }
 
 hipError_t launch_tiled(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total,
-                        int max_groups, hipStream_t st) {
+                        int max_groups, int32_t *queue, hipStream_t st) {
+  if (!queue) return hipErrorInvalidValue;
   const ExpertGemmArgs &a = t.g;
   const long mtiles_bound = (max_rows_total + TBM - 1) / TBM + max_groups;
   const bool gather = gate_up && a.perm != nullptr;
   if (gate_up) {
     if (wf == W_MXFP4)
-      return gather ? launch_tiled_t<true, W_MXFP4, true, false, kTN, kTK>(t, mtiles_bound, st)
-                    : launch_tiled_t<true, W_MXFP4, false, false, kTN, kTK>(t, mtiles_bound, st);
+      return gather ? launch_tiled_t<true, W_MXFP4, true, false, kTN, kTK>(t, mtiles_bound, queue, st)
+                    : launch_tiled_t<true, W_MXFP4, false, false, kTN, kTK>(t, mtiles_bound, queue, st);
     // 128 x 64 tiles pay for themselves where experts hold about one row tile
     // (qwen3_5_moe at T=4096, 80 rows: gate_up 1254 -> 1162 us); with many
     // row tiles per expert (deepseek_v4 at T=4096: 128 on average, up to 602)
     // the doubled re-reads of their token rows cost more (2373 -> 2446 us)
     if (max_rows_total <= 96L * max_groups)
-      return gather ? launch_tiled_t<true, W_BF16, true, false, kTNg, kTKg>(t, mtiles_bound, st)
-                    : launch_tiled_t<true, W_BF16, false, false, kTNg, kTKg>(t, mtiles_bound, st);
-    return gather ? launch_tiled_t<true, W_BF16, true, false, kTN, kTK>(t, mtiles_bound, st)
-                  : launch_tiled_t<true, W_BF16, false, false, kTN, kTK>(t, mtiles_bound, st);
+      return gather ? launch_tiled_t<true, W_BF16, true, false, kTNg, kTKg>(t, mtiles_bound, queue, st)
+                    : launch_tiled_t<true, W_BF16, false, false, kTNg, kTKg>(t, mtiles_bound, queue, st);
+    return gather ? launch_tiled_t<true, W_BF16, true, false, kTN, kTK>(t, mtiles_bound, queue, st)
+                  : launch_tiled_t<true, W_BF16, false, false, kTN, kTK>(t, mtiles_bound, queue, st);
   }
   if (a.A_lo) {
-    if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, true, kTN, kTK>(t, mtiles_bound, st);
-    return launch_tiled_t<false, W_BF16, false, true, kTN, kTK>(t, mtiles_bound, st);
+    if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, true, kTN, kTK>(t, mtiles_bound, queue, st);
+    return launch_tiled_t<false, W_BF16, false, true, kTN, kTK>(t, mtiles_bound, queue, st);
   }
-  if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, false, kTN, kTK>(t, mtiles_bound, st);
-  return launch_tiled_t<false, W_BF16, false, false, kTN, kTK>(t, mtiles_bound, st);
+  if (wf == W_MXFP4) return launch_tiled_t<false, W_MXFP4, false, false, kTN, kTK>(t, mtiles_bound, queue, st);
+  return launch_tiled_t<false, W_BF16, false, false, kTN, kTK>(t, mtiles_bound, queue, st);
 }
 
 int tiled_tile_rows() { return TBM; }
