@@ -99,7 +99,7 @@ struct GemmPlan {
 };
 
 constexpr long kBigTileRows = 256;
-constexpr int kTiledLaunches = 4;  // routed and shared gate_up and down
+constexpr int kQueuedLaunches = 6;  // tiled routed/shared gate_up and down, big-tile routed/shared gate_up
 
 // 32-bit offsets of the big-tile kernel: activations, h and one expert's
 // weights below 4 GiB
@@ -168,8 +168,8 @@ Layout make_layout(const moe_config &c) {
   const bool mxs = gemm_plan(c).mx_scaled;
   L.mxq = take(mxs ? T * H * 2 : 0);
   L.mxs = take(mxs ? T * (H / 32) * 2 : 0);
-  // tile counters of the tiled launches (routed and shared gate_up and down)
-  L.tile_queue = take(kTiledLaunches * kTiledQueueInts * 4);
+  // tile counters of the tiled and big-tile launches
+  L.tile_queue = take(kQueuedLaunches * kTiledQueueInts * 4);
   L.total = off;
   return L;
 }
@@ -499,11 +499,12 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
   // chunks at small T, so that enough work items stream its weights)
   const int sh_chunk_rows = c.T <= 128 ? 16 : 32;
   const long sh_chunks = ((long)c.T + sh_chunk_rows - 1) / sh_chunk_rows;
-  // the tiled launches' tile counters start at zero (one fill for all four)
+  // the tiled and big-tile launches' tile counters start at zero (one fill
+  // for all of them)
   int32_t *queue = reinterpret_cast<int32_t *>(ws + L.tile_queue);
   auto tile_queue = [&](int launch) { return queue + launch * kTiledQueueInts; };
   if (plan.tiled || plan.tiled_shared)
-    HIP_TRY(launch_fill_i32(queue, 0, kTiledLaunches * kTiledQueueInts, st), "fill launch");
+    HIP_TRY(launch_fill_i32(queue, 0, kQueuedLaunches * kTiledQueueInts, st), "fill launch");
   // where routed and shared experts both run on the streaming kernels with
   // bf16 operands, the shared expert's gate_up items ride in the routed
   // gate_up launch.  Measured at T=72 (DeepSeek-V4-style / qwen3_5_moe
@@ -557,7 +558,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
       HIP_TRY(launch_mxfp8_split(static_cast<const uint16_t *>(x), c.T, c.H, xa, st), "activation split launch");
       HIP_TRY(launch_bigtile_mx_scaled(t1, xa, slots, max_groups, st), "routed gate_up launch");
     } else if (plan.big) {
-      HIP_TRY(launch_bigtile(t1, true, wf, slots, max_groups, st), "routed gate_up launch");
+      HIP_TRY(launch_bigtile(t1, true, wf, slots, max_groups, tile_queue(4), st), "routed gate_up launch");
     }
     else HIP_TRY(launch_tiled(t1, true, wf, slots, max_groups, tile_queue(0), st), "routed gate_up launch");
   } else {
@@ -585,7 +586,7 @@ int forward_impl(const moe_config &c, const void *x, const moe_weights *wt, void
       HIP_TRY(launch_gate_up_f32(s1, 1, st), "shared gate_up launch");
     } else if (plan.tiled_shared) {
       TiledGemmArgs ts{s1, nullptr, nullptr, nullptr};
-      if (plan.big_shared) HIP_TRY(launch_bigtile(ts, true, af, c.T, 1, st), "shared gate_up launch");
+      if (plan.big_shared) HIP_TRY(launch_bigtile(ts, true, af, c.T, 1, tile_queue(5), st), "shared gate_up launch");
       else HIP_TRY(launch_tiled(ts, true, af, c.T, 1, tile_queue(1), st), "shared gate_up launch");
     } else {
       HIP_TRY(launch_stream(s1, true, af, sh_chunks, st), "shared gate_up launch");

@@ -512,7 +512,7 @@ __device__ __forceinline__ void interleave_reads_valu() {
 }  // namespace
 
 template <bool GATE_UP, bool GATHER, bool LO, int TM, int WF>
-__global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs ta) {
+__global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs ta, int32_t *queue) {
   using P = DmaPlan<LO, TM, WF>;
   constexpr bool MX = P::MX;
   constexpr int CH = P::CH, WUN = P::WUN, XUN = P::XUN, SLOT = P::SLOT, NSTAGE = P::NSTAGE, OPS = P::OPS;
@@ -534,10 +534,21 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
                              : ((a.single_rows + TM - 1) / TM) * n_tiles;
   const int nst = a.Kdim / P::BK;  // the reduction is a multiple of 32
 
+  // XCD-contiguous ranges of the tile list; inside its range a workgroup
+  // takes the next tile from the XCD's counter when it is free (the thin
+  // tail tiles of the experts cost less than full ones, so a fixed stride
+  // leaves some workgroups idle at the end)
   const int nx = gridDim.x % 8 == 0 ? 8 : 1;
-  const int xcd = blockIdx.x % nx, per = gridDim.x / nx;
+  const int xcd = blockIdx.x % nx;
   const int span = (total + nx - 1) / nx;
-  for (int local = blockIdx.x / nx; local < span; local += per) {
+  int *next = reinterpret_cast<int *>(smem);  // the ring is free between tiles
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) next[0] = atomicAdd(queue + xcd, 1);
+    __syncthreads();
+    const int local = next[0];
+    __syncthreads();
+    if (local >= span) break;
     const int tile = xcd * span + local;
     if (tile >= total) break;
     BigCoord c;
@@ -1024,7 +1035,7 @@ __global__ __launch_bounds__(256) void mxfp8_split(const uint16_t *x, long n_blo
 namespace {
 
 template <bool GATE_UP, bool GATHER, bool LO, int TM = BM, int WF = W_BF16>
-hipError_t launch_dma_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
+hipError_t launch_dma_t(const TiledGemmArgs &t, long tiles_bound, int32_t *queue, hipStream_t st) {
   using P = DmaPlan<LO, TM, WF>;
   auto kern = expert_bigtile_dma<GATE_UP, GATHER, LO, TM, WF>;
   // the ring (+ the MXFP4 scale table), or the gate_up epilogue's staging if
@@ -1037,21 +1048,21 @@ hipError_t launch_dma_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st
       hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
   if (attr != hipSuccess) return attr;
   const int grid = (int)std::max(1L, std::min(tiles_bound, 256L));  // one per CU
-  enqueue_kernel(kern, dim3(grid), dim3(kThreads), lds, st, t);
+  enqueue_kernel(kern, dim3(grid), dim3(kThreads), lds, st, t, queue);
   return hipGetLastError();
 }
 
 template <bool GATE_UP, int WF, bool GATHER, bool LO>
-hipError_t launch_big_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st) {
+hipError_t launch_big_t(const TiledGemmArgs &t, long tiles_bound, int32_t *queue, hipStream_t st) {
   if constexpr (WF == W_BF16) {
-    return launch_dma_t<GATE_UP, GATHER, LO>(t, tiles_bound, st);
+    return launch_dma_t<GATE_UP, GATHER, LO>(t, tiles_bound, queue, st);
   } else {
     if constexpr (GATE_UP && !LO) {
       // MXFP4 gate_up: codes and the tile's scale table fed by direct-to-LDS
       // loads (16-byte loads: the scale array starts on 16 bytes; the table
       // fits beside the ring up to a reduction of MAX_K)
       if ((reinterpret_cast<uintptr_t>(t.g.Wscale) & 15) == 0 && t.g.Kdim <= DmaPlan<LO, BM, W_MXFP4>::MAX_K)
-        return launch_dma_t<GATE_UP, GATHER, LO, BM, W_MXFP4>(t, tiles_bound, st);
+        return launch_dma_t<GATE_UP, GATHER, LO, BM, W_MXFP4>(t, tiles_bound, queue, st);
     }
     // otherwise codes are decoded on their way into LDS (register-staged)
     auto kern = expert_bigtile<GATE_UP, WF, GATHER, LO>;
@@ -1069,7 +1080,8 @@ hipError_t launch_big_t(const TiledGemmArgs &t, long tiles_bound, hipStream_t st
 }  // namespace
 
 hipError_t launch_bigtile(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total, int max_groups,
-                          hipStream_t st) {
+                          int32_t *queue, hipStream_t st) {
+  if (!queue) return hipErrorInvalidValue;
   const ExpertGemmArgs &a = t.g;
   const int cols_per_tile = gate_up ? BN / 2 : BN;
   const long n_tiles = (a.N + cols_per_tile - 1) / cols_per_tile;
@@ -1077,17 +1089,17 @@ hipError_t launch_bigtile(const TiledGemmArgs &t, bool gate_up, WFormat wf, long
   const bool gather = gate_up && a.perm != nullptr;
   if (gate_up) {
     if (wf == W_MXFP4)
-      return gather ? launch_big_t<true, W_MXFP4, true, false>(t, tiles_bound, st)
-                    : launch_big_t<true, W_MXFP4, false, false>(t, tiles_bound, st);
-    return gather ? launch_big_t<true, W_BF16, true, false>(t, tiles_bound, st)
-                  : launch_big_t<true, W_BF16, false, false>(t, tiles_bound, st);
+      return gather ? launch_big_t<true, W_MXFP4, true, false>(t, tiles_bound, queue, st)
+                    : launch_big_t<true, W_MXFP4, false, false>(t, tiles_bound, queue, st);
+    return gather ? launch_big_t<true, W_BF16, true, false>(t, tiles_bound, queue, st)
+                  : launch_big_t<true, W_BF16, false, false>(t, tiles_bound, queue, st);
   }
   if (a.A_lo) {
-    if (wf == W_MXFP4) return launch_big_t<false, W_MXFP4, false, true>(t, tiles_bound, st);
-    return launch_big_t<false, W_BF16, false, true>(t, tiles_bound, st);
+    if (wf == W_MXFP4) return launch_big_t<false, W_MXFP4, false, true>(t, tiles_bound, queue, st);
+    return launch_big_t<false, W_BF16, false, true>(t, tiles_bound, queue, st);
   }
-  if (wf == W_MXFP4) return launch_big_t<false, W_MXFP4, false, false>(t, tiles_bound, st);
-  return launch_big_t<false, W_BF16, false, false>(t, tiles_bound, st);
+  if (wf == W_MXFP4) return launch_big_t<false, W_MXFP4, false, false>(t, tiles_bound, queue, st);
+  return launch_big_t<false, W_BF16, false, false>(t, tiles_bound, queue, st);
 }
 
 int bigtile_rows() { return BM; }

@@ -38,8 +38,9 @@ int tiled_tile_rows();
 
 // Large-tile grouped GEMM (experts with hundreds of rows: matrix-core bound).
 // Activations, h and one expert's weights must each span less than 4 GiB.
+// queue: kTiledQueueInts tile counters, zero when the launch starts.
 hipError_t launch_bigtile(const TiledGemmArgs &t, bool gate_up, WFormat wf, long max_rows_total,
-                          int max_groups, hipStream_t st);
+                          int max_groups, int32_t *queue, hipStream_t st);
 int bigtile_rows();
 
 // MXFP4 gate_up on the block-scaled matrix cores: the activations as two
