@@ -306,11 +306,13 @@ def test_bitwise_deterministic():
     assert torch.equal(ra.weights.view(torch.int32), rb.weights.view(torch.int32))
 
 
-def test_big_tiles_deterministic_under_graph_replay():
-    """The large-tile path with more tiles than workgroups: the same bits on
-    every call whatever the workspace held before, eagerly and under HIP
-    graph replay."""
-    wl = next(w for w in SMALL if w.name == "big_many_tiles_t4096")
+@pytest.mark.parametrize("name", ["big_many_tiles_t4096", "tiled_collapsed_t1500"])
+def test_tiles_deterministic_under_graph_replay(name):
+    """The large-tile and tiled paths with more tiles than workgroups (tiles
+    taken from per-XCD counters in the workspace): the same bits on every
+    call whatever the workspace held before, eagerly and under HIP graph
+    replay."""
+    wl = next(w for w in SMALL if w.name == name)
     case = Case(wl)
     ws = api.alloc_workspace(case.cfg)
     ws.fill_(0xA5)
