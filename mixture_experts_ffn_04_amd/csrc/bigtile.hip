@@ -542,15 +542,31 @@ __global__ __launch_bounds__(kThreads, 1) void expert_bigtile_dma(TiledGemmArgs 
   const int xcd = blockIdx.x % nx;
   const int span = (total + nx - 1) / nx;
   int *next = reinterpret_cast<int *>(smem);  // the ring is free between tiles
+  // once its own range is done, a workgroup of a launch over many experts
+  // takes tiles left in the other XCDs' ranges (gpt-oss MXFP4 gate_up at
+  // T=2048: 481 -> 456 us); a single group's equal tiles stay in their
+  // range (stealing slowed the shared expert's gate_up by 12%: a stolen
+  // tile's operands sit in another XCD's L2)
+  const int sources = a.single_rows == 0 ? nx : 1;
+  int from = 0;  // (thread 0) the counter drawn from: own XCD's, then the others'
   for (;;) {
     __syncthreads();
-    if (tid == 0) next[0] = atomicAdd(queue + xcd, 1);
+    if (tid == 0) {
+      int got = -1;
+      for (; from < sources; ++from) {
+        const int x2 = (xcd + from) % nx;
+        const int local = atomicAdd(queue + x2, 1);
+        if (local < span && x2 * span + local < total) {
+          got = x2 * span + local;
+          break;
+        }
+      }
+      next[0] = got;
+    }
     __syncthreads();
-    const int local = next[0];
+    const int tile = next[0];
     __syncthreads();
-    if (local >= span) break;
-    const int tile = xcd * span + local;
-    if (tile >= total) break;
+    if (tile < 0) break;
     BigCoord c;
     big_coord(ta, tile, n_tiles, c, TM);
     const int col0 = c.n0 * cols_per_tile;

@@ -142,15 +142,42 @@ __global__ __launch_bounds__(TTHREADS, 2) void expert_tiled(TiledGemmArgs ta, in
   const int xcd = blockIdx.x % nx;
   const int chunk = (total + nx - 1) / nx;
   int *next = reinterpret_cast<int *>(smem);  // the LDS is free between tiles
+  // Once its XCD's chunk is done, a workgroup of a routed gate_up (many
+  // experts, tiles of unequal cost) takes tiles left in the other XCDs'
+  // chunks: gate_up 1-3% faster.  The down calls were as often slower as
+  // faster, and a single group's equal tiles only lose (a stolen tile's
+  // operands sit in another XCD's L2), so those stay on their own chunk.
+  const int sources = a.single_rows == 0 ? nx : 1;
+  int from = 0;  // (thread 0) the counter drawn from: own XCD's, then the others'
   for (;;) {
     __syncthreads();  // the previous tile's LDS reads are done
-    if (tid == 0) next[0] = atomicAdd(queue + xcd, 1);
-    __syncthreads();
-    const int local = next[0];
-    __syncthreads();  // read before the tile's first LDS stores
-    if (local >= chunk) break;
-    const int tile = xcd * chunk + local;
-    if (tile >= total) break;
+    int tile;
+    if constexpr (GATE_UP) {
+      if (tid == 0) {
+        int got = -1;
+        for (; from < sources; ++from) {
+          const int x2 = (xcd + from) % nx;
+          const int local = atomicAdd(queue + x2, 1);
+          if (local < chunk && x2 * chunk + local < total) {
+            got = x2 * chunk + local;
+            break;
+          }
+        }
+        next[0] = got;
+      }
+      __syncthreads();
+      tile = next[0];
+      __syncthreads();  // read before the tile's first LDS stores
+      if (tile < 0) break;
+    } else {
+      if (tid == 0) next[0] = atomicAdd(queue + xcd, 1);
+      __syncthreads();
+      const int local = next[0];
+      __syncthreads();  // read before the tile's first LDS stores
+      if (local >= chunk) break;
+      tile = xcd * chunk + local;
+      if (tile >= total) break;
+    }
     TileCoord c;
     tile_coord(ta, tile, n_tiles, c);
     const int col0 = c.n0 * cols_per_tile;
